@@ -1,0 +1,154 @@
+/*
+ * muon.h - C ABI of libmuon: the single-GPU Muon optimizer step and the
+ * periodic-RowNorm non-refresh step on AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what the calls compute (page title, then section/equation):
+ *   "Infra Optimizers" (summary of "Muon is Scalable for LLM Training"):
+ *       Background eq. (1) momentum, the Nesterov remark, the Frobenius
+ *       normalisation, eq. (2) quintic Newton-Schulz with a, b, c;
+ *       "Scaling Up Muon" eq. (3) decoupled weight decay, Lemma 1 and
+ *       eq. (4) the 0.2*sqrt(max(A, B)) update scale, N = 5, mu = 0.95.
+ *   "Scaling Muon for Diffusion Transformers": 2.1 (update
+ *       W <- (1 - lr*wd) W - lr*s(W)*Phi_5(M)), 3.1 (short-side orientation
+ *       and the row-normalisation operator R_eps), abstract (refresh every
+ *       K steps, RowNorm on the current momentum otherwise).
+ *   "DMuon: Efficient Distributed Muon Training with Near-Adam Overhead":
+ *       2.2 (Gram-space Newton-Schulz on the short side, symmetric SYRK-style
+ *       Gram product, batching of same-shape matrices).
+ *
+ * Conventions shared by every call:
+ *   - A matrix i is m_i x n_i, row-major and contiguous (the [out, in]
+ *     layout of a linear layer).  r = min(m, n), c = max(m, n).
+ *   - W (fp32 master weights) and M (fp32 momentum) are updated in place;
+ *     G (gradient, fp32 or bf16 as planned) is read only.
+ *   - Every pointer inside the W / M / G / O_out / R_out arrays is a HIP
+ *     device pointer owned by the caller.  The arrays themselves are host
+ *     arrays of length num_matrices, in the order given to muon_plan.
+ *   - The workspace is a caller-owned device buffer of at least the size
+ *     muon_plan reported, 256-byte aligned.  Its contents between calls are
+ *     irrelevant (every call rewrites what it reads).
+ *   - Calls enqueue work on `stream` and return without synchronising.
+ *     Results are valid once the stream has reached that point.
+ *   - Errors: all validation happens on the host before anything is
+ *     enqueued.  On any status other than MUON_OK and MUON_ERR_HIP nothing
+ *     was enqueued and no memory was touched.  MUON_ERR_HIP means a HIP
+ *     runtime call failed after work may have been enqueued; W and M are
+ *     then undefined.  No C++ exception crosses this interface.
+ *   - Concurrency: at most one call per plan may be in flight on the GPU
+ *     with a given workspace; different plans with different workspaces are
+ *     independent.  A plan may be used from one host thread at a time.
+ *   - The step counter and the refresh schedule (call muon_step_batched when
+ *     t mod K == 0, rownorm_step otherwise) belong to the caller.
+ */
+#ifndef MUON_H
+#define MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct muon_plan_s* muon_plan_t;
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad count/shape/value */
+  MUON_ERR_UNSUPPORTED = 2,        /* valid but not implemented (dtype, steps) */
+  MUON_ERR_WORKSPACE_TOO_SMALL = 3,
+  MUON_ERR_HIP = 4                 /* a HIP runtime call failed */
+} muon_status;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* Hyper-parameters fixed at plan time.  muon_default_hparams fills the
+ * values the pages give: mu = 0.95 and N = 5 ("Infra Optimizers", Scaling Up
+ * Muon), a = 3.4445, b = -4.7750, c = 2.0315 (Background, eq. (2)), the 0.2
+ * RMS-matching factor (eq. (4)), and eps = 1e-8 for R_eps (the pages leave
+ * eps open). */
+typedef struct {
+  float momentum;      /* mu in M <- mu*M + G                               */
+  int   nesterov;      /* 1: NS / RowNorm input U = mu*M' + G; 0: U = M'      */
+  int   ns_steps;      /* Newton-Schulz iterations, 1..16                   */
+  float a, b, c;       /* quintic coefficients                              */
+  float scale_coeff;   /* s(W) = scale_coeff * sqrt(max(m, n))              */
+  float rownorm_eps;   /* eps of R_eps, > 0                                 */
+} muon_hparams;
+
+typedef struct {
+  int64_t num_matrices;      /* >= 1                                         */
+  const int64_t* rows;       /* host array [num_matrices], each m >= 1       */
+  const int64_t* cols;       /* host array [num_matrices], each n >= 1       */
+  muon_dtype grad_dtype;     /* storage type of G: MUON_F32 or MUON_BF16     */
+  muon_dtype ns_dtype;       /* MUON_F32: fp32-MFMA Newton-Schulz path;
+                                MUON_BF16: bf16-MFMA Gram/final products with
+                                an fp16-MFMA r x r recursion                 */
+  muon_hparams hp;
+  int64_t max_workspace_bytes; /* cap for the Newton-Schulz scratch; 0 = the
+                                  library default (16 GiB).  Buckets of
+                                  same-shape matrices are split into chunks
+                                  that fit; a single matrix always fits.     */
+} muon_plan_desc;
+
+/* Fill *hp with the defaults listed above.  Returns MUON_ERR_INVALID_ARGUMENT
+ * if hp is NULL. */
+muon_status muon_default_hparams(muon_hparams* hp);
+
+/* Validate the description, bucket same-shape matrices ("DMuon" 2.2
+ * batching), choose the orientation per bucket ("Scaling Muon for Diffusion
+ * Transformers" 3.1) and lay out the workspace.  Host only: no device work,
+ * no device allocation.  On success *plan owns host memory only and
+ * *workspace_bytes (nullable) receives the workspace size needed by both
+ * step calls. */
+muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* workspace_bytes);
+
+/* Release a plan.  NULL is accepted.  The caller must ensure no work using
+ * the plan is still pending on the GPU. */
+muon_status muon_plan_destroy(muon_plan_t plan);
+
+/* Workspace size of an existing plan. */
+muon_status muon_plan_workspace_size(muon_plan_t plan, size_t* workspace_bytes);
+
+/* Number of same-shape buckets and launch chunks the planner formed. */
+muon_status muon_plan_info(muon_plan_t plan, int64_t* num_buckets, int64_t* num_chunks);
+
+/* Newton-Schulz (refresh) step for every planned matrix:
+ *   M  <- mu*M + G                                   ("Infra Optimizers" eq. (1))
+ *   U   = mu*M + G  (updated M; U = M if nesterov=0)  (Background, Nesterov)
+ *   X0  = O(U) / ||U||_F,  O = transpose iff m > n     (eq. (2) preamble; DiT 3.1)
+ *   X_N = N quintic steps a X + b (X X^T) X + c (X X^T)^2 X, evaluated in
+ *         the r x r Gram space X_N = p(A_{N-1})...p(A_0) X0  (eq. (2); DMuon 2.2)
+ *   W  <- (1 - lr*wd) W - lr * scale_coeff*sqrt(max(m,n)) * O^{-1}(X_N)
+ *                                                      (eq. (4); DiT 2.1)
+ * A matrix with ||U||_F == 0 gets X_N = 0 (pure decay).
+ * G[i] points to fp32 or bf16 data as planned.  O_out is NULL or a host
+ * array of nullable device pointers; a non-NULL O_out[i] (fp32, m x n)
+ * receives O^{-1}(X_N) for matrix i (a parity/debug output).
+ * lr and wd must be finite; workspace_bytes must be >= the planned size. */
+muon_status muon_step_batched(muon_plan_t plan, float* const* W, float* const* M,
+                              const void* const* G, float lr, float weight_decay,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              float* const* O_out);
+
+/* Non-refresh step of periodic RowNorm Muon ("Scaling Muon for Diffusion
+ * Transformers", abstract and 3.1): the same M update and U, then
+ *   R = O^{-1}(R_eps(O(U))),  R_eps(X)_i = X_i / max(||X_i||_2, eps)
+ * over the r rows of the oriented matrix (the columns of U when m > n), and
+ *   W <- (1 - lr*wd) W - lr * scale_coeff*sqrt(max(m,n)) * R.
+ * R_out works like O_out.  Always computed in fp32. */
+muon_status rownorm_step(muon_plan_t plan, float* const* W, float* const* M,
+                         const void* const* G, float lr, float weight_decay,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         float* const* R_out);
+
+/* Static, human-readable name of a status code. */
+const char* muon_status_string(muon_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H */

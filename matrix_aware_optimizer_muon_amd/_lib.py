@@ -1,0 +1,170 @@
+"""ctypes binding of libmuon.so (include/muon.h).
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing the import of the binding
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmuon.so")
+
+MUON_OK = 0
+MUON_ERR_INVALID_ARGUMENT = 1
+MUON_ERR_UNSUPPORTED = 2
+MUON_ERR_WORKSPACE_TOO_SMALL = 3
+MUON_ERR_HIP = 4
+
+MUON_F32 = 0
+MUON_BF16 = 1
+
+EXPORTED = ("muon_default_hparams", "muon_plan", "muon_plan_destroy", "muon_plan_workspace_size",
+            "muon_plan_info", "muon_step_batched", "rownorm_step", "muon_status_string")
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class Hparams(ctypes.Structure):
+    _fields_ = [("momentum", ctypes.c_float), ("nesterov", ctypes.c_int),
+                ("ns_steps", ctypes.c_int), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                ("c", ctypes.c_float), ("scale_coeff", ctypes.c_float),
+                ("rownorm_eps", ctypes.c_float)]
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [("num_matrices", ctypes.c_int64), ("rows", ctypes.POINTER(ctypes.c_int64)),
+                ("cols", ctypes.POINTER(ctypes.c_int64)), ("grad_dtype", ctypes.c_int),
+                ("ns_dtype", ctypes.c_int), ("hp", Hparams),
+                ("max_workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmuon.so from the package directory (built in place)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    lib.muon_default_hparams.argtypes = [ctypes.POINTER(Hparams)]
+    lib.muon_plan.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(P),
+                              ctypes.POINTER(ctypes.c_size_t)]
+    lib.muon_plan_destroy.argtypes = [P]
+    lib.muon_plan_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.muon_plan_info.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    step_args = [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P), ctypes.c_float,
+                 ctypes.c_float, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
+    lib.muon_step_batched.argtypes = step_args
+    lib.rownorm_step.argtypes = step_args
+    lib.muon_status_string.argtypes = [ctypes.c_int]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    for name in ("muon_default_hparams", "muon_plan", "muon_plan_destroy",
+                 "muon_plan_workspace_size", "muon_plan_info", "muon_step_batched",
+                 "rownorm_step"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().muon_status_string(int(status)).decode()
+
+
+def default_hparams() -> Hparams:
+    hp = Hparams()
+    st = load().muon_default_hparams(ctypes.byref(hp))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_default_hparams")
+    return hp
+
+
+def _ptr_array(ptrs: Sequence[Optional[int]]):
+    arr = (ctypes.c_void_p * len(ptrs))()
+    for i, p in enumerate(ptrs):
+        arr[i] = p if p else None
+    return arr
+
+
+class Plan:
+    """A planned set of matrices (muon_plan).  `shapes` is a list of (m, n).
+
+    grad_dtype / ns_dtype are "f32" or "bf16"."""
+
+    def __init__(self, shapes: Sequence[tuple], grad_dtype: str = "f32", ns_dtype: str = "bf16",
+                 hp: Optional[Hparams] = None, max_workspace_bytes: int = 0):
+        lib = load()
+        self._lib = lib
+        self.shapes = [(int(m), int(n)) for m, n in shapes]
+        n = len(self.shapes)
+        rows = (ctypes.c_int64 * max(n, 1))(*[s[0] for s in self.shapes])
+        cols = (ctypes.c_int64 * max(n, 1))(*[s[1] for s in self.shapes])
+        desc = PlanDesc()
+        desc.num_matrices = n
+        desc.rows = ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64))
+        desc.cols = ctypes.cast(cols, ctypes.POINTER(ctypes.c_int64))
+        desc.grad_dtype = {"f32": MUON_F32, "bf16": MUON_BF16}[grad_dtype]
+        desc.ns_dtype = {"f32": MUON_F32, "bf16": MUON_BF16}[ns_dtype]
+        desc.hp = hp if hp is not None else default_hparams()
+        desc.max_workspace_bytes = int(max_workspace_bytes)
+        self.hp = desc.hp
+        self.grad_dtype, self.ns_dtype = grad_dtype, ns_dtype
+        handle = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        st = lib.muon_plan(ctypes.byref(desc), ctypes.byref(handle), ctypes.byref(ws))
+        if st != MUON_OK:
+            raise MuonError(st, "muon_plan")
+        self._handle = handle
+        self.workspace_bytes = int(ws.value)
+
+    def info(self) -> tuple[int, int]:
+        nb, nc = ctypes.c_int64(), ctypes.c_int64()
+        st = self._lib.muon_plan_info(self._handle, ctypes.byref(nb), ctypes.byref(nc))
+        if st != MUON_OK:
+            raise MuonError(st, "muon_plan_info")
+        return int(nb.value), int(nc.value)
+
+    def _call(self, fn, name, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream, out):
+        n = len(self.shapes)
+        if not (len(W) == len(M) == len(G) == n):
+            raise ValueError(f"expected {n} matrices")
+        o_arr = _ptr_array(out) if out is not None else None
+        st = fn(self._handle, _ptr_array(W), _ptr_array(M), _ptr_array(G), ctypes.c_float(lr),
+                ctypes.c_float(wd), ctypes.c_void_p(workspace_ptr), ctypes.c_size_t(workspace_bytes),
+                ctypes.c_void_p(stream or 0), o_arr)
+        if st != MUON_OK:
+            raise MuonError(st, name)
+
+    def step_ptrs(self, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream=0, O_out=None):
+        """muon_step_batched on raw device pointers."""
+        self._call(self._lib.muon_step_batched, "muon_step_batched", W, M, G, lr, wd,
+                   workspace_ptr, workspace_bytes, stream, O_out)
+
+    def rownorm_ptrs(self, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream=0, R_out=None):
+        """rownorm_step on raw device pointers."""
+        self._call(self._lib.rownorm_step, "rownorm_step", W, M, G, lr, wd, workspace_ptr,
+                   workspace_bytes, stream, R_out)
+
+    def close(self):
+        if getattr(self, "_handle", None):
+            self._lib.muon_plan_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+

@@ -1,0 +1,67 @@
+// Shared device helpers for the Muon kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Storage type tags.  16-bit values are kept as raw uint16_t in memory.
+struct BF16 {};
+struct F16 {};
+struct F32 {};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct Store;
+template <> struct Store<BF16> {
+  typedef uint16_t type;
+  static __device__ __forceinline__ uint16_t from(float f) { return f32_to_bf16_bits(f); }
+};
+template <> struct Store<F16> {
+  typedef uint16_t type;
+  static __device__ __forceinline__ uint16_t from(float f) { return f32_to_f16_bits(f); }
+};
+template <> struct Store<F32> {
+  typedef float type;
+  static __device__ __forceinline__ float from(float f) { return f; }
+};
+
+// Map a linear workgroup id so that consecutive logical ids land on the same
+// XCD.  The hardware dispatches workgroup w to XCD (w mod 8); tiles that share
+// operand panels should share that XCD's L2.  Bijective for any total.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+  const uint32_t nx = 8;
+  uint32_t x = bid % nx, slot = bid / nx;
+  uint32_t q = total / nx, rem = total % nx;
+  return x * q + (x < rem ? x : rem) + slot;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace muon

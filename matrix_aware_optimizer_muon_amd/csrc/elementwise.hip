@@ -1,0 +1,477 @@
+// Memory-bound kernels of the Muon and periodic-RowNorm steps.
+//
+// prep:       M <- mu M + G ("Infra Optimizers" eq. (1)); U = mu M + G
+//             (Nesterov remark); partial sums of ||U||_F^2; X0 = O(U) stored
+//             r x c in the Newton-Schulz operand type, transposed through LDS
+//             when m > n ("Scaling Muon for DiT" 3.1), zero padded to the
+//             GEMM tile.  One read of M and G, one write of M and X0.
+// finalize:   deterministic (fixed order, fp64) reduction of the partial sums
+//             to 1/||U||_F per matrix (0 when the norm is 0).
+// rownorm:    the same M update and U, then R_eps over the r oriented rows
+//             ("Scaling Muon for DiT" 3.1) and the decayed, scaled update of W
+//             ("Infra Optimizers" eq. (4)).  m <= n: one workgroup per row,
+//             one pass.  m > n: the rows of O(U) are columns of U, so a column
+//             sum-of-squares pass, a fixed-order finalize and an apply pass.
+#include "common.hpp"
+#include "kernels.h"
+
+namespace muon {
+
+// ---------------------------------------------------------------------------
+// Four consecutive elements of M (fp32) and G (fp32 or bf16), vector or
+// bounds-checked scalar access.
+template <bool GBF16>
+__device__ __forceinline__ float4 load_g4(const void* G, size_t idx, bool vec, int valid) {
+  float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (GBF16) {
+    const uint16_t* g16 = (const uint16_t*)G + idx;
+    if (vec) {
+      const uint2 u = *(const uint2*)g16;
+      g.x = __uint_as_float(u.x << 16);
+      g.y = __uint_as_float(u.x & 0xffff0000u);
+      g.z = __uint_as_float(u.y << 16);
+      g.w = __uint_as_float(u.y & 0xffff0000u);
+    } else {
+      if (valid > 0) g.x = bf16_bits_to_f32(g16[0]);
+      if (valid > 1) g.y = bf16_bits_to_f32(g16[1]);
+      if (valid > 2) g.z = bf16_bits_to_f32(g16[2]);
+      if (valid > 3) g.w = bf16_bits_to_f32(g16[3]);
+    }
+  } else {
+    const float* g32 = (const float*)G + idx;
+    if (vec) {
+      g = *(const float4*)g32;
+    } else {
+      if (valid > 0) g.x = g32[0];
+      if (valid > 1) g.y = g32[1];
+      if (valid > 2) g.z = g32[2];
+      if (valid > 3) g.w = g32[3];
+    }
+  }
+  return g;
+}
+
+__device__ __forceinline__ float4 load_f4(const float* p, bool vec, int valid) {
+  if (vec) return *(const float4*)p;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (valid > 0) v.x = p[0];
+  if (valid > 1) v.y = p[1];
+  if (valid > 2) v.z = p[2];
+  if (valid > 3) v.w = p[3];
+  return v;
+}
+
+__device__ __forceinline__ void store_f4(float* p, float4 v, bool vec, int valid) {
+  if (vec) {
+    *(float4*)p = v;
+    return;
+  }
+  if (valid > 0) p[0] = v.x;
+  if (valid > 1) p[1] = v.y;
+  if (valid > 2) p[2] = v.z;
+  if (valid > 3) p[3] = v.w;
+}
+
+// M' = mu M + G (stored), returns U = mu M' + G (or M' without Nesterov).
+__device__ __forceinline__ float4 momentum4(float4 m, float4 g, float mu, int nesterov,
+                                            float4* mnew) {
+  float4 mn;
+  mn.x = mu * m.x + g.x;
+  mn.y = mu * m.y + g.y;
+  mn.z = mu * m.z + g.z;
+  mn.w = mu * m.w + g.w;
+  *mnew = mn;
+  if (!nesterov) return mn;
+  return make_float4(mu * mn.x + g.x, mu * mn.y + g.y, mu * mn.z + g.z, mu * mn.w + g.w);
+}
+
+template <int BS>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < BS / 64; ++w) s += red[w];
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// prep, m <= n: X0 rows are rows of U.  Block: 256 threads x 4 columns = 1024
+// columns of PREP_ROWS rows.
+constexpr int PREP_ROWS = 8;
+
+template <bool GBF16, bool XF32>
+__global__ void __launch_bounds__(256) prep_rows_kernel(const PrepParams p, int vec) {
+  __shared__ float red[4];
+  const int cblocks = (p.c_pad + 1023) / 1024;
+  const int rblocks = (p.r_pad + PREP_ROWS - 1) / PREP_ROWS;
+  const int per_mat = cblocks * rblocks;
+  const int mat = blockIdx.x / per_mat;
+  const int bl = blockIdx.x - mat * per_mat;
+  const int rb = bl / cblocks, cb = bl - rb * cblocks;
+  const MatPtrs mp = p.table[mat];
+  const int col = cb * 1024 + threadIdx.x * 4;
+  float ss = 0.f;
+  if (col < p.c_pad) {
+    for (int rr = 0; rr < PREP_ROWS; ++rr) {
+      const int row = rb * PREP_ROWS + rr;
+      if (row >= p.r_pad) break;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < p.m && col < p.n) {
+        const int valid = p.n - col;
+        const size_t idx = (size_t)row * p.n + col;
+        const bool v4 = vec && valid >= 4;
+        const float4 m = load_f4(mp.M + idx, v4, valid);
+        const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
+        float4 mn;
+        u = momentum4(m, g, p.mu, p.nesterov, &mn);
+        store_f4(mp.M + idx, mn, v4, valid);
+        if (valid < 4) {  // keep the padding exactly zero
+          if (valid < 2) u.y = 0.f;
+          if (valid < 3) u.z = 0.f;
+          u.w = 0.f;
+        }
+        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+      }
+      const size_t xo = (size_t)mat * p.x_stride + (size_t)row * p.c_pad + col;
+      if (XF32) {
+        *(float4*)((float*)p.X + xo) = u;
+      } else {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(u.x) | ((uint32_t)f32_to_bf16_bits(u.y) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16);
+        *(uint2*)((uint16_t*)p.X + xo) = pk;
+      }
+    }
+  }
+  const float tot = block_sum<256>(ss, red);
+  if (threadIdx.x == 0) p.partials[(size_t)mat * p.blocks_per_mat + bl] = tot;
+}
+
+// prep, m > n: X0 = U^T.  A 64 x 64 tile of U (rows i < m, cols j < n) is
+// read row-major, staged in LDS and written as 64 rows j of X0 (contiguous
+// in i).
+template <bool GBF16, bool XF32>
+__global__ void __launch_bounds__(256) prep_cols_kernel(const PrepParams p, int vec) {
+  __shared__ float tile[64][65];
+  __shared__ float red[4];
+  const int ib = p.c_pad / 64;  // tiles along i (U rows = X0 columns)
+  const int jb = p.r_pad / 64;  // tiles along j (U cols = X0 rows)
+  const int per_mat = ib * jb;
+  const int mat = blockIdx.x / per_mat;
+  const int bl = blockIdx.x - mat * per_mat;
+  const int tj = bl / ib, ti = bl - tj * ib;
+  const MatPtrs mp = p.table[mat];
+  const int t = threadIdx.x;
+  float ss = 0.f;
+  {
+    const int c4 = (t & 15) * 4;
+    const int j = tj * 64 + c4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rl = (t >> 4) + 16 * q;
+      const int i = ti * 64 + rl;
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < p.m && j < p.n) {
+        const int valid = p.n - j;
+        const size_t idx = (size_t)i * p.n + j;
+        const bool v4 = vec && valid >= 4;
+        const float4 m = load_f4(mp.M + idx, v4, valid);
+        const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
+        float4 mn;
+        u = momentum4(m, g, p.mu, p.nesterov, &mn);
+        store_f4(mp.M + idx, mn, v4, valid);
+        if (valid < 4) {
+          if (valid < 2) u.y = 0.f;
+          if (valid < 3) u.z = 0.f;
+          u.w = 0.f;
+        }
+        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+      }
+      tile[rl][c4 + 0] = u.x;
+      tile[rl][c4 + 1] = u.y;
+      tile[rl][c4 + 2] = u.z;
+      tile[rl][c4 + 3] = u.w;
+    }
+  }
+  __syncthreads();
+  {
+    const int jl = t >> 2;          // X0 row within the tile
+    const int i0 = (t & 3) * 16;    // 16 consecutive X0 columns
+    const size_t xo = (size_t)mat * p.x_stride + (size_t)(tj * 64 + jl) * p.c_pad + ti * 64 + i0;
+    if (XF32) {
+      float* xp = (float*)p.X + xo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(xp + 4 * q) = make_float4(tile[i0 + 4 * q][jl], tile[i0 + 4 * q + 1][jl],
+                                             tile[i0 + 4 * q + 2][jl], tile[i0 + 4 * q + 3][jl]);
+    } else {
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = (uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q][jl]) |
+               ((uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q + 1][jl]) << 16);
+      uint4* xp = (uint4*)((uint16_t*)p.X + xo);
+      xp[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      xp[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
+  }
+  const float tot = block_sum<256>(ss, red);
+  if (threadIdx.x == 0) p.partials[(size_t)mat * p.blocks_per_mat + bl] = tot;
+}
+
+__global__ void __launch_bounds__(256) norm_finalize_kernel(const PrepParams p) {
+  __shared__ double red[4];
+  const int mat = blockIdx.x;
+  const float* part = p.partials + (size_t)mat * p.blocks_per_mat;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < p.blocks_per_mat; i += 256) s += (double)part[i];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double tot = red[0] + red[1] + red[2] + red[3];
+    p.inv_norm[mat] = tot > 0.0 ? (float)(1.0 / sqrt(tot)) : 0.0f;
+  }
+}
+
+int prep_blocks_per_mat(int r_pad, int c_pad, int transposed) {
+  if (transposed) return (c_pad / 64) * (r_pad / 64);
+  return ((c_pad + 1023) / 1024) * ((r_pad + PREP_ROWS - 1) / PREP_ROWS);
+}
+
+hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, int vec,
+                       hipStream_t s) {
+  const uint64_t blocks = (uint64_t)nmat * p.blocks_per_mat;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  const dim3 g((uint32_t)blocks), b(256);
+#define PREP_LAUNCH(K, GB, XF) hipLaunchKernelGGL((K<GB, XF>), g, b, 0, s, p, vec)
+  if (p.transposed) {
+    if (grad_bf16) {
+      if (x_f32) PREP_LAUNCH(prep_cols_kernel, true, true); else PREP_LAUNCH(prep_cols_kernel, true, false);
+    } else {
+      if (x_f32) PREP_LAUNCH(prep_cols_kernel, false, true); else PREP_LAUNCH(prep_cols_kernel, false, false);
+    }
+  } else {
+    if (grad_bf16) {
+      if (x_f32) PREP_LAUNCH(prep_rows_kernel, true, true); else PREP_LAUNCH(prep_rows_kernel, true, false);
+    } else {
+      if (x_f32) PREP_LAUNCH(prep_rows_kernel, false, true); else PREP_LAUNCH(prep_rows_kernel, false, false);
+    }
+  }
+#undef PREP_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const PrepParams& p, int nmat, hipStream_t s) {
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmat), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RowNorm, m <= n: one workgroup per row; U cached in registers (CH float4
+// chunks per thread), or re-read from M' and G when CH == 0 (very wide rows).
+template <bool GBF16, int CH>
+__global__ void __launch_bounds__(256) rownorm_rows_kernel(const RowNormParams p, int vec) {
+  __shared__ float red[4];
+  const int mat = blockIdx.x / p.m;
+  const int row = blockIdx.x - mat * p.m;
+  const MatPtrs mp = p.table[mat];
+  const size_t base = (size_t)row * p.n;
+  const int nc = (p.n + 3) / 4;
+  float ss = 0.f;
+  float4 ucache[CH > 0 ? CH : 1];
+#pragma unroll
+  for (int k = 0; k < (CH > 0 ? CH : 1); ++k) ucache[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = threadIdx.x + 256 * k;
+      if (c < nc) {
+        const int col = c * 4, valid = p.n - col;
+        const bool v4 = vec && valid >= 4;
+        const float4 m = load_f4(mp.M + base + col, v4, valid);
+        const float4 g = load_g4<GBF16>(mp.G, base + col, v4, valid);
+        float4 mn;
+        const float4 u = momentum4(m, g, p.mu, p.nesterov, &mn);
+        store_f4(mp.M + base + col, mn, v4, valid);
+        ucache[k] = u;
+        ss += u.x * u.x + u.y * u.y;
+        if (valid > 2) ss += u.z * u.z;
+        if (valid > 3) ss += u.w * u.w;
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < nc; c += 256) {
+      const int col = c * 4, valid = p.n - col;
+      const bool v4 = vec && valid >= 4;
+      const float4 m = load_f4(mp.M + base + col, v4, valid);
+      const float4 g = load_g4<GBF16>(mp.G, base + col, v4, valid);
+      float4 mn;
+      const float4 u = momentum4(m, g, p.mu, p.nesterov, &mn);
+      store_f4(mp.M + base + col, mn, v4, valid);
+      ss += u.x * u.x + u.y * u.y;
+      if (valid > 2) ss += u.z * u.z;
+      if (valid > 3) ss += u.w * u.w;
+    }
+  }
+  const float tot = block_sum<256>(ss, red);
+  const float inv = 1.0f / fmaxf(sqrtf(tot), p.eps);
+  auto apply = [&](int col, float4 u) {
+    const int valid = p.n - col;
+    const bool v4 = vec && valid >= 4;
+    const float4 r = make_float4(u.x * inv, u.y * inv, u.z * inv, u.w * inv);
+    float4 w = load_f4(mp.W + base + col, v4, valid);
+    w.x = p.decay * w.x - p.step * r.x;
+    w.y = p.decay * w.y - p.step * r.y;
+    w.z = p.decay * w.z - p.step * r.z;
+    w.w = p.decay * w.w - p.step * r.w;
+    store_f4(mp.W + base + col, w, v4, valid);
+    if (mp.O) store_f4(mp.O + base + col, r, v4, valid);
+  };
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = threadIdx.x + 256 * k;
+      if (c < nc) apply(c * 4, ucache[k]);
+    }
+  } else {
+    __syncthreads();  // M' of this row is visible to the re-read below
+    for (int c = threadIdx.x; c < nc; c += 256) {
+      const int col = c * 4, valid = p.n - col;
+      const bool v4 = vec && valid >= 4;
+      const float4 mn = load_f4(mp.M + base + col, v4, valid);
+      const float4 g = load_g4<GBF16>(mp.G, base + col, v4, valid);
+      const float4 u = p.nesterov ? make_float4(p.mu * mn.x + g.x, p.mu * mn.y + g.y,
+                                                p.mu * mn.z + g.z, p.mu * mn.w + g.w)
+                                  : mn;
+      apply(col, u);
+    }
+  }
+}
+
+// RowNorm, m > n.  Pass A: M update and column sums of U^2 over a block of
+// RN_ROWS rows (fixed-order partials).  Each thread owns 4 columns.
+constexpr int RN_ROWS = 256;
+
+template <bool GBF16>
+__global__ void __launch_bounds__(256) rownorm_colsum_kernel(const RowNormParams p, int vec) {
+  const int cblocks = (p.n + 1023) / 1024;
+  const int per_mat = cblocks * p.row_blocks;
+  const int mat = blockIdx.x / per_mat;
+  const int bl = blockIdx.x - mat * per_mat;
+  const int rb = bl / cblocks, cb = bl - rb * cblocks;
+  const MatPtrs mp = p.table[mat];
+  const int col = cb * 1024 + threadIdx.x * 4;
+  if (col >= p.n) return;
+  const int valid = p.n - col;
+  const bool v4 = vec && valid >= 4;
+  float4 ss = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int r0 = rb * RN_ROWS, r1 = min(p.m, r0 + RN_ROWS);
+  for (int row = r0; row < r1; ++row) {
+    const size_t idx = (size_t)row * p.n + col;
+    const float4 m = load_f4(mp.M + idx, v4, valid);
+    const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
+    float4 mn;
+    const float4 u = momentum4(m, g, p.mu, p.nesterov, &mn);
+    store_f4(mp.M + idx, mn, v4, valid);
+    ss.x += u.x * u.x;
+    ss.y += u.y * u.y;
+    ss.z += u.z * u.z;
+    ss.w += u.w * u.w;
+  }
+  float* dst = p.partials + ((size_t)mat * p.row_blocks + rb) * p.n + col;
+  store_f4(dst, ss, v4, valid);
+}
+
+__global__ void __launch_bounds__(256) rownorm_colfinal_kernel(const RowNormParams p) {
+  const int cb = (p.n + 255) / 256;
+  const int mat = blockIdx.x / cb;
+  const int col = (blockIdx.x - mat * cb) * 256 + threadIdx.x;
+  if (col >= p.n) return;
+  const float* part = p.partials + (size_t)mat * p.row_blocks * p.n + col;
+  double s = 0.0;
+  for (int rb = 0; rb < p.row_blocks; ++rb) s += (double)part[(size_t)rb * p.n];
+  const float nrm = (float)sqrt(s);
+  p.colscale[(size_t)mat * p.n + col] = 1.0f / fmaxf(nrm, p.eps);
+}
+
+template <bool GBF16>
+__global__ void __launch_bounds__(256) rownorm_colapply_kernel(const RowNormParams p, int vec) {
+  const int cblocks = (p.n + 1023) / 1024;
+  const int per_mat = cblocks * p.row_blocks;
+  const int mat = blockIdx.x / per_mat;
+  const int bl = blockIdx.x - mat * per_mat;
+  const int rb = bl / cblocks, cb = bl - rb * cblocks;
+  const MatPtrs mp = p.table[mat];
+  const int col = cb * 1024 + threadIdx.x * 4;
+  if (col >= p.n) return;
+  const int valid = p.n - col;
+  const bool v4 = vec && valid >= 4;
+  const float4 sc = load_f4(p.colscale + (size_t)mat * p.n + col, v4, valid);
+  const int r0 = rb * RN_ROWS, r1 = min(p.m, r0 + RN_ROWS);
+  for (int row = r0; row < r1; ++row) {
+    const size_t idx = (size_t)row * p.n + col;
+    const float4 mn = load_f4(mp.M + idx, v4, valid);
+    const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
+    const float4 u = p.nesterov ? make_float4(p.mu * mn.x + g.x, p.mu * mn.y + g.y,
+                                              p.mu * mn.z + g.z, p.mu * mn.w + g.w)
+                                : mn;
+    const float4 r = make_float4(u.x * sc.x, u.y * sc.y, u.z * sc.z, u.w * sc.w);
+    float4 w = load_f4(mp.W + idx, v4, valid);
+    w.x = p.decay * w.x - p.step * r.x;
+    w.y = p.decay * w.y - p.step * r.y;
+    w.z = p.decay * w.z - p.step * r.z;
+    w.w = p.decay * w.w - p.step * r.w;
+    store_f4(mp.W + idx, w, v4, valid);
+    if (mp.O) store_f4(mp.O + idx, r, v4, valid);
+  }
+}
+
+int rownorm_row_blocks(int m, int n) {
+  (void)n;
+  return (m + RN_ROWS - 1) / RN_ROWS;
+}
+
+hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec,
+                          hipStream_t s) {
+  if (nmat == 0) return hipSuccess;
+  const dim3 b(256);
+  if (p.m <= p.n) {
+    const uint64_t blocks = (uint64_t)nmat * p.m;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+    const int nc = (p.n + 3) / 4;
+    const dim3 g((uint32_t)blocks);
+#define RN_ROWS_LAUNCH(GB)                                                               \
+  do {                                                                                   \
+    if (nc <= 256) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 1>), g, b, 0, s, p, vec); \
+    else if (nc <= 1024) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 4>), g, b, 0, s, p, vec); \
+    else if (nc <= 4096) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 16>), g, b, 0, s, p, vec); \
+    else hipLaunchKernelGGL((rownorm_rows_kernel<GB, 0>), g, b, 0, s, p, vec);           \
+  } while (0)
+    if (grad_bf16) RN_ROWS_LAUNCH(true); else RN_ROWS_LAUNCH(false);
+#undef RN_ROWS_LAUNCH
+    return hipGetLastError();
+  }
+  const uint64_t blocks = (uint64_t)nmat * p.row_blocks * ((p.n + 1023) / 1024);
+  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  const dim3 g((uint32_t)blocks);
+  if (grad_bf16) hipLaunchKernelGGL((rownorm_colsum_kernel<true>), g, b, 0, s, p, vec);
+  else hipLaunchKernelGGL((rownorm_colsum_kernel<false>), g, b, 0, s, p, vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rownorm_colfinal_kernel, dim3((uint32_t)(nmat * ((p.n + 255) / 256))), b, 0,
+                     s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (grad_bf16) hipLaunchKernelGGL((rownorm_colapply_kernel<true>), g, b, 0, s, p, vec);
+  else hipLaunchKernelGGL((rownorm_colapply_kernel<false>), g, b, 0, s, p, vec);
+  return hipGetLastError();
+}
+
+}  // namespace muon

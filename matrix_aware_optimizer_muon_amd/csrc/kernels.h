@@ -1,0 +1,95 @@
+// Internal launch interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// One entry per matrix, in plan order (device-resident table).
+struct MatPtrs {
+  float* W;
+  float* M;
+  const void* G;
+  float* O;  // nullable direction output
+};
+
+enum Epi : int { EPI_SYRK = 0, EPI_POLY = 1, EPI_PQPG = 2, EPI_PH = 3, EPI_FINAL = 4 };
+enum OpType : int { OP_BF16 = 0, OP_F32 = 1 };
+
+// Parameters of one batched GEMM launch C = A * B^T over a chunk of
+// same-shape matrices, plus its fused epilogue.  All matrices of the chunk
+// use the same strides; matrix `mat` of the chunk adds mat*stride.
+struct GemmParams {
+  const void* A;
+  const void* B;
+  const void* B2;          // second B operand of a two-product launch
+  int64_t a_stride, b_stride, b2_stride;  // elements between matrices
+  int lda, ldb;            // leading dimensions (elements)
+  int Mdim, Ndim, Kdim;    // padded sizes (multiples of the tile / K step)
+  int tiles_m, tiles_n;
+  int triangular;          // lower-triangle tiles only (symmetric result)
+  int tiles_per_prod;      // tiles of one product of one matrix
+  int products;            // 1 or 2
+  int prod_base;           // epilogue product index of the first product
+  // r x r recursion buffers (fp32 master copies and MFMA operand copies)
+  float* Gf;
+  float* Qf_src;
+  float* Qf_dst;
+  float* Hf;
+  void* Gh;
+  void* Ph;
+  void* Qh_dst;
+  void* Hh;
+  int64_t rr_stride;       // elements between matrices in r x r buffers
+  int ldr;                 // r_pad
+  float a, b, c;           // quintic coefficients
+  float sG, sP, sQ, sH;    // power-of-two operand scales
+  int first, last;
+  // final update
+  const MatPtrs* table;    // chunk's first entry
+  const float* inv_norm;   // per matrix of the chunk
+  int out_rows, out_cols;  // m, n of the parameter
+  float decay;             // 1 - lr*wd
+  float step;              // lr * scale_coeff * sqrt(max(m, n))
+};
+
+hipError_t launch_gemm(const GemmParams& p, int epi, int op, int bt, int a_kstrided,
+                       int b_kstrided, int nmat, hipStream_t s);
+
+// ---- memory-bound kernels ------------------------------------------------
+struct PrepParams {
+  const MatPtrs* table;
+  int m, n;                // parameter shape
+  int r_pad, c_pad;        // X~ padded shape (r x c oriented)
+  int transposed;          // m > n
+  float mu;
+  int nesterov;
+  void* X;                 // X~ for matrix 0 of the chunk
+  int64_t x_stride;        // elements between matrices
+  float* partials;         // [nmat][blocks_per_mat]
+  int blocks_per_mat;
+  float* inv_norm;         // [nmat]
+};
+
+hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, int vec,
+                       hipStream_t s);
+hipError_t launch_norm_finalize(const PrepParams& p, int nmat, hipStream_t s);
+int prep_blocks_per_mat(int r_pad, int c_pad, int transposed);
+
+struct RowNormParams {
+  const MatPtrs* table;
+  int m, n;
+  float mu;
+  int nesterov;
+  float eps;
+  float decay, step;
+  float* partials;         // tall case: [nmat][row_blocks][n]
+  float* colscale;         // tall case: [nmat][n]
+  int row_blocks;
+};
+
+hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec, hipStream_t s);
+int rownorm_row_blocks(int m, int n);
+
+}  // namespace muon

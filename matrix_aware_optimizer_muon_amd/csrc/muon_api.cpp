@@ -1,0 +1,591 @@
+// C ABI of libmuon: planner, validation and launch sequence.
+//
+// Planner ("DMuon" 2.2 batching): matrices are bucketed by shape (m, n);
+// each bucket gets the short-side orientation of "Scaling Muon for DiT" 3.1
+// (transpose iff m > n), a GEMM tile size chosen from r = min(m, n), padded
+// sizes r_pad / c_pad (multiples of the tile, zero filled), and is split into
+// equal chunks whose Newton-Schulz scratch fits the workspace cap.  Chunks run
+// one after another on the caller's stream and reuse one scratch region.
+//
+// Per chunk the refresh step enqueues:
+//   prep (M update, U, ||U||^2 partials, X0 = O(U))  -> finalize (1/||U||)
+//   -> SYRK G0 -> N x {POLY, PQ(+PG), PH} -> FINAL (O = Q X0, W update)
+// which evaluates "Infra Optimizers" eq. (2) in the Gram space:
+//   X_N = P_N ... P_1 X0,  P_k = a I + b G_{k-1} + c G_{k-1}^2,
+//   G_k = P_k G_{k-1} P_k  (all P, G commute),
+// with P_k = a I + P~_k, H = P G = a G + P~ G, G_k = P H = a H + P~ H and
+// Q_k = P_k Q_{k-1} = a Q_{k-1} + P~_k Q_{k-1}, so every MFMA product acts on
+// the non-identity part and the identity terms are added in fp32.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "muon.h"
+
+using namespace muon;
+
+namespace {
+
+constexpr int64_t kDefaultCap = 16ll << 30;   // Newton-Schulz scratch cap (bytes)
+constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
+constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
+constexpr int kRing = 4;                      // pinned descriptor staging slots
+
+// Operand scales (powers of two, exact) of the fp16 r x r recursion.  They
+// keep every operand inside fp16's normal range: eigenvalues of G lie in
+// [0, 1.45] (f^k maps [0, 1] into [0, 1.2025]), of P~ = b G + c G^2 in
+// [-2.81, 0], of H = P G in [0, 5.0], of Q = P_k...P_1 in [0, a^N]; entries
+// are bounded by the largest eigenvalue in magnitude.
+constexpr float kSG = 16384.0f, kSP = 16384.0f, kSH = 8192.0f, kSQ = 64.0f;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Chunk {
+  int first;  // index into plan order
+  int count;
+};
+
+struct Bucket {
+  int64_t m, n, r, c, r_pad, c_pad;
+  bool transposed;
+  int bt;
+  int first, count;  // range in plan order
+  std::vector<Chunk> chunks;
+  int64_t scratch_per_mat;
+  int prep_blocks;
+  int rn_row_blocks;
+};
+
+struct Slot {
+  void* host = nullptr;
+  hipEvent_t ev = nullptr;
+  bool used = false;
+};
+
+}  // namespace
+
+struct muon_plan_s {
+  int64_t nmat = 0;
+  muon_dtype grad_dtype = MUON_F32;
+  muon_dtype ns_dtype = MUON_BF16;
+  muon_hparams hp{};
+  std::vector<int64_t> rows, cols;
+  std::vector<int> order;  // plan position -> caller index
+  std::vector<Bucket> buckets;
+  // workspace layout
+  size_t off_table = 0, off_inv = 0, off_part = 0, off_colscale = 0, off_scratch = 0;
+  size_t ws_bytes = 0;
+  size_t max_scratch = 0;
+  // descriptor staging
+  Slot ring[kRing];
+  int next_slot = 0;
+  bool ring_ready = false;
+  std::vector<MatPtrs> host_table;
+};
+
+namespace {
+
+bool finite(float x) { return std::isfinite(x); }
+
+muon_status validate_hp(const muon_hparams& hp) {
+  if (!finite(hp.momentum) || hp.momentum < 0.0f || hp.momentum > 1.0f) return MUON_ERR_INVALID_ARGUMENT;
+  if (hp.nesterov != 0 && hp.nesterov != 1) return MUON_ERR_INVALID_ARGUMENT;
+  if (hp.ns_steps < 1) return MUON_ERR_INVALID_ARGUMENT;
+  if (hp.ns_steps > 16) return MUON_ERR_UNSUPPORTED;
+  if (!finite(hp.a) || !finite(hp.b) || !finite(hp.c)) return MUON_ERR_INVALID_ARGUMENT;
+  if (!finite(hp.scale_coeff) || hp.scale_coeff < 0.0f) return MUON_ERR_INVALID_ARGUMENT;
+  if (!finite(hp.rownorm_eps) || !(hp.rownorm_eps > 0.0f)) return MUON_ERR_INVALID_ARGUMENT;
+  return MUON_OK;
+}
+
+int choose_tile(int64_t r, bool f32path) {
+  if (r <= 64) return 64;
+  if (f32path || r <= 768) return 128;
+  return 256;
+}
+
+void release_ring(muon_plan_s* p) {
+  for (auto& s : p->ring) {
+    if (s.ev) (void)hipEventDestroy(s.ev);
+    if (s.host) (void)hipHostFree(s.host);
+    s.ev = nullptr;
+    s.host = nullptr;
+    s.used = false;
+  }
+  p->ring_ready = false;
+}
+
+muon_status ensure_ring(muon_plan_s* p) {
+  if (p->ring_ready) return MUON_OK;
+  const size_t bytes = sizeof(MatPtrs) * (size_t)p->nmat;
+  for (auto& s : p->ring) {
+    if (hipHostMalloc(&s.host, bytes, hipHostMallocDefault) != hipSuccess) {
+      s.host = nullptr;
+      release_ring(p);
+      return MUON_ERR_HIP;
+    }
+    if (hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
+      s.ev = nullptr;
+      release_ring(p);
+      return MUON_ERR_HIP;
+    }
+  }
+  p->ring_ready = true;
+  return MUON_OK;
+}
+
+// Upload the per-matrix pointer table into the workspace (one H->D copy per
+// call, from a pinned slot that is reused only after its previous copy ran).
+muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
+  muon_status st = ensure_ring(p);
+  if (st != MUON_OK) return st;
+  Slot& s = p->ring[p->next_slot];
+  p->next_slot = (p->next_slot + 1) % kRing;
+  if (s.used && hipEventSynchronize(s.ev) != hipSuccess) return MUON_ERR_HIP;
+  const size_t bytes = sizeof(MatPtrs) * (size_t)p->nmat;
+  std::memcpy(s.host, p->host_table.data(), bytes);
+  if (hipMemcpyAsync((char*)ws + p->off_table, s.host, bytes, hipMemcpyHostToDevice, stream) !=
+      hipSuccess)
+    return MUON_ERR_HIP;
+  if (hipEventRecord(s.ev, stream) != hipSuccess) return MUON_ERR_HIP;
+  s.used = true;
+  return MUON_OK;
+}
+
+muon_status validate_call(muon_plan_s* p, float* const* W, float* const* M, const void* const* G,
+                          float lr, float wd, void* ws, size_t ws_bytes) {
+  if (!p || !W || !M || !G || !ws) return MUON_ERR_INVALID_ARGUMENT;
+  if (!finite(lr) || !finite(wd)) return MUON_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)ws & 255u) != 0) return MUON_ERR_INVALID_ARGUMENT;
+  for (int64_t i = 0; i < p->nmat; ++i)
+    if (!W[i] || !M[i] || !G[i]) return MUON_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p->ws_bytes) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  return MUON_OK;
+}
+
+void fill_table(muon_plan_s* p, float* const* W, float* const* M, const void* const* G,
+                float* const* O) {
+  p->host_table.resize((size_t)p->nmat);
+  for (int64_t k = 0; k < p->nmat; ++k) {
+    const int i = p->order[(size_t)k];
+    p->host_table[(size_t)k] = MatPtrs{W[i], M[i], G[i], O ? O[i] : nullptr};
+  }
+}
+
+// Vector (16-byte) access is valid for a chunk when n is a multiple of 4 and
+// every pointer of the chunk is 16-byte aligned.
+int chunk_vec(const muon_plan_s* p, const Bucket& b, const Chunk& ch) {
+  if (b.n % 4 != 0) return 0;
+  for (int k = ch.first; k < ch.first + ch.count; ++k) {
+    const MatPtrs& e = p->host_table[(size_t)k];
+    const uintptr_t bits = (uintptr_t)e.W | (uintptr_t)e.M | (uintptr_t)e.G | (uintptr_t)e.O;
+    if (bits & 15u) return 0;
+  }
+  return 1;
+}
+
+muon_status hip_ok(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_default_hparams(muon_hparams* hp) {
+  if (!hp) return MUON_ERR_INVALID_ARGUMENT;
+  hp->momentum = 0.95f;
+  hp->nesterov = 1;
+  hp->ns_steps = 5;
+  hp->a = 3.4445f;
+  hp->b = -4.7750f;
+  hp->c = 2.0315f;
+  hp->scale_coeff = 0.2f;
+  hp->rownorm_eps = 1e-8f;
+  return MUON_OK;
+}
+
+const char* muon_status_string(muon_status s) {
+  switch (s) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARGUMENT: return "MUON_ERR_INVALID_ARGUMENT";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "MUON_ERR_WORKSPACE_TOO_SMALL";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+  }
+  return "MUON_UNKNOWN_STATUS";
+}
+
+muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* workspace_bytes) {
+  if (!desc || !plan) return MUON_ERR_INVALID_ARGUMENT;
+  *plan = nullptr;
+  if (desc->num_matrices < 1 || !desc->rows || !desc->cols) return MUON_ERR_INVALID_ARGUMENT;
+  if (desc->num_matrices > (1ll << 24)) return MUON_ERR_UNSUPPORTED;
+  if (desc->grad_dtype != MUON_F32 && desc->grad_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
+  if (desc->ns_dtype != MUON_F32 && desc->ns_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
+  if (desc->max_workspace_bytes < 0) return MUON_ERR_INVALID_ARGUMENT;
+  muon_status st = validate_hp(desc->hp);
+  if (st != MUON_OK) return st;
+  for (int64_t i = 0; i < desc->num_matrices; ++i) {
+    const int64_t m = desc->rows[i], n = desc->cols[i];
+    if (m < 1 || n < 1) return MUON_ERR_INVALID_ARGUMENT;
+    if (m > kMaxDim || n > kMaxDim || std::min(m, n) > kMaxShort) return MUON_ERR_UNSUPPORTED;
+  }
+  muon_plan_s* p = nullptr;
+  try {
+    p = new muon_plan_s();
+    p->nmat = desc->num_matrices;
+    p->grad_dtype = desc->grad_dtype;
+    p->ns_dtype = desc->ns_dtype;
+    p->hp = desc->hp;
+    p->rows.assign(desc->rows, desc->rows + desc->num_matrices);
+    p->cols.assign(desc->cols, desc->cols + desc->num_matrices);
+    const bool f32path = desc->ns_dtype == MUON_F32;
+    const int64_t cap = desc->max_workspace_bytes > 0 ? desc->max_workspace_bytes : kDefaultCap;
+
+    // buckets in order of first appearance
+    std::vector<std::vector<int>> members;
+    for (int64_t i = 0; i < p->nmat; ++i) {
+      size_t b = 0;
+      for (; b < p->buckets.size(); ++b)
+        if (p->buckets[b].m == p->rows[i] && p->buckets[b].n == p->cols[i]) break;
+      if (b == p->buckets.size()) {
+        Bucket nb{};
+        nb.m = p->rows[i];
+        nb.n = p->cols[i];
+        p->buckets.push_back(nb);
+        members.emplace_back();
+      }
+      members[b].push_back((int)i);
+    }
+    size_t part_floats = 0, colscale_floats = 0, max_scratch = 0;
+    for (size_t b = 0; b < p->buckets.size(); ++b) {
+      Bucket& B = p->buckets[b];
+      B.transposed = B.m > B.n;
+      B.r = std::min(B.m, B.n);
+      B.c = std::max(B.m, B.n);
+      B.bt = choose_tile(B.r, f32path);
+      B.r_pad = round_up(B.r, B.bt);
+      B.c_pad = round_up(B.c, B.bt);
+      B.first = (int)p->order.size();
+      B.count = (int)members[b].size();
+      for (int i : members[b]) p->order.push_back(i);
+      const int64_t xes = f32path ? 4 : 2;
+      const int64_t rr = B.r_pad * B.r_pad;
+      B.scratch_per_mat = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes)) +
+                          (f32path ? 5 * (int64_t)align256((size_t)(rr * 4))
+                                   : 4 * (int64_t)align256((size_t)(rr * 4)) +
+                                         5 * (int64_t)align256((size_t)(rr * 2)));
+      int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
+      per_chunk = std::min<int64_t>(per_chunk, B.count);
+      const int64_t nchunks = (B.count + per_chunk - 1) / per_chunk;
+      const int64_t even = (B.count + nchunks - 1) / nchunks;
+      for (int64_t f = 0; f < B.count; f += even)
+        B.chunks.push_back(Chunk{B.first + (int)f, (int)std::min<int64_t>(even, B.count - f)});
+      B.prep_blocks = prep_blocks_per_mat((int)B.r_pad, (int)B.c_pad, B.transposed ? 1 : 0);
+      B.rn_row_blocks = rownorm_row_blocks((int)B.m, (int)B.n);
+      max_scratch = std::max(max_scratch, (size_t)(even * B.scratch_per_mat));
+      part_floats = std::max(part_floats, (size_t)even * (size_t)B.prep_blocks);
+      if (B.transposed) {
+        // RowNorm runs on whole buckets (no NS scratch needed)
+        part_floats = std::max(part_floats, (size_t)B.count * B.rn_row_blocks * (size_t)B.n);
+        colscale_floats = std::max(colscale_floats, (size_t)B.count * (size_t)B.n);
+      }
+    }
+    p->off_table = 0;
+    p->off_inv = align256(sizeof(MatPtrs) * (size_t)p->nmat);
+    p->off_part = p->off_inv + align256(sizeof(float) * (size_t)p->nmat);
+    p->off_colscale = p->off_part + align256(sizeof(float) * std::max<size_t>(part_floats, 1));
+    p->off_scratch = p->off_colscale + align256(sizeof(float) * std::max<size_t>(colscale_floats, 1));
+    p->max_scratch = max_scratch;
+    p->ws_bytes = p->off_scratch + max_scratch;
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  *plan = p;
+  if (workspace_bytes) *workspace_bytes = p->ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_destroy(muon_plan_t plan) {
+  if (!plan) return MUON_OK;
+  release_ring(plan);
+  delete plan;
+  return MUON_OK;
+}
+
+muon_status muon_plan_workspace_size(muon_plan_t plan, size_t* workspace_bytes) {
+  if (!plan || !workspace_bytes) return MUON_ERR_INVALID_ARGUMENT;
+  *workspace_bytes = plan->ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_info(muon_plan_t plan, int64_t* num_buckets, int64_t* num_chunks) {
+  if (!plan) return MUON_ERR_INVALID_ARGUMENT;
+  int64_t nc = 0;
+  for (const auto& b : plan->buckets) nc += (int64_t)b.chunks.size();
+  if (num_buckets) *num_buckets = (int64_t)plan->buckets.size();
+  if (num_chunks) *num_chunks = nc;
+  return MUON_OK;
+}
+
+muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
+                              float lr, float wd, void* ws, size_t ws_bytes, hipStream_t stream,
+                              float* const* O_out) {
+  muon_status st = validate_call(p, W, M, G, lr, wd, ws, ws_bytes);
+  if (st != MUON_OK) return st;
+  try {
+    fill_table(p, W, M, G, O_out);
+  } catch (const std::bad_alloc&) {
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  st = upload_table(p, ws, stream);
+  if (st != MUON_OK) return st;
+
+  char* wsb = (char*)ws;
+  const MatPtrs* d_table = (const MatPtrs*)(wsb + p->off_table);
+  float* d_inv = (float*)(wsb + p->off_inv);
+  float* d_part = (float*)(wsb + p->off_part);
+  char* scratch = wsb + p->off_scratch;
+  const bool f32path = p->ns_dtype == MUON_F32;
+  const int op = f32path ? OP_F32 : OP_BF16;
+  const int xes = f32path ? 4 : 2;
+  const int gbf16 = p->grad_dtype == MUON_BF16 ? 1 : 0;
+  const muon_hparams& hp = p->hp;
+  const int N = hp.ns_steps;
+
+  for (const Bucket& B : p->buckets) {
+    const int64_t rr = B.r_pad * B.r_pad;
+    const int T = (int)(B.r_pad / B.bt);
+    const int ntri = T * (T + 1) / 2;
+    for (const Chunk& ch : B.chunks) {
+      const int nm = ch.count;
+      // scratch layout for this chunk
+      size_t off = 0;
+      auto take = [&](size_t per_mat_bytes) {
+        char* q = scratch + off;
+        off += align256(per_mat_bytes) * (size_t)nm;
+        return q;
+      };
+      // per-matrix strides must be uniform: use the aligned per-matrix size
+      const size_t xbytes = align256((size_t)(B.r_pad * B.c_pad * xes));
+      const size_t f32b = align256((size_t)(rr * 4));
+      const size_t h16b = f32path ? f32b : align256((size_t)(rr * 2));
+      void* X = take(xbytes);
+      float* Gf = (float*)take(f32b);
+      float* Qf[2] = {(float*)take(f32b), (float*)take(f32b)};
+      float* Hf = (float*)take(f32b);
+      void* Gh;
+      void* Ph;
+      void* Qh[2];
+      void* Hh;
+      if (f32path) {
+        Gh = Gf;
+        Ph = take(f32b);
+        Qh[0] = Qf[0];
+        Qh[1] = Qf[1];
+        Hh = Hf;
+      } else {
+        Gh = take(h16b);
+        Ph = take(h16b);
+        Qh[0] = take(h16b);
+        Qh[1] = take(h16b);
+        Hh = take(h16b);
+      }
+      const int64_t x_stride = (int64_t)(xbytes / xes);
+      const int64_t rr_stride = (int64_t)(f32b / 4);
+      const int64_t h_stride = (int64_t)(h16b / (f32path ? 4 : 2));
+      // the epilogues index fp32 and 16-bit r x r buffers with one element
+      // stride; r_pad is a multiple of 64, so both are exactly r_pad^2
+      if (rr_stride != h_stride || rr_stride != rr) return MUON_ERR_HIP;
+      const int vec = chunk_vec(p, B, ch);
+
+      PrepParams pp{};
+      pp.table = d_table + ch.first;
+      pp.m = (int)B.m;
+      pp.n = (int)B.n;
+      pp.r_pad = (int)B.r_pad;
+      pp.c_pad = (int)B.c_pad;
+      pp.transposed = B.transposed ? 1 : 0;
+      pp.mu = hp.momentum;
+      pp.nesterov = hp.nesterov;
+      pp.X = X;
+      pp.x_stride = x_stride;
+      pp.partials = d_part;
+      pp.blocks_per_mat = B.prep_blocks;
+      pp.inv_norm = d_inv + ch.first;
+      st = hip_ok(launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream));
+      if (st != MUON_OK) return st;
+      st = hip_ok(launch_norm_finalize(pp, nm, stream));
+      if (st != MUON_OK) return st;
+
+      GemmParams g{};
+      g.rr_stride = rr_stride;
+      g.ldr = (int)B.r_pad;
+      g.a = hp.a;
+      g.b = hp.b;
+      g.c = hp.c;
+      if (f32path) {
+        g.sG = g.sP = g.sQ = g.sH = 1.0f;
+      } else {
+        g.sG = kSG;
+        g.sP = kSP;
+        g.sQ = kSQ;
+        g.sH = kSH;
+      }
+      g.inv_norm = d_inv + ch.first;
+      g.table = d_table + ch.first;
+      g.Gf = Gf;
+      g.Hf = Hf;
+      g.Gh = Gh;
+      g.Ph = Ph;
+      g.Hh = Hh;
+      g.products = 1;
+      auto rr_setup = [&](const void* A, const void* Bop, const void* B2, int products) {
+        g.A = A;
+        g.B = Bop;
+        g.B2 = B2;
+        g.a_stride = g.b_stride = g.b2_stride = h_stride;
+        g.lda = g.ldb = (int)B.r_pad;
+        g.Mdim = g.Ndim = g.Kdim = (int)B.r_pad;
+        g.tiles_m = g.tiles_n = T;
+        g.triangular = 1;
+        g.tiles_per_prod = ntri;
+        g.products = products;
+      };
+
+      // G0 = X0 X0^T / ||U||^2
+      g.A = g.B = g.B2 = X;
+      g.a_stride = g.b_stride = g.b2_stride = x_stride;
+      g.lda = g.ldb = (int)B.c_pad;
+      g.Mdim = g.Ndim = (int)B.r_pad;
+      g.Kdim = (int)B.c_pad;
+      g.tiles_m = g.tiles_n = T;
+      g.triangular = 1;
+      g.tiles_per_prod = ntri;
+      g.products = 1;
+      st = hip_ok(launch_gemm(g, EPI_SYRK, op, B.bt, 0, 0, nm, stream));
+      if (st != MUON_OK) return st;
+
+      for (int k = 0; k < N; ++k) {
+        const int dst = k & 1, src = dst ^ 1;
+        g.first = k == 0;
+        g.last = k == N - 1;
+        g.Qf_src = Qf[src];
+        g.Qf_dst = Qf[dst];
+        g.Qh_dst = Qh[dst];
+        // P~ = b G + c G^2 (and Q1 = a I + P~ on the first iteration)
+        rr_setup(Gh, Gh, Gh, 1);
+        st = hip_ok(launch_gemm(g, EPI_POLY, op, B.bt, 0, 0, nm, stream));
+        if (st != MUON_OK) return st;
+        const bool need_q = k > 0;
+        const bool need_h = k < N - 1;
+        if (need_q || need_h) {
+          // PQ: Q_k = a Q_{k-1} + P~ Q_{k-1};  PG: H = a G + P~ G
+          if (need_q && need_h) {
+            rr_setup(Ph, Qh[src], Gh, 2);
+            g.prod_base = 0;
+          } else if (need_q) {
+            rr_setup(Ph, Qh[src], Qh[src], 1);
+            g.prod_base = 0;
+          } else {  // first iteration: Q1 came from the POLY epilogue
+            rr_setup(Ph, Gh, Gh, 1);
+            g.prod_base = 1;
+          }
+          st = hip_ok(launch_gemm(g, EPI_PQPG, op, B.bt, 0, 0, nm, stream));
+          g.prod_base = 0;
+          if (st != MUON_OK) return st;
+        }
+        if (need_h) {
+          // G_k = a H + P~ H
+          rr_setup(Ph, Hh, Hh, 1);
+          st = hip_ok(launch_gemm(g, EPI_PH, op, B.bt, 0, 0, nm, stream));
+          if (st != MUON_OK) return st;
+        }
+      }
+
+      // O = Q X0 / ||U||;  W <- (1 - lr wd) W - lr s O   (with O^-1 orientation)
+      const void* Qfinal = f32path ? (const void*)Qf[(N - 1) & 1] : (const void*)Qh[(N - 1) & 1];
+      GemmParams fg = g;
+      fg.Kdim = (int)B.r_pad;
+      fg.triangular = 0;
+      fg.products = 1;
+      fg.out_rows = (int)B.m;
+      fg.out_cols = (int)B.n;
+      fg.decay = (float)(1.0 - (double)lr * wd);
+      fg.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
+      int aks, bks;
+      if (!B.transposed) {  // O (r x c) = Q (r x r) * X0 (r x c): B K-strided
+        fg.A = Qfinal;
+        fg.a_stride = h_stride;
+        fg.lda = (int)B.r_pad;
+        fg.B = fg.B2 = X;
+        fg.b_stride = fg.b2_stride = x_stride;
+        fg.ldb = (int)B.c_pad;
+        fg.Mdim = (int)B.r_pad;
+        fg.Ndim = (int)B.c_pad;
+        aks = 0;
+        bks = 1;
+      } else {  // O^T (c x r) = X0^T (c x r) * Q: A K-strided
+        fg.A = X;
+        fg.a_stride = x_stride;
+        fg.lda = (int)B.c_pad;
+        fg.B = fg.B2 = Qfinal;
+        fg.b_stride = fg.b2_stride = h_stride;
+        fg.ldb = (int)B.r_pad;
+        fg.Mdim = (int)B.c_pad;
+        fg.Ndim = (int)B.r_pad;
+        aks = 1;
+        bks = 0;
+      }
+      fg.tiles_m = fg.Mdim / B.bt;
+      fg.tiles_n = fg.Ndim / B.bt;
+      fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
+      st = hip_ok(launch_gemm(fg, EPI_FINAL, op, B.bt, aks, bks, nm, stream));
+      if (st != MUON_OK) return st;
+    }
+  }
+  return MUON_OK;
+}
+
+muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
+                         float lr, float wd, void* ws, size_t ws_bytes, hipStream_t stream,
+                         float* const* R_out) {
+  muon_status st = validate_call(p, W, M, G, lr, wd, ws, ws_bytes);
+  if (st != MUON_OK) return st;
+  try {
+    fill_table(p, W, M, G, R_out);
+  } catch (const std::bad_alloc&) {
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  st = upload_table(p, ws, stream);
+  if (st != MUON_OK) return st;
+  char* wsb = (char*)ws;
+  const MatPtrs* d_table = (const MatPtrs*)(wsb + p->off_table);
+  const int gbf16 = p->grad_dtype == MUON_BF16 ? 1 : 0;
+  for (const Bucket& B : p->buckets) {
+    RowNormParams rp{};
+    rp.table = d_table + B.first;
+    rp.m = (int)B.m;
+    rp.n = (int)B.n;
+    rp.mu = p->hp.momentum;
+    rp.nesterov = p->hp.nesterov;
+    rp.eps = p->hp.rownorm_eps;
+    rp.decay = (float)(1.0 - (double)lr * wd);
+    rp.step = (float)((double)lr * p->hp.scale_coeff * std::sqrt((double)B.c));
+    rp.partials = (float*)(wsb + p->off_part);
+    rp.colscale = (float*)(wsb + p->off_colscale);
+    rp.row_blocks = B.rn_row_blocks;
+    const int vec = chunk_vec(p, B, Chunk{B.first, B.count});
+    st = hip_ok(launch_rownorm(rp, gbf16, B.count, vec, stream));
+    if (st != MUON_OK) return st;
+  }
+  return MUON_OK;
+}
+
+}  // extern "C"

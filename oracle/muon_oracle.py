@@ -168,16 +168,19 @@ def apply_update(W, D, lr: float, wd: float, scale: float) -> np.ndarray:
     return (1.0 - lr * wd) * _f64(W) - lr * scale * _f64(D)
 
 
-def muon_step(W, M, G, lr: float, wd: float, hp: Hyper = Hyper()):
+def muon_step(W, M, G, lr: float, wd: float, hp: Hyper = Hyper(), form: str = "direct"):
     """One Newton-Schulz (refresh) step for a single m x n matrix.
 
     Returns (W_new, M_new, O) where O = O^{-1}(NS5(O(U))) is the m x n
-    orthogonalised direction before scaling."""
+    orthogonalised direction before scaling.  form="gram" evaluates the same
+    map through ns5_gram (pinned equal to the direct form), which is cheaper
+    for very wide matrices."""
     m, n = np.shape(W)
     M_new = momentum_update(M, G, hp.momentum)
     U = nesterov_input(M_new, G, hp.momentum, hp.nesterov)
     X, tr = orient(U)
-    O = unorient(ns5_direct(X, hp), tr)
+    ns = ns5_gram if form == "gram" else ns5_direct
+    O = unorient(ns(X, hp), tr)
     W_new = apply_update(W, O, lr, wd, update_scale(m, n, hp.scale_coeff))
     return W_new, M_new, O
 

@@ -1,0 +1,121 @@
+"""Host-side checks of the C ABI, no GPU needed: the library loads, exports
+every function include/muon.h declares, and rejects invalid plans and calls
+with the documented status before touching any device memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from matrix_aware_optimizer_muon_amd import _lib as L
+from matrix_aware_optimizer_muon_amd import workloads as WL
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "muon.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_default_hparams_are_the_pages_values():
+    hp = L.default_hparams()
+    assert hp.momentum == pytest.approx(0.95) and hp.nesterov == 1 and hp.ns_steps == 5
+    assert (hp.a, hp.b, hp.c) == pytest.approx((3.4445, -4.7750, 2.0315))
+    assert hp.scale_coeff == pytest.approx(0.2) and hp.rownorm_eps == pytest.approx(1e-8)
+
+
+def test_status_strings():
+    for code, name in [(0, "MUON_OK"), (1, "MUON_ERR_INVALID_ARGUMENT"), (2, "MUON_ERR_UNSUPPORTED"),
+                       (3, "MUON_ERR_WORKSPACE_TOO_SMALL"), (4, "MUON_ERR_HIP")]:
+        assert L.status_string(code) == name
+
+
+def plan_status(shapes, **kw):
+    try:
+        L.Plan(shapes, **kw)
+        return 0
+    except L.MuonError as e:
+        return e.status
+
+
+def test_plan_rejects_bad_descriptions():
+    assert plan_status([]) == L.MUON_ERR_INVALID_ARGUMENT
+    assert plan_status([(0, 5)]) == L.MUON_ERR_INVALID_ARGUMENT
+    assert plan_status([(5, -1)]) == L.MUON_ERR_INVALID_ARGUMENT
+    assert plan_status([(1 << 25, 4)]) == L.MUON_ERR_UNSUPPORTED
+    assert plan_status([(70000, 70000)]) == L.MUON_ERR_UNSUPPORTED
+    hp = L.default_hparams(); hp.ns_steps = 0
+    assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_INVALID_ARGUMENT
+    hp = L.default_hparams(); hp.ns_steps = 17
+    assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_UNSUPPORTED
+    hp = L.default_hparams(); hp.rownorm_eps = 0.0
+    assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_INVALID_ARGUMENT
+    hp = L.default_hparams(); hp.momentum = float("nan")
+    assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_INVALID_ARGUMENT
+    assert plan_status([(4, 4)], max_workspace_bytes=-1) == L.MUON_ERR_INVALID_ARGUMENT
+    lib = L.load()
+    h = ctypes.c_void_p()
+    assert lib.muon_plan(None, ctypes.byref(h), None) == L.MUON_ERR_INVALID_ARGUMENT
+    desc = L.PlanDesc(); desc.num_matrices = 1; desc.grad_dtype = 7
+    assert lib.muon_plan(ctypes.byref(desc), ctypes.byref(h), None) == L.MUON_ERR_INVALID_ARGUMENT
+
+
+def test_plan_buckets_and_chunks():
+    p = L.Plan(WL.config(3).shapes)
+    assert p.info() == (4, 4)  # 3584^2, 512x3584, 18944x3584, 3584x18944
+    p4 = L.Plan(WL.config(4).shapes, grad_dtype="bf16")
+    nb, nc = p4.info()
+    assert nb == 4 and nc >= 4
+    small = L.Plan(WL.config(4).shapes, grad_dtype="bf16", max_workspace_bytes=1)
+    assert small.info() == (4, 196)  # a single matrix always fits
+    assert small.workspace_bytes < p4.workspace_bytes
+    p2 = L.Plan(WL.config(2).shapes)
+    assert p2.info() == (2, 2)
+
+
+def test_step_validation_happens_before_device_work():
+    # Fake (never dereferenced) device pointers: every call must fail in host
+    # validation, so nothing reaches the GPU (none exists here).
+    p = L.Plan([(16, 32), (32, 16)])
+    fake = [0x1000, 0x2000]
+    ws = 0x10000
+    lib = L.load()
+
+    def call(fn, W, M, G, lr=0.02, wd=0.1, wsp=ws, wsb=None):
+        wsb = p.workspace_bytes if wsb is None else wsb
+        try:
+            fn(W, M, G, lr, wd, wsp, wsb)
+            return 0
+        except L.MuonError as e:
+            return e.status
+
+    for fn in (p.step_ptrs, p.rownorm_ptrs):
+        assert call(fn, fake, fake, [0x3000, 0]) == L.MUON_ERR_INVALID_ARGUMENT
+        assert call(fn, fake, fake, fake, lr=float("inf")) == L.MUON_ERR_INVALID_ARGUMENT
+        assert call(fn, fake, fake, fake, wd=float("nan")) == L.MUON_ERR_INVALID_ARGUMENT
+        assert call(fn, fake, fake, fake, wsp=0) == L.MUON_ERR_INVALID_ARGUMENT
+        assert call(fn, fake, fake, fake, wsp=ws + 16) == L.MUON_ERR_INVALID_ARGUMENT
+        assert call(fn, fake, fake, fake, wsb=p.workspace_bytes - 1) == L.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert lib.muon_step_batched(None, None, None, None, 0.0, 0.0, None, 0, None, None) == \
+        L.MUON_ERR_INVALID_ARGUMENT
+    assert lib.muon_plan_destroy(None) == L.MUON_OK
+
+
+def test_workspace_size_query_matches_plan():
+    p = L.Plan([(100, 300)] * 3)
+    n = ctypes.c_size_t()
+    assert L.load().muon_plan_workspace_size(p._handle, ctypes.byref(n)) == L.MUON_OK
+    assert n.value == p.workspace_bytes > 0

@@ -1,0 +1,237 @@
+"""GPU parity of the HIP path against the float64 oracle, through the C ABI.
+
+Tolerances (relative Frobenius): NS output <= 1e-4 on the fp32 path and
+<= 2e-2 on the bf16-MFMA path; updated weights <= 1e-5 (end to end on the
+fp32 path; on the bf16 path the update epilogue is checked against the
+oracle's update applied to the GPU's own direction output); RowNorm
+direction and weights <= 1e-6; momentum <= 1e-6."""
+import math
+
+import numpy as np
+import pytest
+
+from matrix_aware_optimizer_muon_amd import workloads as WL
+from oracle import muon_oracle as OR
+from tests.gpu_common import rel, run
+
+pytestmark = pytest.mark.gpu
+
+LR, WD = 0.02, 0.1
+TOL_NS = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import matrix_aware_optimizer_muon_amd as pkg
+    pkg.load()  # fails loudly if libmuon.so is missing
+
+
+def seeded(shapes, seed, gscale=1e-3, mscale=0.0):
+    rng = np.random.default_rng(seed)
+    W = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    G = [(rng.standard_normal(s) * gscale).astype(np.float32) for s in shapes]
+    M = [(rng.standard_normal(s) * mscale).astype(np.float32) for s in shapes]
+    return W, M, G
+
+
+def check_ns(shapes, W, M, G, ns_dtype, grad_dtype="f32", lr=LR, wd=WD, label="", form="direct",
+             **kw):
+    (Wg, Mg, Og), plan = run(shapes, W, M, G, lr, wd, grad_dtype, ns_dtype, **kw)
+    worst = 0.0
+    for i, (m, n) in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], lr, wd, form=form)
+        e_o = rel(Og[i], Oo)
+        worst = max(worst, e_o)
+        assert e_o <= TOL_NS[ns_dtype], f"{label} matrix {i} {m}x{n}: NS rel err {e_o:.3e}"
+        assert rel(Mg[i], Mo) <= 1e-6, f"{label} matrix {i}: momentum"
+        if ns_dtype == "f32":
+            assert rel(Wg[i], Wo) <= 1e-5, f"{label} matrix {i}: weights {rel(Wg[i], Wo):.3e}"
+        else:
+            W_epi = OR.apply_update(W[i], Og[i], lr, wd, OR.update_scale(m, n))
+            assert rel(Wg[i], W_epi) <= 1e-5, f"{label} matrix {i}: update epilogue"
+    print(f"{label}: worst NS rel err {worst:.3e}")
+    return worst
+
+
+def test_config1_fp32_path():
+    w = WL.config(1)
+    W = [WL.host_weight(w, 0)]
+    G = [WL.host_grad(w, 0)]
+    M = [np.zeros_like(W[0])]
+    check_ns(w.shapes, W, M, G, "f32", label="config1")
+
+
+@pytest.mark.parametrize("ns_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", [(1, 1), (1, 7), (7, 1), (3, 5), (5, 3), (70, 130), (130, 70),
+                                   (200, 200), (129, 515), (515, 129), (33, 1000), (300, 64)])
+def test_ragged_shapes(shape, ns_dtype):
+    W, M, G = seeded([shape], hash(shape) % 1000, mscale=1e-3)
+    check_ns([shape], W, M, G, ns_dtype, label=f"ragged {shape} {ns_dtype}")
+
+
+def test_mixed_buckets_and_orientation_bf16():
+    shapes = [(256, 1024), (1024, 256), (256, 1024), (300, 300), (64, 640), (640, 64)]
+    W, M, G = seeded(shapes, 5, mscale=1e-3)
+    check_ns(shapes, W, M, G, "bf16", label="mixed")
+
+
+def test_bf16_gradients():
+    shapes = [(512, 1536), (1536, 512)]
+    W, M, G = seeded(shapes, 6)
+    G = [WL.bf16_round(g * 3.0) for g in G]
+    check_ns(shapes, W, M, G, "bf16", grad_dtype="bf16", label="bf16 grads")
+
+
+def test_config2_batched_small():
+    w = WL.config(2)
+    n = len(w.shapes)
+    W = [WL.host_weight(w, i) for i in range(n)]
+    G = [WL.host_grad(w, i, 0) for i in range(n)]
+    # momentum from three prior seeded gradients: oracle recursion here, and
+    # the GPU builds its own through rownorm_step with lr = wd = 0
+    priors = [[WL.host_grad(w, i, s) for i in range(n)] for s in (-3, -2, -1)]
+    M_or = [np.zeros(s, np.float32) for s in w.shapes]
+    for pg in priors:
+        M_or = [OR.momentum_update(M_or[i], pg[i], 0.95) for i in range(n)]
+    import torch
+    from matrix_aware_optimizer_muon_amd import Plan
+    from tests.gpu_common import to_dev
+    plan = Plan(w.shapes, "f32", "bf16")
+    Wd = [to_dev(x) for x in W]
+    Md = [torch.zeros_like(x) for x in Wd]
+    Od = [torch.empty_like(x) for x in Wd]
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    ptr = lambda L: [x.data_ptr() for x in L]
+    for pg in priors:
+        Gd = [to_dev(x) for x in pg]
+        plan.rownorm_ptrs(ptr(Wd), ptr(Md), ptr(Gd), 0.0, 0.0, ws.data_ptr(), ws.numel(), st)
+    Gd = [to_dev(x) for x in G]
+    plan.step_ptrs(ptr(Wd), ptr(Md), ptr(Gd), w.lr, w.wd, ws.data_ptr(), ws.numel(), st, ptr(Od))
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, (m, nn) in enumerate(w.shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M_or[i], G[i], w.lr, w.wd)
+        Og = Od[i].cpu().numpy()
+        e = rel(Og, Oo)
+        worst = max(worst, e)
+        assert e <= 2e-2, f"matrix {i} {m}x{nn}: {e:.3e}"
+        assert rel(Md[i].cpu().numpy(), Mo) <= 1e-6
+        W_epi = OR.apply_update(W[i], Og, w.lr, w.wd, OR.update_scale(m, nn))
+        assert rel(Wd[i].cpu().numpy(), W_epi) <= 1e-5
+    print(f"config2 worst NS rel err {worst:.3e}")
+
+
+def test_zero_gradient_is_pure_decay():
+    shapes = [(256, 1024), (1024, 256), (130, 70)]
+    W, M, G = seeded(shapes, 7, gscale=0.0)
+    for ns in ("bf16", "f32"):
+        (Wg, Mg, Og), _ = run(shapes, W, M, G, LR, WD, "f32", ns)
+        for i in range(len(shapes)):
+            assert np.all(Og[i] == 0.0)
+            assert np.all(Mg[i] == 0.0)
+            assert rel(Wg[i], (1 - LR * WD) * W[i].astype(np.float64)) <= 1e-7
+
+
+def test_determinism_and_chunking_bitwise():
+    shapes = [(256, 1024)] * 5 + [(1024, 256)] * 3
+    W, M, G = seeded(shapes, 8, mscale=1e-3)
+    a, _ = run(shapes, W, M, G, LR, WD)
+    b, _ = run(shapes, W, M, G, LR, WD)
+    c, plan = run(shapes, W, M, G, LR, WD, max_ws=1)  # one matrix per chunk
+    assert plan.info()[1] == len(shapes)
+    for x, y, z in zip(a, b, c):
+        for i in range(len(shapes)):
+            assert np.array_equal(x[i], y[i]) and np.array_equal(x[i], z[i])
+
+
+@pytest.mark.parametrize("shape", [(256, 1024), (1024, 256), (300, 300), (5, 3), (3, 5),
+                                   (130, 1030), (1030, 130), (64, 20000), (4100, 7)])
+def test_rownorm_step(shape):
+    W, M, G = seeded([shape], 9 + shape[0], mscale=1e-3)
+    if shape[0] >= 4 and shape[1] >= 4:
+        # force the eps branch on one oriented row and a zero row
+        if shape[0] <= shape[1]:
+            M[0][1] = 0.0; G[0][1] = 0.0
+            M[0][2] = 0.0; G[0][2] *= 1e-8  # |U row| ~ 2e-11*sqrt(n) < eps
+        else:
+            M[0][:, 1] = 0.0; G[0][:, 1] = 0.0
+            M[0][:, 2] = 0.0; G[0][:, 2] *= 1e-8
+    (Wg, Mg, Rg), _ = run([shape], W, M, G, LR, WD, rownorm=True)
+    Wo, Mo, Ro = OR.rownorm_step(W[0], M[0], G[0], LR, WD)
+    assert rel(Rg[0], Ro) <= 1e-6
+    assert rel(Mg[0], Mo) <= 1e-6
+    assert rel(Wg[0], Wo) <= 1e-6
+
+
+def test_rownorm_bf16_grad_and_no_nesterov():
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    hp = default_hparams()
+    hp.nesterov = 0
+    shapes = [(384, 1000), (1000, 384)]
+    W, M, G = seeded(shapes, 10, mscale=1e-3)
+    G = [WL.bf16_round(g) for g in G]
+    (Wg, Mg, Rg), _ = run(shapes, W, M, G, LR, WD, grad_dtype="bf16", rownorm=True, hp=hp)
+    ohp = OR.Hyper(nesterov=False)
+    for i in range(2):
+        Wo, Mo, Ro = OR.rownorm_step(W[i], M[i], G[i], LR, WD, ohp)
+        assert rel(Rg[i], Ro) <= 1e-6 and rel(Wg[i], Wo) <= 1e-6
+
+
+def test_checkpoint_resume_bitwise():
+    import torch
+    from matrix_aware_optimizer_muon_amd.optim import MuonMI355X
+    shapes = [(256, 1024), (1024, 256)]
+    rng = np.random.default_rng(11)
+    W0 = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    grads = [[(rng.standard_normal(s) * 1e-3).astype(np.float32) for s in shapes] for _ in range(5)]
+    gd = [[torch.from_numpy(g).cuda() for g in gs] for gs in grads]
+
+    def fresh(Wl, Ml=None, t=0):
+        params = [torch.from_numpy(np.array(w)).cuda() for w in Wl]
+        opt = MuonMI355X(params, refresh_period=2)
+        if Ml is not None:
+            for m, h in zip(opt.momentum, Ml):
+                m.copy_(torch.from_numpy(h))
+        opt.t = t
+        return opt
+
+    a = fresh(W0)
+    for s in range(5):
+        a.step(gd[s], LR, WD)
+    b = fresh(W0)
+    for s in range(3):
+        b.step(gd[s], LR, WD)
+    torch.cuda.synchronize()
+    ck_W = [p.cpu().numpy() for p in b.params]
+    ck_M = [m.cpu().numpy() for m in b.momentum]
+    del b
+    c = fresh(ck_W, ck_M, t=3)
+    for s in range(3, 5):
+        c.step(gd[s], LR, WD)
+    torch.cuda.synchronize()
+    for x, y in zip(a.params + a.momentum, c.params + c.momentum):
+        assert torch.equal(x, y)
+
+
+def test_invalid_calls_leave_memory_untouched():
+    import torch
+    from matrix_aware_optimizer_muon_amd import MuonError, Plan
+    plan = Plan([(64, 64)], "f32", "bf16")
+    w = torch.randn(64, 64, device="cuda")
+    m = torch.zeros_like(w)
+    g = torch.randn_like(w)
+    w0 = w.clone()
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    with pytest.raises(MuonError):
+        plan.step_ptrs([w.data_ptr()], [m.data_ptr()], [g.data_ptr()], LR, WD, ws.data_ptr(),
+                       ws.numel() - 1, st)
+    with pytest.raises(MuonError):
+        plan.step_ptrs([w.data_ptr()], [m.data_ptr()], [g.data_ptr()], float("nan"), WD,
+                       ws.data_ptr(), ws.numel(), st)
+    torch.cuda.synchronize()
+    assert torch.equal(w, w0) and torch.count_nonzero(m) == 0
