@@ -1,0 +1,241 @@
+#!/usr/bin/env python
+"""Benchmark of the single-GPU Muon optimizer step on MI355X.
+
+One "step" is one muon_step_batched call over the whole matrix set (for
+the periodic-RowNorm workload, one call of the schedule: refresh when
+t mod K == 0, RowNorm otherwise).  Inputs are synthetic, seeded and already
+resident in HBM when the timed region starts.
+
+Prints one JSON line: whole-step time, algorithmic TFLOP/s, the roofline of
+the dominant kernel class (timed live with HIP events on the library's
+stream) and the float64 CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Muon step ms + achieved MFMA TFLOP/s on Qwen2.5-7B-shaped matrix set"
+PEAK_MFMA_16BIT = 2500.0   # TFLOP/s, MI355X dense bf16 / fp16
+PEAK_MFMA_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix
+PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
+GEMM_CLASSES = ("syrk", "poly", "pqpg", "ph", "final")
+
+
+def ns_flops(shapes) -> float:
+    """Algorithmic flops of the Gram-space step as this library evaluates it:
+    SYRK r^2 c + (17 r x r products of r^3 each for N = 5) + final 2 r^2 c,
+    symmetric products counted on the lower triangle."""
+    tot = 0.0
+    for m, n in shapes:
+        r, c = min(m, n), max(m, n)
+        tot += 3.0 * r * r * c + 17.0 * r ** 3
+    return tot
+
+
+def make_device_inputs(w, dev, torch):
+    from matrix_aware_optimizer_muon_amd import workloads as WL
+    W = [WL.device_weight(w, i, dev) for i in range(len(w.shapes))]
+    M = [torch.zeros_like(x) for x in W]
+    G = [WL.device_grad(w, i, 0, dev) for i in range(len(w.shapes))]
+    return W, M, G
+
+
+def cpu_baseline(w, sample_shapes_max: int = 3):
+    """Time the float64 oracle on one matrix per distinct shape (largest
+    first, at most `sample_shapes_max` shapes, ~10-30 s of CPU work) and
+    extrapolate to the whole matrix set by count."""
+    import numpy as np
+    from matrix_aware_optimizer_muon_amd import workloads as WL
+    from oracle import muon_oracle as OR
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    counts = {}
+    for s in w.shapes:
+        key = (min(s), max(s))
+        counts[key] = counts.get(key, 0) + 1
+    keys = sorted(counts, key=lambda k: -k[0] * k[0] * k[1])[:sample_shapes_max]
+    per_shape = {}
+    for r, c in keys:
+        i = next(j for j, s in enumerate(w.shapes) if (min(s), max(s)) == (r, c))
+        Wh = WL.host_weight(w, i)
+        Gh = WL.host_grad(w, i, 0)
+        Mh = np.zeros_like(Wh)
+        t0 = time.perf_counter()
+        OR.muon_step(Wh, Mh, Gh, w.lr, w.wd)
+        per_shape[(r, c)] = time.perf_counter() - t0
+    covered = sum(counts[k] for k in keys)
+    total_s = sum(per_shape[k] * counts[k] for k in keys)
+    covered_flops = sum(ns_flops([k]) * counts[k] for k in keys)
+    sample = ", ".join(f"{c}x{r} ({per_shape[(r, c)]:.1f} s)" for r, c in keys)
+    return {
+        "value": covered_flops / total_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads if threads else cores,
+        "kind": "oracle",
+        "sample": (f"float64 direct-form oracle, one matrix per shape [{sample}], "
+                   f"extrapolated by count to {covered} of {len(w.shapes)} matrices; "
+                   f"value = the GPU path's algorithmic flops / oracle seconds"),
+        "ms_per_step_extrapolated": total_s * 1e3 * len(w.shapes) / covered,
+        "host_cores_visible": cores,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = Qwen2.5-7B, 28 layers)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-launch event timing")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        a = torch.ones(n, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4}))
+        return
+
+    import matrix_aware_optimizer_muon_amd as pkg
+    from matrix_aware_optimizer_muon_amd import workloads as WL
+
+    w = WL.config(args.config)
+    dev = torch.device("cuda:0")
+    lib_path = pkg.load()._name
+    W, M, G = make_device_inputs(w, dev, torch)
+    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ptr = lambda L: [x.data_ptr() for x in L]
+    Wp, Mp, Gp = ptr(W), ptr(M), ptr(G)
+
+    if w.prior_steps:
+        # momentum from seeded prior gradients, accumulated by the library's
+        # own momentum update (RowNorm step with lr = wd = 0 leaves W as is)
+        for s in range(-w.prior_steps, 0):
+            Gs = [WL.device_grad(w, i, s, dev) for i in range(len(w.shapes))]
+            plan.rownorm_ptrs(Wp, Mp, ptr(Gs), 0.0, 0.0, ws.data_ptr(), ws.numel(), sp)
+        torch.cuda.synchronize()
+
+    K = w.refresh_period
+
+    def one_step(t):
+        if K and t % K != 0:
+            plan.rownorm_ptrs(Wp, Mp, Gp, w.lr, w.wd, ws.data_ptr(), ws.numel(), sp)
+            return "rownorm"
+        plan.step_ptrs(Wp, Mp, Gp, w.lr, w.wd, ws.data_ptr(), ws.numel(), sp)
+        return "refresh"
+
+    for t in range(args.warmup):
+        one_step(t)
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        plan.set_profiling(True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    kinds = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        evs[t][0].record(stream)
+        kinds.append(one_step(t))
+        evs[t][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in evs]
+    ktimes = plan.kernel_times() if not args.no_profile else {}
+    plan.set_profiling(False)
+
+    ms_per_step = wall * 1e3 / args.steps
+    refresh_ms = [m for m, k in zip(step_ms, kinds) if k == "refresh"]
+    rownorm_ms = [m for m, k in zip(step_ms, kinds) if k == "rownorm"]
+    F = ns_flops(w.shapes)
+    n_refresh = len(refresh_ms)
+    value = F * n_refresh / (wall) / 1e12 if n_refresh else 0.0
+
+    kernels = {}
+    for k, v in ktimes.items():
+        e = {"ms_total": round(v["ms"], 4), "launches": v["launches"],
+             "ms_per_launch": round(v["ms"] / v["launches"], 5)}
+        if v["flops"] > 0:
+            e["tflops"] = round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2)
+        if v["bytes"] > 0:
+            e["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
+        kernels[k] = e
+    roofline = None
+    if ktimes:
+        dom = max(ktimes, key=lambda k: ktimes[k]["ms"])
+        v = ktimes[dom]
+        if dom in GEMM_CLASSES:
+            peak = PEAK_MFMA_F32 if w.ns_dtype == "f32" else PEAK_MFMA_16BIT
+            ach = v["flops"] / (v["ms"] * 1e-3) / 1e12
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                        "ms_per_launch": round(v["ms"] / v["launches"], 5),
+                        "share_of_step": round(v["ms"] / sum(x["ms"] for x in ktimes.values()), 3)}
+        else:
+            ach = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "traffic": None,
+                        "ms_per_launch": round(v["ms"] / v["launches"], 5),
+                        "share_of_step": round(v["ms"] / sum(x["ms"] for x in ktimes.values()), 3)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian W, G; random init, no checkpoints)",
+        "config": {"workload": w.name, "matrices": len(w.shapes), "params": w.numel(),
+                   "grad_dtype": w.grad_dtype, "ns_dtype": w.ns_dtype,
+                   "refresh_period": K, "algorithmic_tflop_per_refresh": round(F / 1e12, 4)},
+        "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
+        "step_ms_p90": round(sorted(step_ms)[min(len(step_ms) - 1, int(0.9 * len(step_ms)))], 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "library": os.path.relpath(lib_path, ROOT),
+    }
+    if refresh_ms and rownorm_ms:
+        out["refresh_ms"] = round(sum(refresh_ms) / len(refresh_ms), 4)
+        out["rownorm_ms"] = round(sum(rownorm_ms) / len(rownorm_ms), 4)
+        out["cycle_ms"] = round(out["refresh_ms"] + (K - 1) * out["rownorm_ms"], 4)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -144,6 +144,36 @@ muon_status rownorm_step(muon_plan_t plan, float* const* W, float* const* M,
                          void* workspace, size_t workspace_bytes, hipStream_t stream,
                          float* const* R_out);
 
+/* Kernel classes reported by the launch profiler. */
+typedef enum {
+  MUON_K_PREP = 0,        /* momentum, Nesterov blend, ||U|| partials, X0 */
+  MUON_K_NORM = 1,        /* fixed-order norm reduction                  */
+  MUON_K_SYRK = 2,        /* G0 = X0 X0^T, lower tiles                   */
+  MUON_K_POLY = 3,        /* G^2 and P~ = b G + c G^2                    */
+  MUON_K_PQPG = 4,        /* P~ Q and P~ G                               */
+  MUON_K_PH = 5,          /* P~ H                                        */
+  MUON_K_FINAL = 6,       /* Q X0 fused with the weight update           */
+  MUON_K_ROWNORM = 7,     /* RowNorm, one pass (m <= n)                  */
+  MUON_K_COLSUM = 8,      /* RowNorm m > n: M update + column sums        */
+  MUON_K_COLFINAL = 9,    /* RowNorm m > n: column scale                 */
+  MUON_K_COLAPPLY = 10,   /* RowNorm m > n: apply                         */
+  MUON_K_COUNT = 11
+} muon_kernel_class;
+
+/* Launch profiler (measurement support, off by default).  While enabled,
+ * each kernel launch of the step calls is bracketed by a pair of HIP events
+ * recorded on the caller's stream.  muon_plan_kernel_times waits for the
+ * recorded events, adds their elapsed times into per-class totals, and
+ * returns the totals accumulated since the last reset: total milliseconds,
+ * number of launches, and the algorithmic flops and HBM bytes of those
+ * launches (flops: symmetric products counted on the lower triangle; bytes:
+ * each operand read once and each result written once).  Enabling or
+ * disabling resets the totals.  Arrays have MUON_K_COUNT entries; any may be
+ * NULL. */
+muon_status muon_plan_set_profiling(muon_plan_t plan, int enable);
+muon_status muon_plan_kernel_times(muon_plan_t plan, double* total_ms, int64_t* launches,
+                                   double* flops, double* bytes);
+
 /* Static, human-readable name of a status code. */
 const char* muon_status_string(muon_status s);
 

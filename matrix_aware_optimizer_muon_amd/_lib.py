@@ -24,7 +24,10 @@ MUON_F32 = 0
 MUON_BF16 = 1
 
 EXPORTED = ("muon_default_hparams", "muon_plan", "muon_plan_destroy", "muon_plan_workspace_size",
-            "muon_plan_info", "muon_step_batched", "rownorm_step", "muon_status_string")
+            "muon_plan_info", "muon_step_batched", "rownorm_step", "muon_plan_set_profiling",
+            "muon_plan_kernel_times", "muon_status_string")
+KERNEL_CLASSES = ("prep", "norm", "syrk", "poly", "pqpg", "ph", "final", "rownorm", "colsum",
+                  "colfinal", "colapply")
 
 
 class MuonError(RuntimeError):
@@ -69,11 +72,14 @@ def load() -> ctypes.CDLL:
                  ctypes.c_float, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
     lib.muon_step_batched.argtypes = step_args
     lib.rownorm_step.argtypes = step_args
+    lib.muon_plan_set_profiling.argtypes = [P, ctypes.c_int]
+    D = ctypes.POINTER(ctypes.c_double)
+    lib.muon_plan_kernel_times.argtypes = [P, D, ctypes.POINTER(ctypes.c_int64), D, D]
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     for name in ("muon_default_hparams", "muon_plan", "muon_plan_destroy",
                  "muon_plan_workspace_size", "muon_plan_info", "muon_step_batched",
-                 "rownorm_step"):
+                 "rownorm_step", "muon_plan_set_profiling", "muon_plan_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -156,6 +162,23 @@ class Plan:
         """rownorm_step on raw device pointers."""
         self._call(self._lib.rownorm_step, "rownorm_step", W, M, G, lr, wd, workspace_ptr,
                    workspace_bytes, stream, R_out)
+
+    def set_profiling(self, enable: bool):
+        st = self._lib.muon_plan_set_profiling(self._handle, 1 if enable else 0)
+        if st != MUON_OK:
+            raise MuonError(st, "muon_plan_set_profiling")
+
+    def kernel_times(self) -> dict:
+        """Per kernel class: total ms, launches, algorithmic flops and bytes
+        accumulated since profiling was enabled (waits for the events)."""
+        n = len(KERNEL_CLASSES)
+        ms, fl, by = (ctypes.c_double * n)(), (ctypes.c_double * n)(), (ctypes.c_double * n)()
+        la = (ctypes.c_int64 * n)()
+        st = self._lib.muon_plan_kernel_times(self._handle, ms, la, fl, by)
+        if st != MUON_OK:
+            raise MuonError(st, "muon_plan_kernel_times")
+        return {k: {"ms": ms[i], "launches": int(la[i]), "flops": fl[i], "bytes": by[i]}
+                for i, k in enumerate(KERNEL_CLASSES) if la[i] > 0}
 
     def close(self):
         if getattr(self, "_handle", None):

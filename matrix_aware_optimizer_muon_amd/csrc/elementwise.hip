@@ -438,39 +438,41 @@ int rownorm_row_blocks(int m, int n) {
   return (m + RN_ROWS - 1) / RN_ROWS;
 }
 
-hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec,
+hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec, int phase,
                           hipStream_t s) {
   if (nmat == 0) return hipSuccess;
   const dim3 b(256);
-  if (p.m <= p.n) {
+  if (phase == RN_PHASE_ROWS) {
     const uint64_t blocks = (uint64_t)nmat * p.m;
     if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
     const int nc = (p.n + 3) / 4;
     const dim3 g((uint32_t)blocks);
-#define RN_ROWS_LAUNCH(GB)                                                               \
-  do {                                                                                   \
-    if (nc <= 256) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 1>), g, b, 0, s, p, vec); \
+#define RN_ROWS_LAUNCH(GB)                                                                    \
+  do {                                                                                        \
+    if (nc <= 256) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 1>), g, b, 0, s, p, vec);      \
     else if (nc <= 1024) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 4>), g, b, 0, s, p, vec); \
     else if (nc <= 4096) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 16>), g, b, 0, s, p, vec); \
-    else hipLaunchKernelGGL((rownorm_rows_kernel<GB, 0>), g, b, 0, s, p, vec);           \
+    else hipLaunchKernelGGL((rownorm_rows_kernel<GB, 0>), g, b, 0, s, p, vec);                \
   } while (0)
     if (grad_bf16) RN_ROWS_LAUNCH(true); else RN_ROWS_LAUNCH(false);
 #undef RN_ROWS_LAUNCH
     return hipGetLastError();
   }
+  if (phase == RN_PHASE_COLFINAL) {
+    hipLaunchKernelGGL(rownorm_colfinal_kernel, dim3((uint32_t)(nmat * ((p.n + 255) / 256))), b,
+                       0, s, p);
+    return hipGetLastError();
+  }
   const uint64_t blocks = (uint64_t)nmat * p.row_blocks * ((p.n + 1023) / 1024);
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   const dim3 g((uint32_t)blocks);
-  if (grad_bf16) hipLaunchKernelGGL((rownorm_colsum_kernel<true>), g, b, 0, s, p, vec);
-  else hipLaunchKernelGGL((rownorm_colsum_kernel<false>), g, b, 0, s, p, vec);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rownorm_colfinal_kernel, dim3((uint32_t)(nmat * ((p.n + 255) / 256))), b, 0,
-                     s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (grad_bf16) hipLaunchKernelGGL((rownorm_colapply_kernel<true>), g, b, 0, s, p, vec);
-  else hipLaunchKernelGGL((rownorm_colapply_kernel<false>), g, b, 0, s, p, vec);
+  if (phase == RN_PHASE_COLSUM) {
+    if (grad_bf16) hipLaunchKernelGGL((rownorm_colsum_kernel<true>), g, b, 0, s, p, vec);
+    else hipLaunchKernelGGL((rownorm_colsum_kernel<false>), g, b, 0, s, p, vec);
+  } else {
+    if (grad_bf16) hipLaunchKernelGGL((rownorm_colapply_kernel<true>), g, b, 0, s, p, vec);
+    else hipLaunchKernelGGL((rownorm_colapply_kernel<false>), g, b, 0, s, p, vec);
+  }
   return hipGetLastError();
 }
 

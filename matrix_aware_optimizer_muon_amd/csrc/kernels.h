@@ -89,7 +89,9 @@ struct RowNormParams {
   int row_blocks;
 };
 
-hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec, hipStream_t s);
+enum RowNormPhase : int { RN_PHASE_ROWS = 0, RN_PHASE_COLSUM = 1, RN_PHASE_COLFINAL = 2, RN_PHASE_COLAPPLY = 3 };
+hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec, int phase,
+                          hipStream_t s);
 int rownorm_row_blocks(int m, int n);
 
 }  // namespace muon

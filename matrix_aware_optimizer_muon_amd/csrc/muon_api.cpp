@@ -68,6 +68,12 @@ struct Slot {
   bool used = false;
 };
 
+struct TimedLaunch {
+  hipEvent_t start = nullptr, stop = nullptr;
+  int cls = 0;
+  double flops = 0.0, bytes = 0.0;
+};
+
 }  // namespace
 
 struct muon_plan_s {
@@ -87,6 +93,12 @@ struct muon_plan_s {
   int next_slot = 0;
   bool ring_ready = false;
   std::vector<MatPtrs> host_table;
+  // launch profiler
+  bool profiling = false;
+  std::vector<TimedLaunch> tpool;
+  size_t tused = 0;
+  double t_ms[MUON_K_COUNT] = {}, t_flops[MUON_K_COUNT] = {}, t_bytes[MUON_K_COUNT] = {};
+  int64_t t_launches[MUON_K_COUNT] = {};
 };
 
 namespace {
@@ -191,6 +203,46 @@ int chunk_vec(const muon_plan_s* p, const Bucket& b, const Chunk& ch) {
 }
 
 muon_status hip_ok(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_HIP; }
+
+// Run one launch, bracketed by profiler events when profiling is enabled.
+template <class F>
+muon_status timed(muon_plan_s* p, hipStream_t s, int cls, double flops, double bytes, F&& launch) {
+  if (!p->profiling) return hip_ok(launch());
+  if (p->tused == p->tpool.size()) {
+    TimedLaunch t;
+    if (hipEventCreate(&t.start) != hipSuccess) return MUON_ERR_HIP;
+    if (hipEventCreate(&t.stop) != hipSuccess) {
+      (void)hipEventDestroy(t.start);
+      return MUON_ERR_HIP;
+    }
+    p->tpool.push_back(t);
+  }
+  TimedLaunch& t = p->tpool[p->tused++];
+  t.cls = cls;
+  t.flops = flops;
+  t.bytes = bytes;
+  if (hipEventRecord(t.start, s) != hipSuccess) return MUON_ERR_HIP;
+  muon_status st = hip_ok(launch());
+  if (st != MUON_OK) return st;
+  return hip_ok(hipEventRecord(t.stop, s));
+}
+
+void reset_profile(muon_plan_s* p) {
+  p->tused = 0;
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    p->t_ms[k] = p->t_flops[k] = p->t_bytes[k] = 0.0;
+    p->t_launches[k] = 0;
+  }
+}
+
+void release_profile(muon_plan_s* p) {
+  for (auto& t : p->tpool) {
+    if (t.start) (void)hipEventDestroy(t.start);
+    if (t.stop) (void)hipEventDestroy(t.stop);
+  }
+  p->tpool.clear();
+  p->tused = 0;
+}
 
 }  // namespace
 
@@ -315,6 +367,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
 muon_status muon_plan_destroy(muon_plan_t plan) {
   if (!plan) return MUON_OK;
   release_ring(plan);
+  release_profile(plan);
   delete plan;
   return MUON_OK;
 }
@@ -404,6 +457,11 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       // stride; r_pad is a multiple of 64, so both are exactly r_pad^2
       if (rr_stride != h_stride || rr_stride != rr) return MUON_ERR_HIP;
       const int vec = chunk_vec(p, B, ch);
+      // algorithmic work per matrix (true sizes; symmetric products on the
+      // lower triangle): SYRK r^2 c, each r x r product r^3, final 2 r^2 c
+      const double r2 = (double)B.r * B.r, r3 = r2 * B.r, cc = (double)B.c;
+      const double rcf = (double)B.r * B.c;
+      const double hes = f32path ? 4.0 : 2.0;
 
       PrepParams pp{};
       pp.table = d_table + ch.first;
@@ -419,9 +477,13 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       pp.partials = d_part;
       pp.blocks_per_mat = B.prep_blocks;
       pp.inv_norm = d_inv + ch.first;
-      st = hip_ok(launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream));
+      const double elems = (double)B.m * B.n * nm;
+      st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + xes), [&] {
+        return launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream);
+      });
       if (st != MUON_OK) return st;
-      st = hip_ok(launch_norm_finalize(pp, nm, stream));
+      st = timed(p, stream, MUON_K_NORM, 0.0, 4.0 * B.prep_blocks * nm,
+                 [&] { return launch_norm_finalize(pp, nm, stream); });
       if (st != MUON_OK) return st;
 
       GemmParams g{};
@@ -469,7 +531,8 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       g.triangular = 1;
       g.tiles_per_prod = ntri;
       g.products = 1;
-      st = hip_ok(launch_gemm(g, EPI_SYRK, op, B.bt, 0, 0, nm, stream));
+      st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (xes * rcf + r2 * (4 + (f32path ? 0 : 2))) * nm,
+                 [&] { return launch_gemm(g, EPI_SYRK, op, B.bt, 0, 0, nm, stream); });
       if (st != MUON_OK) return st;
 
       for (int k = 0; k < N; ++k) {
@@ -481,7 +544,8 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         g.Qh_dst = Qh[dst];
         // P~ = b G + c G^2 (and Q1 = a I + P~ on the first iteration)
         rr_setup(Gh, Gh, Gh, 1);
-        st = hip_ok(launch_gemm(g, EPI_POLY, op, B.bt, 0, 0, nm, stream));
+        st = timed(p, stream, MUON_K_POLY, r3 * nm, r2 * (hes + 4 + hes) * nm,
+                   [&] { return launch_gemm(g, EPI_POLY, op, B.bt, 0, 0, nm, stream); });
         if (st != MUON_OK) return st;
         const bool need_q = k > 0;
         const bool need_h = k < N - 1;
@@ -497,14 +561,17 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
             rr_setup(Ph, Gh, Gh, 1);
             g.prod_base = 1;
           }
-          st = hip_ok(launch_gemm(g, EPI_PQPG, op, B.bt, 0, 0, nm, stream));
+          const int np = g.products;
+          st = timed(p, stream, MUON_K_PQPG, r3 * np * nm, r2 * (hes + np * (hes + 4 + 4 + hes)) * nm,
+                     [&] { return launch_gemm(g, EPI_PQPG, op, B.bt, 0, 0, nm, stream); });
           g.prod_base = 0;
           if (st != MUON_OK) return st;
         }
         if (need_h) {
           // G_k = a H + P~ H
           rr_setup(Ph, Hh, Hh, 1);
-          st = hip_ok(launch_gemm(g, EPI_PH, op, B.bt, 0, 0, nm, stream));
+          st = timed(p, stream, MUON_K_PH, r3 * nm, r2 * (hes + hes + 4 + 4 + hes) * nm,
+                     [&] { return launch_gemm(g, EPI_PH, op, B.bt, 0, 0, nm, stream); });
           if (st != MUON_OK) return st;
         }
       }
@@ -546,7 +613,8 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       fg.tiles_m = fg.Mdim / B.bt;
       fg.tiles_n = fg.Ndim / B.bt;
       fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
-      st = hip_ok(launch_gemm(fg, EPI_FINAL, op, B.bt, aks, bks, nm, stream));
+      st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + hes * r2 + 8.0 * rcf) * nm,
+                 [&] { return launch_gemm(fg, EPI_FINAL, op, B.bt, aks, bks, nm, stream); });
       if (st != MUON_OK) return st;
     }
   }
@@ -582,8 +650,59 @@ muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const 
     rp.colscale = (float*)(wsb + p->off_colscale);
     rp.row_blocks = B.rn_row_blocks;
     const int vec = chunk_vec(p, B, Chunk{B.first, B.count});
-    st = hip_ok(launch_rownorm(rp, gbf16, B.count, vec, stream));
+    const double elems = (double)B.m * B.n * B.count;
+    const double gb = gbf16 ? 2.0 : 4.0;
+    const int nm = B.count;
+    if (!B.transposed) {
+      // read M, G, W; write M, W
+      st = timed(p, stream, MUON_K_ROWNORM, 0.0, elems * (4 + gb + 4 + 4 + 4), [&] {
+        return launch_rownorm(rp, gbf16, nm, vec, RN_PHASE_ROWS, stream);
+      });
+      if (st != MUON_OK) return st;
+      continue;
+    }
+    st = timed(p, stream, MUON_K_COLSUM, 0.0, elems * (4 + gb + 4), [&] {
+      return launch_rownorm(rp, gbf16, nm, vec, RN_PHASE_COLSUM, stream);
+    });
     if (st != MUON_OK) return st;
+    st = timed(p, stream, MUON_K_COLFINAL, 0.0, 4.0 * (B.rn_row_blocks + 1) * B.n * nm, [&] {
+      return launch_rownorm(rp, gbf16, nm, vec, RN_PHASE_COLFINAL, stream);
+    });
+    if (st != MUON_OK) return st;
+    st = timed(p, stream, MUON_K_COLAPPLY, 0.0, elems * (4 + gb + 4 + 4), [&] {
+      return launch_rownorm(rp, gbf16, nm, vec, RN_PHASE_COLAPPLY, stream);
+    });
+    if (st != MUON_OK) return st;
+  }
+  return MUON_OK;
+}
+
+muon_status muon_plan_set_profiling(muon_plan_t plan, int enable) {
+  if (!plan || (enable != 0 && enable != 1)) return MUON_ERR_INVALID_ARGUMENT;
+  plan->profiling = enable == 1;
+  reset_profile(plan);
+  return MUON_OK;
+}
+
+muon_status muon_plan_kernel_times(muon_plan_t plan, double* total_ms, int64_t* launches,
+                                   double* flops, double* bytes) {
+  if (!plan) return MUON_ERR_INVALID_ARGUMENT;
+  for (size_t i = 0; i < plan->tused; ++i) {
+    TimedLaunch& t = plan->tpool[i];
+    float ms = 0.0f;
+    if (hipEventSynchronize(t.stop) != hipSuccess) return MUON_ERR_HIP;
+    if (hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) return MUON_ERR_HIP;
+    plan->t_ms[t.cls] += ms;
+    plan->t_flops[t.cls] += t.flops;
+    plan->t_bytes[t.cls] += t.bytes;
+    plan->t_launches[t.cls] += 1;
+  }
+  plan->tused = 0;
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    if (total_ms) total_ms[k] = plan->t_ms[k];
+    if (launches) launches[k] = plan->t_launches[k];
+    if (flops) flops[k] = plan->t_flops[k];
+    if (bytes) bytes[k] = plan->t_bytes[k];
   }
   return MUON_OK;
 }
