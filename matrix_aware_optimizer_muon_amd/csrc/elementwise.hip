@@ -1,10 +1,11 @@
 // Memory-bound kernels of the Muon and periodic-RowNorm steps.
 //
 // prep:       M <- mu M + G ("Infra Optimizers" eq. (1)); U = mu M + G
-//             (Nesterov remark); partial sums of ||U||_F^2; X0 = O(U) stored
-//             r x c in the Newton-Schulz operand type, transposed through LDS
-//             when m > n ("Scaling Muon for DiT" 3.1), zero padded to the
-//             GEMM tile.  One read of M and G, one write of M and X0.
+//             (Nesterov remark); partial sums of ||U||_F^2; U stored in the
+//             Newton-Schulz operand type both as is and transposed through
+//             LDS, zero padded to the GEMM tile: one copy is X0 = O(U)
+//             ("Scaling Muon for DiT" 3.1), the other X0^T.  One read of M
+//             and G, one write of M and of the two copies.
 // finalize:   deterministic (fixed order, fp64) reduction of the partial sums
 //             to 1/||U||_F per matrix (0 when the norm is 0).
 // rownorm:    the same M update and U, then R_eps over the r oriented rows
@@ -99,73 +100,22 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 }
 
 // ---------------------------------------------------------------------------
-// prep, m <= n: X0 rows are rows of U.  Block: 256 threads x 4 columns = 1024
-// columns of PREP_ROWS rows.
-constexpr int PREP_ROWS = 8;
-
+// prep: one 64 x 64 tile of U (rows i < m, cols j < n; zero in the padding)
+// per workgroup.  U is written twice in the operand type: in its natural
+// layout (m_pad x n_pad) and transposed through LDS (n_pad x m_pad), so that
+// X0 = O(U) and X0^T are both available K-contiguous to the GEMMs.
 template <bool GBF16, bool XF32>
-__global__ void __launch_bounds__(256) prep_rows_kernel(const PrepParams p, int vec) {
-  __shared__ float red[4];
-  const int cblocks = (p.c_pad + 1023) / 1024;
-  const int rblocks = (p.r_pad + PREP_ROWS - 1) / PREP_ROWS;
-  const int per_mat = cblocks * rblocks;
-  const int mat = blockIdx.x / per_mat;
-  const int bl = blockIdx.x - mat * per_mat;
-  const int rb = bl / cblocks, cb = bl - rb * cblocks;
-  const MatPtrs mp = p.table[mat];
-  const int col = cb * 1024 + threadIdx.x * 4;
-  float ss = 0.f;
-  if (col < p.c_pad) {
-    for (int rr = 0; rr < PREP_ROWS; ++rr) {
-      const int row = rb * PREP_ROWS + rr;
-      if (row >= p.r_pad) break;
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row < p.m && col < p.n) {
-        const int valid = p.n - col;
-        const size_t idx = (size_t)row * p.n + col;
-        const bool v4 = vec && valid >= 4;
-        const float4 m = load_f4(mp.M + idx, v4, valid);
-        const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
-        float4 mn;
-        u = momentum4(m, g, p.mu, p.nesterov, &mn);
-        store_f4(mp.M + idx, mn, v4, valid);
-        if (valid < 4) {  // keep the padding exactly zero
-          if (valid < 2) u.y = 0.f;
-          if (valid < 3) u.z = 0.f;
-          u.w = 0.f;
-        }
-        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
-      }
-      const size_t xo = (size_t)mat * p.x_stride + (size_t)row * p.c_pad + col;
-      if (XF32) {
-        *(float4*)((float*)p.X + xo) = u;
-      } else {
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(u.x) | ((uint32_t)f32_to_bf16_bits(u.y) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16);
-        *(uint2*)((uint16_t*)p.X + xo) = pk;
-      }
-    }
-  }
-  const float tot = block_sum<256>(ss, red);
-  if (threadIdx.x == 0) p.partials[(size_t)mat * p.blocks_per_mat + bl] = tot;
-}
-
-// prep, m > n: X0 = U^T.  A 64 x 64 tile of U (rows i < m, cols j < n) is
-// read row-major, staged in LDS and written as 64 rows j of X0 (contiguous
-// in i).
-template <bool GBF16, bool XF32>
-__global__ void __launch_bounds__(256) prep_cols_kernel(const PrepParams p, int vec) {
+__global__ void __launch_bounds__(256) prep_tile_kernel(const PrepParams p, int vec) {
   __shared__ float tile[64][65];
   __shared__ float red[4];
-  const int ib = p.c_pad / 64;  // tiles along i (U rows = X0 columns)
-  const int jb = p.r_pad / 64;  // tiles along j (U cols = X0 rows)
+  const int ib = p.m_pad / 64, jb = p.n_pad / 64;
   const int per_mat = ib * jb;
   const int mat = blockIdx.x / per_mat;
   const int bl = blockIdx.x - mat * per_mat;
-  const int tj = bl / ib, ti = bl - tj * ib;
+  const int ti = bl / jb, tj = bl - ti * jb;
   const MatPtrs mp = p.table[mat];
   const int t = threadIdx.x;
+  const size_t xbase = (size_t)mat * p.x_stride;
   float ss = 0.f;
   {
     const int c4 = (t & 15) * 4;
@@ -184,12 +134,21 @@ __global__ void __launch_bounds__(256) prep_cols_kernel(const PrepParams p, int 
         float4 mn;
         u = momentum4(m, g, p.mu, p.nesterov, &mn);
         store_f4(mp.M + idx, mn, v4, valid);
-        if (valid < 4) {
+        if (valid < 4) {  // keep the padding exactly zero
           if (valid < 2) u.y = 0.f;
           if (valid < 3) u.z = 0.f;
           u.w = 0.f;
         }
         ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+      }
+      const size_t xo = xbase + (size_t)i * p.n_pad + j;
+      if (XF32) {
+        *(float4*)((float*)p.X + xo) = u;
+      } else {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_bits(u.x) | ((uint32_t)f32_to_bf16_bits(u.y) << 16);
+        pk.y = (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16);
+        *(uint2*)((uint16_t*)p.X + xo) = pk;
       }
       tile[rl][c4 + 0] = u.x;
       tile[rl][c4 + 1] = u.y;
@@ -199,11 +158,11 @@ __global__ void __launch_bounds__(256) prep_cols_kernel(const PrepParams p, int 
   }
   __syncthreads();
   {
-    const int jl = t >> 2;          // X0 row within the tile
-    const int i0 = (t & 3) * 16;    // 16 consecutive X0 columns
-    const size_t xo = (size_t)mat * p.x_stride + (size_t)(tj * 64 + jl) * p.c_pad + ti * 64 + i0;
+    const int jl = t >> 2;        // transposed row within the tile
+    const int i0 = (t & 3) * 16;  // 16 consecutive transposed columns
+    const size_t xo = xbase + (size_t)(tj * 64 + jl) * p.m_pad + ti * 64 + i0;
     if (XF32) {
-      float* xp = (float*)p.X + xo;
+      float* xp = (float*)p.XT + xo;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *(float4*)(xp + 4 * q) = make_float4(tile[i0 + 4 * q][jl], tile[i0 + 4 * q + 1][jl],
@@ -214,7 +173,7 @@ __global__ void __launch_bounds__(256) prep_cols_kernel(const PrepParams p, int 
       for (int q = 0; q < 8; ++q)
         w[q] = (uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q][jl]) |
                ((uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q + 1][jl]) << 16);
-      uint4* xp = (uint4*)((uint16_t*)p.X + xo);
+      uint4* xp = (uint4*)((uint16_t*)p.XT + xo);
       xp[0] = make_uint4(w[0], w[1], w[2], w[3]);
       xp[1] = make_uint4(w[4], w[5], w[6], w[7]);
     }
@@ -239,32 +198,21 @@ __global__ void __launch_bounds__(256) norm_finalize_kernel(const PrepParams p) 
   }
 }
 
-int prep_blocks_per_mat(int r_pad, int c_pad, int transposed) {
-  if (transposed) return (c_pad / 64) * (r_pad / 64);
-  return ((c_pad + 1023) / 1024) * ((r_pad + PREP_ROWS - 1) / PREP_ROWS);
-}
+int prep_blocks_per_mat(int m_pad, int n_pad) { return (m_pad / 64) * (n_pad / 64); }
 
 hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, int vec,
                        hipStream_t s) {
   const uint64_t blocks = (uint64_t)nmat * p.blocks_per_mat;
   if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  if (blocks > 0x7fffffffull || p.m_pad % 64 || p.n_pad % 64) return hipErrorInvalidValue;
   const dim3 g((uint32_t)blocks), b(256);
-#define PREP_LAUNCH(K, GB, XF) hipLaunchKernelGGL((K<GB, XF>), g, b, 0, s, p, vec)
-  if (p.transposed) {
-    if (grad_bf16) {
-      if (x_f32) PREP_LAUNCH(prep_cols_kernel, true, true); else PREP_LAUNCH(prep_cols_kernel, true, false);
-    } else {
-      if (x_f32) PREP_LAUNCH(prep_cols_kernel, false, true); else PREP_LAUNCH(prep_cols_kernel, false, false);
-    }
+  if (grad_bf16) {
+    if (x_f32) hipLaunchKernelGGL((prep_tile_kernel<true, true>), g, b, 0, s, p, vec);
+    else hipLaunchKernelGGL((prep_tile_kernel<true, false>), g, b, 0, s, p, vec);
   } else {
-    if (grad_bf16) {
-      if (x_f32) PREP_LAUNCH(prep_rows_kernel, true, true); else PREP_LAUNCH(prep_rows_kernel, true, false);
-    } else {
-      if (x_f32) PREP_LAUNCH(prep_rows_kernel, false, true); else PREP_LAUNCH(prep_rows_kernel, false, false);
-    }
+    if (x_f32) hipLaunchKernelGGL((prep_tile_kernel<false, true>), g, b, 0, s, p, vec);
+    else hipLaunchKernelGGL((prep_tile_kernel<false, false>), g, b, 0, s, p, vec);
   }
-#undef PREP_LAUNCH
   return hipGetLastError();
 }
 

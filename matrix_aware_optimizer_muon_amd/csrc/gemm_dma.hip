@@ -1,0 +1,285 @@
+// 256 x 256 MFMA GEMM C = A * B^T with a four-stage LDS ring filled by
+// direct global->LDS loads (gfx950 global_load_lds_dwordx4), for the large
+// products of the Gram-space Newton-Schulz step (SYRK, the r x r recursion
+// and the final product; epilogues in gemm_epilogue.hpp).
+//
+// Both operands are K-contiguous (the prep kernel writes X0 and X0^T).
+// 256 threads = 4 wave64 in 2 x 2, each wave owns 128 x 128 = 4 x 4 blocks of
+// 32x32x16 MFMAs (256 fp32 accumulators).  A stage holds 32 K elements of
+// both 256-row operand tiles (2 x 16 KB); every wave issues 8 one-KB DMA
+// instructions per stage, lane L landing at LDS offset 16*L of its block, so
+// the 16-byte chunk swizzle is applied on the global side.  Up to four stages
+// are in flight; each K step has one barrier, placed so that it both
+// publishes the next stage and retires the reads of the current one.  The
+// two K=16 halves of a stage are software pipelined: the fragments of one
+// half are read from LDS while the MFMAs of the other run.
+#include "common.hpp"
+#include "gemm_epilogue.hpp"
+#include "kernels.h"
+
+namespace muon {
+
+namespace {
+
+constexpr int DT = 256;                        // tile rows / cols
+constexpr int DBK = 32;                        // K elements per stage
+constexpr int DSTAGES = 4;
+constexpr int ROWB = DBK * 2;                  // bytes of one tile row per stage
+constexpr int OPB = DT * ROWB;                 // one operand per stage: 16 KB
+constexpr int STAGEB = 2 * OPB;                // 32 KB
+constexpr int DMA_PER_OP = OPB / 1024 / 4;     // 1-KB DMA instructions per wave per operand
+constexpr int DPS = 2 * DMA_PER_OP;            // per wave per stage (vmcnt units)
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt
+// [6:4] left at its maximum, lgkmcnt [11:8].
+constexpr int wait_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+typedef const __attribute__((address_space(1))) void gbl_ptr_t;
+
+// 16-byte chunk swizzle of a 64-byte row: conflict free for the MFMA
+// fragment reads under both 8-lane (32 banks) and 16-lane (64 banks) LDS
+// service groups.
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int KIND>
+__device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) {
+  if constexpr (KIND == 0) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                               __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+}  // namespace
+
+template <int KIND, int EPI>
+__global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
+  constexpr int RR = 128;
+  constexpr int EPI_LD = DT + 1;
+  constexpr int SMEM_OPS = DSTAGES * STAGEB;
+  constexpr int SMEM_EPI = RR * EPI_LD * 4;
+  constexpr int SMEM_BYTES = SMEM_OPS > SMEM_EPI ? SMEM_OPS : SMEM_EPI;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
+  float* stile = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_mat = p.tiles_per_prod * p.products;
+  const int mat = bid / per_mat;
+  int t = bid - mat * per_mat;
+  const int pi = t / p.tiles_per_prod;
+  t -= pi * p.tiles_per_prod;
+  const int prod = pi + p.prod_base;
+  int ti, tj;
+  if (p.triangular) {
+    ti = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    while (ti * (ti + 1) / 2 > t) --ti;
+    tj = t - ti * (ti + 1) / 2;
+  } else {
+    ti = t / p.tiles_n;
+    tj = t - ti * p.tiles_n;
+  }
+  const int row0A = ti * DT, row0B = tj * DT;
+  const char* Ab = (const char*)p.A + (size_t)mat * p.a_stride * 2;
+  const char* Bb = pi ? (const char*)p.B2 + (size_t)mat * p.b2_stride * 2
+                      : (const char*)p.B + (size_t)mat * p.b_stride * 2;
+
+  // DMA sources: instruction i of this wave fills LDS rows
+  // [(wave*DMA_PER_OP + i)*16, +16) of an operand; lane L -> row (L>>2),
+  // physical chunk (L&3), which holds logical chunk (L&3) ^ swz4(row).
+  const char* srcA[DMA_PER_OP];
+  const char* srcB[DMA_PER_OP];
+#pragma unroll
+  for (int i = 0; i < DMA_PER_OP; ++i) {
+    const int row = (wave * DMA_PER_OP + i) * 16 + (lane >> 2);
+    const int ch = (lane & 3) ^ swz4(row);
+    srcA[i] = Ab + ((size_t)(row0A + row) * p.lda + ch * 8) * 2;
+    srcB[i] = Bb + ((size_t)(row0B + row) * p.ldb + ch * 8) * 2;
+  }
+  auto issue = [&](int ks) {
+    char* sb = smem + (ks & (DSTAGES - 1)) * STAGEB;
+    const int koff = ks * ROWB;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OP; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(srcA[i] + koff),
+                                       (lds_ptr_t*)(sb + (wave * DMA_PER_OP + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < DMA_PER_OP; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(srcB[i] + koff),
+                                       (lds_ptr_t*)(sb + OPB + (wave * DMA_PER_OP + i) * 1024), 16,
+                                       0, 0);
+  };
+
+  // fragment addresses (byte offsets within an operand block) for half s
+  int offA[2][4], offB[2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int ra = wm * 128 + f * 32 + l32;
+      const int rb = wn * 128 + f * 32 + l32;
+      offA[s][f] = ra * ROWB + (((2 * s + h) ^ swz4(ra)) << 4);
+      offB[s][f] = OPB + rb * ROWB + (((2 * s + h) ^ swz4(rb)) << 4);
+    }
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  const int nk = p.Kdim / DBK;
+
+  // prologue: stages 0..3 in flight, wait for stage 0
+#pragma unroll
+  for (int s = 0; s < DSTAGES; ++s)
+    if (s < nk) issue(s);
+  if (nk >= 4) __builtin_amdgcn_s_waitcnt(wait_imm(3 * DPS, 15));
+  else if (nk == 3) __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 15));
+  else if (nk == 2) __builtin_amdgcn_s_waitcnt(wait_imm(DPS, 15));
+  else __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+  barrier();
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    fa0[f] = *(const u32x4*)(smem + offA[0][f]);
+    fb0[f] = *(const u32x4*)(smem + offB[0][f]);
+  }
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* sb = smem + (kt & (DSTAGES - 1)) * STAGEB;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      fa1[f] = *(const u32x4*)(sb + offA[1][f]);
+      fb1[f] = *(const u32x4*)(sb + offB[1][f]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs below
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mfma<KIND>(fa0[i], fb0[j], acc[i][j]);
+    // this wave's reads of stage kt are done and its DMA of stage kt+1 landed
+    if (kt + 3 < nk) __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 0));
+    else if (kt + 3 == nk) __builtin_amdgcn_s_waitcnt(wait_imm(DPS, 0));
+    else __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
+    barrier();
+    if (kt + DSTAGES < nk) issue(kt + DSTAGES);  // refills the buffer of stage kt
+    {  // next stage's first half (unused after the last step; always in LDS bounds)
+      const char* sn = smem + ((kt + 1) & (DSTAGES - 1)) * STAGEB;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        fa0[f] = *(const u32x4*)(sn + offA[0][f]);
+        fb0[f] = *(const u32x4*)(sn + offB[0][f]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mfma<KIND>(fa1[i], fb1[j], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  // Epilogue through LDS, 128 rows per round.  Row pass: each thread takes
+  // four consecutive columns (vector loads/stores, 64 threads per tile row)
+  // and writes the primary value back to LDS; mirror pass (symmetric
+  // results, strictly-lower elements): four consecutive tile rows of one
+  // column become four consecutive elements of the mirrored row.
+  const bool diag = p.triangular && ti == tj;
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    if (wm == round) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int jl = wn * 128 + j * 32 + l32;
+            stile[il * EPI_LD + jl] = acc[i][j][v];
+          }
+    }
+    __syncthreads();
+    const int gr0 = row0A + round * RR;
+    const int jl = (tid & 63) * 4;
+#pragma unroll 4
+    for (int e = 0; e < RR / 4; ++e) {
+      const int il = e * 4 + (tid >> 6);
+      float* sp = stile + il * EPI_LD + jl;
+      const float4 av = make_float4(sp[0], sp[1], sp[2], sp[3]);
+      const int gi = gr0 + il, gj = row0B + jl;
+      if constexpr (EPI == EPI_FINAL) {
+        epilogue_final4(p, mat, gi, gj, av);
+      } else if (!diag) {
+        const float4 pv = epilogue_rr4<EPI>(p, mat, prod, gi, gj, av);
+        sp[0] = pv.x; sp[1] = pv.y; sp[2] = pv.z; sp[3] = pv.w;
+      } else {
+        // diagonal tile: element-wise lower-triangle mask
+        const float a4[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (gi >= gj + k) sp[k] = epilogue_rr1<EPI>(p, mat, prod, gi, gj + k, a4[k]);
+      }
+    }
+    if constexpr (EPI != EPI_FINAL) {
+      __syncthreads();
+      const int il0 = (tid & 31) * 4;
+#pragma unroll 4
+      for (int e = 0; e < DT / 8; ++e) {
+        const int jc = e * 8 + (tid >> 5);
+        const int gi0 = gr0 + il0, gj = row0B + jc;
+        const float4 pv = make_float4(stile[il0 * EPI_LD + jc], stile[(il0 + 1) * EPI_LD + jc],
+                                      stile[(il0 + 2) * EPI_LD + jc], stile[(il0 + 3) * EPI_LD + jc]);
+        const size_t o = (size_t)mat * p.rr_stride + (size_t)gj * p.ldr + gi0;
+        if (!diag) {
+          store_rr4<EPI>(p, o, prod, pv, pv);
+        } else {
+          const float a4[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (gi0 + k > gj) store_rr1<EPI>(p, o + k, prod, a4[k]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int KIND, int EPI>
+static hipError_t launch_dma_one(const GemmParams& p, int nmat, hipStream_t s) {
+  const uint64_t blocks = (uint64_t)nmat * p.tiles_per_prod * p.products;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  if (p.Kdim % DBK != 0 || p.Mdim % DT != 0 || p.Ndim % DT != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_dma_kernel<KIND, EPI>), dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s) {
+  switch (epi) {
+    case EPI_SYRK: return launch_dma_one<0, EPI_SYRK>(p, nmat, s);
+    case EPI_POLY: return launch_dma_one<1, EPI_POLY>(p, nmat, s);
+    case EPI_PQPG: return launch_dma_one<1, EPI_PQPG>(p, nmat, s);
+    case EPI_PH: return launch_dma_one<1, EPI_PH>(p, nmat, s);
+    case EPI_FINAL: return launch_dma_one<0, EPI_FINAL>(p, nmat, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace muon

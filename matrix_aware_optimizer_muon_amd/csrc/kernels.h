@@ -40,6 +40,7 @@ struct GemmParams {
   void* Gh;
   void* Ph;
   void* Qh_dst;
+  const void* Qh_src;      // fp16 copy of the previous Q (fp16-only epilogues)
   void* Hh;
   int64_t rr_stride;       // elements between matrices in r x r buffers
   int ldr;                 // r_pad
@@ -52,21 +53,23 @@ struct GemmParams {
   int out_rows, out_cols;  // m, n of the parameter
   float decay;             // 1 - lr*wd
   float step;              // lr * scale_coeff * sqrt(max(m, n))
+  int vec;                 // W / O rows allow 16-byte access
 };
 
-hipError_t launch_gemm(const GemmParams& p, int epi, int op, int bt, int a_kstrided,
-                       int b_kstrided, int nmat, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, int epi, int op, int bt, int nmat, hipStream_t s);
+// 256-tile 16-bit products with the direct-to-LDS pipeline (gemm_dma.hip)
+hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s);
 
 // ---- memory-bound kernels ------------------------------------------------
 struct PrepParams {
   const MatPtrs* table;
   int m, n;                // parameter shape
-  int r_pad, c_pad;        // X~ padded shape (r x c oriented)
-  int transposed;          // m > n
+  int m_pad, n_pad;        // padded natural shape (multiples of 64)
   float mu;
   int nesterov;
-  void* X;                 // X~ for matrix 0 of the chunk
-  int64_t x_stride;        // elements between matrices
+  void* X;                 // U, natural layout m_pad x n_pad (matrix 0 of the chunk)
+  void* XT;                // U^T, n_pad x m_pad
+  int64_t x_stride;        // elements between matrices (both copies)
   float* partials;         // [nmat][blocks_per_mat]
   int blocks_per_mat;
   float* inv_norm;         // [nmat]
@@ -75,7 +78,7 @@ struct PrepParams {
 hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, int vec,
                        hipStream_t s);
 hipError_t launch_norm_finalize(const PrepParams& p, int nmat, hipStream_t s);
-int prep_blocks_per_mat(int r_pad, int c_pad, int transposed);
+int prep_blocks_per_mat(int m_pad, int n_pad);
 
 struct RowNormParams {
   const MatPtrs* table;

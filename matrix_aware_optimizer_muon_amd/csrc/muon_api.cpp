@@ -53,7 +53,9 @@ struct Chunk {
 
 struct Bucket {
   int64_t m, n, r, c, r_pad, c_pad;
+  int64_t m_pad, n_pad;  // padded natural shape (m_pad x n_pad)
   bool transposed;
+  bool dma;  // 256-tile direct-to-LDS path with fp16-only r x r buffers
   int bt;
   int first, count;  // range in plan order
   std::vector<Chunk> chunks;
@@ -328,17 +330,24 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       for (int i : members[b]) p->order.push_back(i);
       const int64_t xes = f32path ? 4 : 2;
       const int64_t rr = B.r_pad * B.r_pad;
-      B.scratch_per_mat = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes)) +
-                          (f32path ? 5 * (int64_t)align256((size_t)(rr * 4))
-                                   : 4 * (int64_t)align256((size_t)(rr * 4)) +
-                                         5 * (int64_t)align256((size_t)(rr * 2)));
+      B.dma = !f32path && B.bt == 256;
+      // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
+      // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
+      // the 256-tile path keeps only the fp16 copies
+      const int64_t rr_bytes =
+          f32path ? 5 * (int64_t)align256((size_t)(rr * 4))
+                  : (B.dma ? 0 : 4 * (int64_t)align256((size_t)(rr * 4))) +
+                        5 * (int64_t)align256((size_t)(rr * 2));
+      B.scratch_per_mat = 2 * (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes)) + rr_bytes;
       int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
       per_chunk = std::min<int64_t>(per_chunk, B.count);
       const int64_t nchunks = (B.count + per_chunk - 1) / per_chunk;
       const int64_t even = (B.count + nchunks - 1) / nchunks;
       for (int64_t f = 0; f < B.count; f += even)
         B.chunks.push_back(Chunk{B.first + (int)f, (int)std::min<int64_t>(even, B.count - f)});
-      B.prep_blocks = prep_blocks_per_mat((int)B.r_pad, (int)B.c_pad, B.transposed ? 1 : 0);
+      B.m_pad = B.transposed ? B.c_pad : B.r_pad;
+      B.n_pad = B.transposed ? B.r_pad : B.c_pad;
+      B.prep_blocks = prep_blocks_per_mat((int)B.m_pad, (int)B.n_pad);
       B.rn_row_blocks = rownorm_row_blocks((int)B.m, (int)B.n);
       max_scratch = std::max(max_scratch, (size_t)(even * B.scratch_per_mat));
       part_floats = std::max(part_floats, (size_t)even * (size_t)B.prep_blocks);
@@ -429,10 +438,20 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       const size_t xbytes = align256((size_t)(B.r_pad * B.c_pad * xes));
       const size_t f32b = align256((size_t)(rr * 4));
       const size_t h16b = f32path ? f32b : align256((size_t)(rr * 2));
-      void* X = take(xbytes);
-      float* Gf = (float*)take(f32b);
-      float* Qf[2] = {(float*)take(f32b), (float*)take(f32b)};
-      float* Hf = (float*)take(f32b);
+      void* Xnat = take(xbytes);  // U, m_pad x n_pad
+      void* Xtr = take(xbytes);   // U^T, n_pad x m_pad
+      // X0 = O(U) is r_pad x c_pad (ld c_pad); X0^T is c_pad x r_pad (ld r_pad)
+      void* X = B.transposed ? Xtr : Xnat;
+      void* XT = B.transposed ? Xnat : Xtr;
+      float* Gf = nullptr;
+      float* Qf[2] = {nullptr, nullptr};
+      float* Hf = nullptr;
+      if (!B.dma) {
+        Gf = (float*)take(f32b);
+        Qf[0] = (float*)take(f32b);
+        Qf[1] = (float*)take(f32b);
+        Hf = (float*)take(f32b);
+      }
       void* Gh;
       void* Ph;
       void* Qh[2];
@@ -457,6 +476,10 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       // stride; r_pad is a multiple of 64, so both are exactly r_pad^2
       if (rr_stride != h_stride || rr_stride != rr) return MUON_ERR_HIP;
       const int vec = chunk_vec(p, B, ch);
+      auto gemm = [&](const GemmParams& gp, int epi) {
+        return B.dma ? launch_gemm_dma(gp, epi, nm, stream)
+                     : launch_gemm(gp, epi, op, B.bt, nm, stream);
+      };
       // algorithmic work per matrix (true sizes; symmetric products on the
       // lower triangle): SYRK r^2 c, each r x r product r^3, final 2 r^2 c
       const double r2 = (double)B.r * B.r, r3 = r2 * B.r, cc = (double)B.c;
@@ -467,18 +490,18 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       pp.table = d_table + ch.first;
       pp.m = (int)B.m;
       pp.n = (int)B.n;
-      pp.r_pad = (int)B.r_pad;
-      pp.c_pad = (int)B.c_pad;
-      pp.transposed = B.transposed ? 1 : 0;
+      pp.m_pad = (int)B.m_pad;
+      pp.n_pad = (int)B.n_pad;
       pp.mu = hp.momentum;
       pp.nesterov = hp.nesterov;
-      pp.X = X;
+      pp.X = Xnat;
+      pp.XT = Xtr;
       pp.x_stride = x_stride;
       pp.partials = d_part;
       pp.blocks_per_mat = B.prep_blocks;
       pp.inv_norm = d_inv + ch.first;
       const double elems = (double)B.m * B.n * nm;
-      st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + xes), [&] {
+      st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + 2 * xes), [&] {
         return launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream);
       });
       if (st != MUON_OK) return st;
@@ -532,7 +555,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       g.tiles_per_prod = ntri;
       g.products = 1;
       st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (xes * rcf + r2 * (4 + (f32path ? 0 : 2))) * nm,
-                 [&] { return launch_gemm(g, EPI_SYRK, op, B.bt, 0, 0, nm, stream); });
+                 [&] { return gemm(g, EPI_SYRK); });
       if (st != MUON_OK) return st;
 
       for (int k = 0; k < N; ++k) {
@@ -542,10 +565,11 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         g.Qf_src = Qf[src];
         g.Qf_dst = Qf[dst];
         g.Qh_dst = Qh[dst];
+        g.Qh_src = Qh[src];
         // P~ = b G + c G^2 (and Q1 = a I + P~ on the first iteration)
         rr_setup(Gh, Gh, Gh, 1);
         st = timed(p, stream, MUON_K_POLY, r3 * nm, r2 * (hes + 4 + hes) * nm,
-                   [&] { return launch_gemm(g, EPI_POLY, op, B.bt, 0, 0, nm, stream); });
+                   [&] { return gemm(g, EPI_POLY); });
         if (st != MUON_OK) return st;
         const bool need_q = k > 0;
         const bool need_h = k < N - 1;
@@ -563,7 +587,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
           }
           const int np = g.products;
           st = timed(p, stream, MUON_K_PQPG, r3 * np * nm, r2 * (hes + np * (hes + 4 + 4 + hes)) * nm,
-                     [&] { return launch_gemm(g, EPI_PQPG, op, B.bt, 0, 0, nm, stream); });
+                     [&] { return gemm(g, EPI_PQPG); });
           g.prod_base = 0;
           if (st != MUON_OK) return st;
         }
@@ -571,7 +595,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
           // G_k = a H + P~ H
           rr_setup(Ph, Hh, Hh, 1);
           st = timed(p, stream, MUON_K_PH, r3 * nm, r2 * (hes + hes + 4 + 4 + hes) * nm,
-                     [&] { return launch_gemm(g, EPI_PH, op, B.bt, 0, 0, nm, stream); });
+                     [&] { return gemm(g, EPI_PH); });
           if (st != MUON_OK) return st;
         }
       }
@@ -582,39 +606,35 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       fg.Kdim = (int)B.r_pad;
       fg.triangular = 0;
       fg.products = 1;
+      fg.vec = vec;
       fg.out_rows = (int)B.m;
       fg.out_cols = (int)B.n;
       fg.decay = (float)(1.0 - (double)lr * wd);
       fg.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
-      int aks, bks;
-      if (!B.transposed) {  // O (r x c) = Q (r x r) * X0 (r x c): B K-strided
+      if (!B.transposed) {  // O (r x c) = Q (r x r) * (X0^T)^T
         fg.A = Qfinal;
         fg.a_stride = h_stride;
         fg.lda = (int)B.r_pad;
-        fg.B = fg.B2 = X;
+        fg.B = fg.B2 = XT;
         fg.b_stride = fg.b2_stride = x_stride;
-        fg.ldb = (int)B.c_pad;
+        fg.ldb = (int)B.r_pad;
         fg.Mdim = (int)B.r_pad;
         fg.Ndim = (int)B.c_pad;
-        aks = 0;
-        bks = 1;
-      } else {  // O^T (c x r) = X0^T (c x r) * Q: A K-strided
-        fg.A = X;
+      } else {  // O^T (c x r) = X0^T (c x r) * Q
+        fg.A = XT;
         fg.a_stride = x_stride;
-        fg.lda = (int)B.c_pad;
+        fg.lda = (int)B.r_pad;
         fg.B = fg.B2 = Qfinal;
         fg.b_stride = fg.b2_stride = h_stride;
         fg.ldb = (int)B.r_pad;
         fg.Mdim = (int)B.c_pad;
         fg.Ndim = (int)B.r_pad;
-        aks = 1;
-        bks = 0;
       }
       fg.tiles_m = fg.Mdim / B.bt;
       fg.tiles_n = fg.Ndim / B.bt;
       fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
       st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + hes * r2 + 8.0 * rcf) * nm,
-                 [&] { return launch_gemm(fg, EPI_FINAL, op, B.bt, aks, bks, nm, stream); });
+                 [&] { return gemm(fg, EPI_FINAL); });
       if (st != MUON_OK) return st;
     }
   }
