@@ -108,18 +108,17 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
     srcA[i] = Ab + ((size_t)(row0A + row) * p.lda + ch * 8) * 2;
     srcB[i] = Bb + ((size_t)(row0B + row) * p.ldb + ch * 8) * 2;
   }
-  auto issue = [&](int ks) {
-    char* sb = smem + (ks & (DSTAGES - 1)) * STAGEB;
-    const int koff = ks * ROWB;
-#pragma unroll
-    for (int i = 0; i < DMA_PER_OP; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(srcA[i] + koff),
-                                       (lds_ptr_t*)(sb + (wave * DMA_PER_OP + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < DMA_PER_OP; ++i)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t*)(srcB[i] + koff),
-                                       (lds_ptr_t*)(sb + OPB + (wave * DMA_PER_OP + i) * 1024), 16,
-                                       0, 0);
+  // One 1-KB DMA instruction (q = 0..DPS-1: A blocks, then B blocks) of
+  // stage ks into ring buffer `buf`.  Stages past the last one re-read the
+  // last stage (in bounds; their buffer is never read), so every K step
+  // issues the same number of DMAs and the vmcnt bookkeeping is constant.
+  const int nk = p.Kdim / DBK;
+  auto dma = [&](int q, int buf, int ks) {
+    const int koff = (ks < nk ? ks : nk - 1) * ROWB;
+    char* sb = smem + buf * STAGEB + (q >= DMA_PER_OP ? OPB : 0) +
+               (wave * DMA_PER_OP + (q % DMA_PER_OP)) * 1024;
+    const char* src = (q < DMA_PER_OP ? srcA[q] : srcB[q - DMA_PER_OP]) + koff;
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)sb, 16, 0, 0);
   };
 
   // fragment addresses (byte offsets within an operand block) for half s
@@ -143,16 +142,13 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
-  const int nk = p.Kdim / DBK;
 
   // prologue: stages 0..3 in flight, wait for stage 0
 #pragma unroll
-  for (int s = 0; s < DSTAGES; ++s)
-    if (s < nk) issue(s);
-  if (nk >= 4) __builtin_amdgcn_s_waitcnt(wait_imm(3 * DPS, 15));
-  else if (nk == 3) __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 15));
-  else if (nk == 2) __builtin_amdgcn_s_waitcnt(wait_imm(DPS, 15));
-  else __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+  for (int st = 0; st < DSTAGES; ++st)
+#pragma unroll
+    for (int q = 0; q < DPS; ++q) dma(q, st, st);
+  __builtin_amdgcn_s_waitcnt(wait_imm(3 * DPS, 15));
   barrier();
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
@@ -161,24 +157,29 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
   }
 
   for (int kt = 0; kt < nk; ++kt) {
-    const char* sb = smem + (kt & (DSTAGES - 1)) * STAGEB;
+    const int buf = kt & (DSTAGES - 1);
+    const char* sb = smem + buf * STAGEB;
+    // first half: 4 MFMAs, then this stage's second-half fragment reads,
+    // then the remaining 12 MFMAs (the reads land behind them)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mfma<KIND>(fa0[0], fb0[j], acc[0][j]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       fa1[f] = *(const u32x4*)(sb + offA[1][f]);
       fb1[f] = *(const u32x4*)(sb + offB[1][f]);
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs below
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 1; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mfma<KIND>(fa0[i], fb0[j], acc[i][j]);
-    // this wave's reads of stage kt are done and its DMA of stage kt+1 landed
-    if (kt + 3 < nk) __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 0));
-    else if (kt + 3 == nk) __builtin_amdgcn_s_waitcnt(wait_imm(DPS, 0));
-    else __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt+1 landed for this wave (stages kt+2, kt+3 may still fly) and
+    // this wave's reads of stage kt are done; then publish / retire
+    __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 0));
     barrier();
-    if (kt + DSTAGES < nk) issue(kt + DSTAGES);  // refills the buffer of stage kt
-    {  // next stage's first half (unused after the last step; always in LDS bounds)
+    {  // next stage's first half (unused after the last step; in LDS bounds)
       const char* sn = smem + ((kt + 1) & (DSTAGES - 1)) * STAGEB;
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -187,22 +188,56 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // second half, with the refill of this stage's buffer (stage kt+4)
+    // interleaved: two MFMAs per DMA instruction
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mfma<KIND>(fa1[i], fb1[j], acc[i][j]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 8; ++g) {
+      mfma<KIND>(fa1[(2 * g) >> 2], fb1[(2 * g) & 3], acc[(2 * g) >> 2][(2 * g) & 3]);
+      mfma<KIND>(fa1[(2 * g + 1) >> 2], fb1[(2 * g + 1) & 3], acc[(2 * g + 1) >> 2][(2 * g + 1) & 3]);
+      if (g < DPS) dma(g, buf, kt + DSTAGES);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
   __syncthreads();
 
-  // Epilogue through LDS, 128 rows per round.  Row pass: each thread takes
-  // four consecutive columns (vector loads/stores, 64 threads per tile row)
-  // and writes the primary value back to LDS; mirror pass (symmetric
-  // results, strictly-lower elements): four consecutive tile rows of one
-  // column become four consecutive elements of the mirrored row.
+  // Epilogue through LDS, 128 rows per round.  At the start of a round all
+  // of its global inputs (the fp16 identity-term operand, or W for the final
+  // product) are requested at once, 32 loads per thread, so their latency
+  // overlaps the staging of the accumulators.  Row pass: each thread takes
+  // four consecutive columns (64 threads per tile row) and writes the primary
+  // value back to LDS; mirror pass (symmetric results, strictly-lower
+  // elements): four consecutive tile rows of one column become four
+  // consecutive elements of the mirrored row.
   const bool diag = p.triangular && ti == tj;
+  const int jl = (tid & 63) * 4;
+  const int gj = row0B + jl;
+  constexpr int PER = RR / 4;  // row-pass iterations per round
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
+    const int gr0 = row0A + round * RR;
+    uint2 hin[EPI == EPI_FINAL || EPI == EPI_SYRK ? 1 : PER];
+    float4 win[EPI == EPI_FINAL ? PER : 1];
+    bool wvec = false;
+    if constexpr (EPI == EPI_FINAL) {
+      const MatPtrs mp = p.table[mat];
+      wvec = p.vec && gj + 4 <= p.out_cols;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int gi = gr0 + e * 4 + (tid >> 6);
+        win[e] = (wvec && gi < p.out_rows) ? *(const float4*)(mp.W + (size_t)gi * p.out_cols + gj)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else if constexpr (EPI != EPI_SYRK) {
+      if (!diag) {
+        float inv_scale;
+        const uint16_t* src = (const uint16_t*)rr_input<EPI>(p, prod, &inv_scale);
+        const size_t base = (size_t)mat * p.rr_stride + gj;
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          hin[e] = *(const uint2*)(src + base + (size_t)(gr0 + e * 4 + (tid >> 6)) * p.ldr);
+      }
+    }
     if (wm == round) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -211,24 +246,37 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int jl = wn * 128 + j * 32 + l32;
-            stile[il * EPI_LD + jl] = acc[i][j][v];
+            const int jc = wn * 128 + j * 32 + l32;
+            stile[il * EPI_LD + jc] = acc[i][j][v];
           }
     }
     __syncthreads();
-    const int gr0 = row0A + round * RR;
-    const int jl = (tid & 63) * 4;
-#pragma unroll 4
-    for (int e = 0; e < RR / 4; ++e) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
       const int il = e * 4 + (tid >> 6);
       float* sp = stile + il * EPI_LD + jl;
       const float4 av = make_float4(sp[0], sp[1], sp[2], sp[3]);
-      const int gi = gr0 + il, gj = row0B + jl;
+      const int gi = gr0 + il;
       if constexpr (EPI == EPI_FINAL) {
-        epilogue_final4(p, mat, gi, gj, av);
+        if (wvec) {
+          if (gi < p.out_rows) {
+            const MatPtrs mp = p.table[mat];
+            const float inv = p.inv_norm[mat];
+            const float4 o = make_float4(av.x * inv, av.y * inv, av.z * inv, av.w * inv);
+            const size_t idx = (size_t)gi * p.out_cols + gj;
+            *(float4*)(mp.W + idx) = f4_axpy(p.decay, win[e], -p.step, o);
+            if (mp.O) *(float4*)(mp.O + idx) = o;
+          }
+        } else {
+          epilogue_final4(p, mat, gi, gj, av);
+        }
       } else if (!diag) {
-        const float4 pv = epilogue_rr4<EPI>(p, mat, prod, gi, gj, av);
-        sp[0] = pv.x; sp[1] = pv.y; sp[2] = pv.z; sp[3] = pv.w;
+        const float4 pv =
+            epilogue_rr4_pre<EPI>(p, mat, prod, gi, gj, av, hin[EPI == EPI_SYRK ? 0 : e]);
+        sp[0] = pv.x;
+        sp[1] = pv.y;
+        sp[2] = pv.z;
+        sp[3] = pv.w;
       } else {
         // diagonal tile: element-wise lower-triangle mask
         const float a4[4] = {av.x, av.y, av.z, av.w};
@@ -240,20 +288,20 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
     if constexpr (EPI != EPI_FINAL) {
       __syncthreads();
       const int il0 = (tid & 31) * 4;
-#pragma unroll 4
+#pragma unroll 8
       for (int e = 0; e < DT / 8; ++e) {
         const int jc = e * 8 + (tid >> 5);
-        const int gi0 = gr0 + il0, gj = row0B + jc;
+        const int gi0 = gr0 + il0, gjm = row0B + jc;
         const float4 pv = make_float4(stile[il0 * EPI_LD + jc], stile[(il0 + 1) * EPI_LD + jc],
                                       stile[(il0 + 2) * EPI_LD + jc], stile[(il0 + 3) * EPI_LD + jc]);
-        const size_t o = (size_t)mat * p.rr_stride + (size_t)gj * p.ldr + gi0;
+        const size_t o = (size_t)mat * p.rr_stride + (size_t)gjm * p.ldr + gi0;
         if (!diag) {
           store_rr4<EPI>(p, o, prod, pv, pv);
         } else {
           const float a4[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            if (gi0 + k > gj) store_rr1<EPI>(p, o + k, prod, a4[k]);
+            if (gi0 + k > gjm) store_rr1<EPI>(p, o + k, prod, a4[k]);
         }
       }
     }

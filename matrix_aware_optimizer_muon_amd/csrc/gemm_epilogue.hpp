@@ -218,6 +218,53 @@ __device__ __forceinline__ float4 epilogue_rr4(const GemmParams& p, int mat, int
   return v;
 }
 
+// Row pass with the identity-term input already loaded (4 raw fp16 values).
+__device__ __forceinline__ float4 h4_from_raw(uint2 u, float inv_scale) {
+  const _Float16* h = (const _Float16*)&u;
+  return make_float4((float)h[0] * inv_scale, (float)h[1] * inv_scale, (float)h[2] * inv_scale,
+                     (float)h[3] * inv_scale);
+}
+
+template <int EPI>
+__device__ __forceinline__ const void* rr_input(const GemmParams& p, int prod, float* inv_scale) {
+  if constexpr (EPI == EPI_POLY) {
+    *inv_scale = 1.0f / p.sG;
+    return p.Gh;
+  } else if constexpr (EPI == EPI_PQPG) {
+    *inv_scale = prod == 1 ? 1.0f / p.sG : 1.0f / p.sQ;
+    return prod == 1 ? p.Gh : p.Qh_src;
+  } else {  // EPI_PH
+    *inv_scale = 1.0f / p.sH;
+    return p.Hh;
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ float4 epilogue_rr4_pre(const GemmParams& p, int mat, int prod, int gi,
+                                                   int gj, float4 acc, uint2 raw) {
+  const size_t o = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
+  float4 v, q;
+  if constexpr (EPI == EPI_SYRK) {
+    const float inv = p.inv_norm[mat];
+    v = f4_axpy(inv * inv, acc, 0.0f, acc);
+    q = v;
+  } else if constexpr (EPI == EPI_POLY) {
+    v = f4_axpy(p.b, h4_from_raw(raw, 1.0f / p.sG), p.c * (1.0f / (p.sG * p.sG)), acc);
+    q = v;
+    if (p.first) {  // off-diagonal tile: Q1 = P~ there
+    }
+  } else if constexpr (EPI == EPI_PQPG) {
+    if (prod == 1) v = f4_axpy(p.a, h4_from_raw(raw, 1.0f / p.sG), 1.0f / (p.sP * p.sG), acc);
+    else v = f4_axpy(p.a, h4_from_raw(raw, 1.0f / p.sQ), 1.0f / (p.sP * p.sQ), acc);
+    q = v;
+  } else {  // EPI_PH
+    v = f4_axpy(p.a, h4_from_raw(raw, 1.0f / p.sH), 1.0f / (p.sP * p.sH), acc);
+    q = v;
+  }
+  store_rr4<EPI>(p, o, prod, v, q);
+  return v;
+}
+
 // Final product: O = acc / ||U||, W <- decay W - step O at (gi, gj..gj+3).
 __device__ __forceinline__ void epilogue_final4(const GemmParams& p, int mat, int gi, int gj,
                                                 float4 acc) {
