@@ -4,11 +4,13 @@
 // and the final product; epilogues in gemm_epilogue.hpp).
 //
 // Both operands are K-contiguous (the prep kernel writes X0 and X0^T).
-// 256 threads = 4 wave64 in 2 x 2, each wave owns 128 x 128 = 4 x 4 blocks of
-// 32x32x16 MFMAs (256 fp32 accumulators).  A stage holds 32 K elements of
-// both 256-row operand tiles (2 x 16 KB); every wave issues 8 one-KB DMA
-// instructions per stage, lane L landing at LDS offset 16*L of its block, so
-// the 16-byte chunk swizzle is applied on the global side.  Up to four stages
+// 8 wave64 (two per SIMD) in 2 x 4, each owning 128 x 64 = 4 x 2 blocks of
+// 32x32x16 MFMAs (128 fp32 accumulators), so one wave's barrier, DMA-issue
+// and LDS waits overlap the other's MFMAs (a 4-wave 128 x 128 variant is
+// kept as a template option).  A stage holds 32 K elements of both 256-row
+// operand tiles (2 x 16 KB); every 1-KB DMA instruction lands lane L at LDS
+// offset 16*L of its block, so the 16-byte chunk swizzle is applied on the
+// global side.  Up to four stages
 // are in flight; each K step has one barrier, placed so that it both
 // publishes the next stage and retires the reads of the current one.  The
 // two K=16 halves of a stage are software pipelined: the fragments of one
@@ -27,8 +29,6 @@ constexpr int DSTAGES = 4;
 constexpr int ROWB = DBK * 2;                  // bytes of one tile row per stage
 constexpr int OPB = DT * ROWB;                 // one operand per stage: 16 KB
 constexpr int STAGEB = 2 * OPB;                // 32 KB
-constexpr int DMA_PER_OP = OPB / 1024 / 4;     // 1-KB DMA instructions per wave per operand
-constexpr int DPS = 2 * DMA_PER_OP;            // per wave per stage (vmcnt units)
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in [3:0] and [15:14], expcnt
 // [6:4] left at its maximum, lgkmcnt [11:8].
@@ -59,8 +59,18 @@ __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) 
 
 }  // namespace
 
-template <int KIND, int EPI>
-__global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
+// NW = 4: waves in 2 x 2, each 128 x 128 (4 x 4 MFMA blocks, one wave per SIMD)
+// NW = 8: waves in 2 x 4, each 128 x 64 (4 x 2 MFMA blocks, two waves per SIMD)
+template <int KIND, int EPI, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p) {
+  constexpr int NT = 64 * NW;                    // threads
+  constexpr int WGN = NW / 2;                    // waves along N
+  constexpr int WTN = DT / WGN;                  // wave tile N (128 or 64)
+  constexpr int FM = 4, FN = WTN / 32;           // MFMA blocks per wave
+  constexpr int DMA_PER_OP = OPB / 1024 / NW;    // 1-KB DMA instructions per wave per operand
+  constexpr int DPS = 2 * DMA_PER_OP;            // per wave per stage (vmcnt units)
+  constexpr int NMF = FM * FN;                   // MFMAs per half stage
+  static_assert(NMF == 2 * DPS, "two MFMAs per DMA instruction");
   constexpr int RR = 128;
   constexpr int EPI_LD = DT + 1;
   constexpr int SMEM_OPS = DSTAGES * STAGEB;
@@ -71,7 +81,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int h = lane >> 5, l32 = lane & 31;
 
   const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -121,27 +131,31 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)sb, 16, 0, 0);
   };
 
-  // fragment addresses (byte offsets within an operand block) for half s
-  int offA[2][4], offB[2][4];
+  // fragment addresses (byte offsets within a stage) for half s
+  int offA[2][FM], offB[2][FN];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
+    for (int f = 0; f < FM; ++f) {
       const int ra = wm * 128 + f * 32 + l32;
-      const int rb = wn * 128 + f * 32 + l32;
       offA[s][f] = ra * ROWB + (((2 * s + h) ^ swz4(ra)) << 4);
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      const int rb = wn * WTN + f * 32 + l32;
       offB[s][f] = OPB + rb * ROWB + (((2 * s + h) ^ swz4(rb)) << 4);
     }
+  }
 
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  u32x4 fa0[4], fb0[4], fa1[4], fb1[4];
+  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
   // prologue: stages 0..3 in flight, wait for stage 0
 #pragma unroll
@@ -151,29 +165,27 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
   __builtin_amdgcn_s_waitcnt(wait_imm(3 * DPS, 15));
   barrier();
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    fa0[f] = *(const u32x4*)(smem + offA[0][f]);
-    fb0[f] = *(const u32x4*)(smem + offB[0][f]);
-  }
+  for (int f = 0; f < FM; ++f) fa0[f] = *(const u32x4*)(smem + offA[0][f]);
+#pragma unroll
+  for (int f = 0; f < FN; ++f) fb0[f] = *(const u32x4*)(smem + offB[0][f]);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & (DSTAGES - 1);
     const char* sb = smem + buf * STAGEB;
-    // first half: 4 MFMAs, then this stage's second-half fragment reads,
-    // then the remaining 12 MFMAs (the reads land behind them)
+    // first half: one row of MFMAs, then this stage's second-half fragment
+    // reads, then the remaining MFMAs (the reads land behind them)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) mfma<KIND>(fa0[0], fb0[j], acc[0][j]);
+    for (int j = 0; j < FN; ++j) mfma<KIND>(fa0[0], fb0[j], acc[0][j]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      fa1[f] = *(const u32x4*)(sb + offA[1][f]);
-      fb1[f] = *(const u32x4*)(sb + offB[1][f]);
-    }
+    for (int f = 0; f < FM; ++f) fa1[f] = *(const u32x4*)(sb + offA[1][f]);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) fb1[f] = *(const u32x4*)(sb + offB[1][f]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 1; i < 4; ++i)
+    for (int i = 1; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma<KIND>(fa0[i], fb0[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) mfma<KIND>(fa0[i], fb0[j], acc[i][j]);
     __builtin_amdgcn_sched_barrier(0);
     // stage kt+1 landed for this wave (stages kt+2, kt+3 may still fly) and
     // this wave's reads of stage kt are done; then publish / retire
@@ -182,19 +194,19 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
     {  // next stage's first half (unused after the last step; in LDS bounds)
       const char* sn = smem + ((kt + 1) & (DSTAGES - 1)) * STAGEB;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        fa0[f] = *(const u32x4*)(sn + offA[0][f]);
-        fb0[f] = *(const u32x4*)(sn + offB[0][f]);
-      }
+      for (int f = 0; f < FM; ++f) fa0[f] = *(const u32x4*)(sn + offA[0][f]);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) fb0[f] = *(const u32x4*)(sn + offB[0][f]);
     }
     __builtin_amdgcn_sched_barrier(0);
     // second half, with the refill of this stage's buffer (stage kt+4)
     // interleaved: two MFMAs per DMA instruction
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      mfma<KIND>(fa1[(2 * g) >> 2], fb1[(2 * g) & 3], acc[(2 * g) >> 2][(2 * g) & 3]);
-      mfma<KIND>(fa1[(2 * g + 1) >> 2], fb1[(2 * g + 1) & 3], acc[(2 * g + 1) >> 2][(2 * g + 1) & 3]);
-      if (g < DPS) dma(g, buf, kt + DSTAGES);
+    for (int g = 0; g < DPS; ++g) {
+      mfma<KIND>(fa1[(2 * g) / FN], fb1[(2 * g) % FN], acc[(2 * g) / FN][(2 * g) % FN]);
+      mfma<KIND>(fa1[(2 * g + 1) / FN], fb1[(2 * g + 1) % FN],
+                 acc[(2 * g + 1) / FN][(2 * g + 1) % FN]);
+      dma(g, buf, kt + DSTAGES);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -203,16 +215,17 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
 
   // Epilogue through LDS, 128 rows per round.  At the start of a round all
   // of its global inputs (the fp16 identity-term operand, or W for the final
-  // product) are requested at once, 32 loads per thread, so their latency
-  // overlaps the staging of the accumulators.  Row pass: each thread takes
-  // four consecutive columns (64 threads per tile row) and writes the primary
-  // value back to LDS; mirror pass (symmetric results, strictly-lower
-  // elements): four consecutive tile rows of one column become four
-  // consecutive elements of the mirrored row.
+  // product) are requested at once, so their latency overlaps the staging of
+  // the accumulators.  Row pass: each thread takes four consecutive columns
+  // (64 threads per tile row) and writes the primary value back to LDS;
+  // mirror pass (symmetric results, strictly-lower elements): four
+  // consecutive tile rows of one column become four consecutive elements of
+  // the mirrored row.
   const bool diag = p.triangular && ti == tj;
   const int jl = (tid & 63) * 4;
   const int gj = row0B + jl;
-  constexpr int PER = RR / 4;  // row-pass iterations per round
+  constexpr int RPI = NT / 64;   // tile rows per row-pass iteration
+  constexpr int PER = RR / RPI;  // row-pass iterations per round
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int gr0 = row0A + round * RR;
@@ -224,7 +237,7 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
       wvec = p.vec && gj + 4 <= p.out_cols;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const int gi = gr0 + e * 4 + (tid >> 6);
+        const int gi = gr0 + e * RPI + (tid >> 6);
         win[e] = (wvec && gi < p.out_rows) ? *(const float4*)(mp.W + (size_t)gi * p.out_cols + gj)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -235,25 +248,25 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
         const size_t base = (size_t)mat * p.rr_stride + gj;
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-          hin[e] = *(const uint2*)(src + base + (size_t)(gr0 + e * 4 + (tid >> 6)) * p.ldr);
+          hin[e] = *(const uint2*)(src + base + (size_t)(gr0 + e * RPI + (tid >> 6)) * p.ldr);
       }
     }
     if (wm == round) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int jc = wn * 128 + j * 32 + l32;
+            const int jc = wn * WTN + j * 32 + l32;
             stile[il * EPI_LD + jc] = acc[i][j][v];
           }
     }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int il = e * 4 + (tid >> 6);
+      const int il = e * RPI + (tid >> 6);
       float* sp = stile + il * EPI_LD + jl;
       const float4 av = make_float4(sp[0], sp[1], sp[2], sp[3]);
       const int gi = gr0 + il;
@@ -288,9 +301,10 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
     if constexpr (EPI != EPI_FINAL) {
       __syncthreads();
       const int il0 = (tid & 31) * 4;
+      constexpr int CPI = NT / 32;  // mirror columns per iteration
 #pragma unroll 8
-      for (int e = 0; e < DT / 8; ++e) {
-        const int jc = e * 8 + (tid >> 5);
+      for (int e = 0; e < DT / CPI; ++e) {
+        const int jc = e * CPI + (tid >> 5);
         const int gi0 = gr0 + il0, gjm = row0B + jc;
         const float4 pv = make_float4(stile[il0 * EPI_LD + jc], stile[(il0 + 1) * EPI_LD + jc],
                                       stile[(il0 + 2) * EPI_LD + jc], stile[(il0 + 3) * EPI_LD + jc]);
@@ -309,13 +323,19 @@ __global__ void __launch_bounds__(256, 1) gemm_dma_kernel(const GemmParams p) {
   }
 }
 
+#ifndef MUON_DMA_WAVES
+#define MUON_DMA_WAVES 8
+#endif
+
 template <int KIND, int EPI>
 static hipError_t launch_dma_one(const GemmParams& p, int nmat, hipStream_t s) {
   const uint64_t blocks = (uint64_t)nmat * p.tiles_per_prod * p.products;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   if (p.Kdim % DBK != 0 || p.Mdim % DT != 0 || p.Ndim % DT != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_dma_kernel<KIND, EPI>), dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  constexpr int NW = MUON_DMA_WAVES;
+  hipLaunchKernelGGL((gemm_dma_kernel<KIND, EPI, NW>), dim3((uint32_t)blocks), dim3(64 * NW), 0, s,
+                     p);
   return hipGetLastError();
 }
 
