@@ -72,9 +72,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   constexpr int NMF = FM * FN;                   // MFMAs per half stage
   static_assert(NMF == 2 * DPS, "two MFMAs per DMA instruction");
   constexpr int RR = 128;
-  constexpr int EPI_LD = DT + 1;
   constexpr int SMEM_OPS = DSTAGES * STAGEB;
-  constexpr int SMEM_EPI = RR * EPI_LD * 4;
+  constexpr int SMEM_EPI = RR * DT * 4;
   constexpr int SMEM_BYTES = SMEM_OPS > SMEM_EPI ? SMEM_OPS : SMEM_EPI;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   float* stile = reinterpret_cast<float*>(smem);
@@ -213,14 +212,19 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
   __syncthreads();
 
-  // Epilogue through LDS, 128 rows per round.  At the start of a round all
-  // of its global inputs (the fp16 identity-term operand, or W for the final
-  // product) are requested at once, so their latency overlaps the staging of
-  // the accumulators.  Row pass: each thread takes four consecutive columns
-  // (64 threads per tile row) and writes the primary value back to LDS;
-  // mirror pass (symmetric results, strictly-lower elements): four
-  // consecutive tile rows of one column become four consecutive elements of
-  // the mirrored row.
+  // Epilogue through LDS, 128 rows per round.  The fp32 tile is staged with
+  // its 16-byte column chunks XOR-swizzled by (row / 4) (see epi_off), which
+  // makes both passes below conflict free with 16-byte LDS accesses.  At the
+  // start of a round all of its global inputs (the fp16 identity-term
+  // operand, or W for the final product) are requested at once, so their
+  // latency overlaps the staging.  Row pass: each thread takes four
+  // consecutive columns (64 threads per tile row) and writes the primary
+  // value back; mirror pass (symmetric results, strictly-lower elements): a
+  // thread reads a 4 x 4 block, transposes it in registers and writes four
+  // consecutive elements into each of four mirrored rows.
+  auto epi_off = [](int il, int jc) {
+    return il * DT + ((((jc >> 2) ^ ((il >> 2) & 63)) << 2) | (jc & 3));
+  };
   const bool diag = p.triangular && ti == tj;
   const int jl = (tid & 63) * 4;
   const int gj = row0B + jl;
@@ -260,17 +264,16 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
           for (int v = 0; v < 16; ++v) {
             const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             const int jc = wn * WTN + j * 32 + l32;
-            stile[il * EPI_LD + jc] = acc[i][j][v];
+            stile[epi_off(il, jc)] = acc[i][j][v];
           }
     }
     __syncthreads();
+    if constexpr (EPI == EPI_FINAL) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int il = e * RPI + (tid >> 6);
-      float* sp = stile + il * EPI_LD + jl;
-      const float4 av = make_float4(sp[0], sp[1], sp[2], sp[3]);
-      const int gi = gr0 + il;
-      if constexpr (EPI == EPI_FINAL) {
+      for (int e = 0; e < PER; ++e) {
+        const int il = e * RPI + (tid >> 6);
+        const float4 av = *(const float4*)(stile + epi_off(il, jl));
+        const int gi = gr0 + il;
         if (wvec) {
           if (gi < p.out_rows) {
             const MatPtrs mp = p.table[mat];
@@ -283,39 +286,56 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
         } else {
           epilogue_final4(p, mat, gi, gj, av);
         }
-      } else if (!diag) {
-        const float4 pv =
-            epilogue_rr4_pre<EPI>(p, mat, prod, gi, gj, av, hin[EPI == EPI_SYRK ? 0 : e]);
-        sp[0] = pv.x;
-        sp[1] = pv.y;
-        sp[2] = pv.z;
-        sp[3] = pv.w;
-      } else {
-        // diagonal tile: element-wise lower-triangle mask
-        const float a4[4] = {av.x, av.y, av.z, av.w};
+      }
+    } else if (!diag) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int il = e * RPI + (tid >> 6);
+        float4* sp = (float4*)(stile + epi_off(il, jl));
+        *sp = epilogue_rr4_pre<EPI>(p, mat, prod, gr0 + il, gj, *sp, hin[EPI == EPI_SYRK ? 0 : e]);
+      }
+    } else {
+      // diagonal tile: element-wise lower-triangle mask
+#pragma unroll 1
+      for (int e = 0; e < PER; ++e) {
+        const int il = e * RPI + (tid >> 6);
+        float4* sp = (float4*)(stile + epi_off(il, jl));
+        const float4 av = *sp;
+        const int gi = gr0 + il;
+        float a4[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (gi >= gj + k) sp[k] = epilogue_rr1<EPI>(p, mat, prod, gi, gj + k, a4[k]);
+          if (gi >= gj + k) a4[k] = epilogue_rr1<EPI>(p, mat, prod, gi, gj + k, a4[k]);
+        *sp = make_float4(a4[0], a4[1], a4[2], a4[3]);
       }
     }
     if constexpr (EPI != EPI_FINAL) {
       __syncthreads();
       const int il0 = (tid & 31) * 4;
-      constexpr int CPI = NT / 32;  // mirror columns per iteration
-#pragma unroll 8
-      for (int e = 0; e < DT / CPI; ++e) {
-        const int jc = e * CPI + (tid >> 5);
-        const int gi0 = gr0 + il0, gjm = row0B + jc;
-        const float4 pv = make_float4(stile[il0 * EPI_LD + jc], stile[(il0 + 1) * EPI_LD + jc],
-                                      stile[(il0 + 2) * EPI_LD + jc], stile[(il0 + 3) * EPI_LD + jc]);
-        const size_t o = (size_t)mat * p.rr_stride + (size_t)gjm * p.ldr + gi0;
-        if (!diag) {
-          store_rr4<EPI>(p, o, prod, pv, pv);
-        } else {
-          const float a4[4] = {pv.x, pv.y, pv.z, pv.w};
+      constexpr int CG = NT / 32;  // 4-column groups per iteration
+#pragma unroll 1
+      for (int e = 0; e < DT / 4 / CG; ++e) {
+        const int jc0 = ((tid >> 5) + CG * e) * 4;
+        float4 r[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (gi0 + k > gjm) store_rr1<EPI>(p, o + k, prod, a4[k]);
+        for (int q = 0; q < 4; ++q) r[q] = *(const float4*)(stile + epi_off(il0 + q, jc0));
+        const float4 c[4] = {make_float4(r[0].x, r[1].x, r[2].x, r[3].x),
+                             make_float4(r[0].y, r[1].y, r[2].y, r[3].y),
+                             make_float4(r[0].z, r[1].z, r[2].z, r[3].z),
+                             make_float4(r[0].w, r[1].w, r[2].w, r[3].w)};
+        const int gi0 = gr0 + il0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int gjm = row0B + jc0 + k;
+          const size_t o = (size_t)mat * p.rr_stride + (size_t)gjm * p.ldr + gi0;
+          if (!diag) {
+            store_rr4<EPI>(p, o, prod, c[k], c[k]);
+          } else {
+            const float a4[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (gi0 + q > gjm) store_rr1<EPI>(p, o + q, prod, a4[q]);
+          }
         }
       }
     }
