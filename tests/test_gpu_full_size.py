@@ -1,0 +1,90 @@
+"""Parity at the benchmark's full sizes and launch configuration.
+
+The whole matrix set of a workload is planned and stepped at once (as
+bench.py does, inputs drawn on the device); a few sampled matrices get a
+direction output and their inputs and results are copied to the host and
+checked against the float64 oracle (Gram-form evaluation of the same map,
+pinned equal to the direct form)."""
+import numpy as np
+import pytest
+
+from matrix_aware_optimizer_muon_amd import workloads as WL
+from oracle import muon_oracle as OR
+from tests.gpu_common import rel
+
+pytestmark = pytest.mark.gpu
+
+
+def setup(w, dev, torch):
+    from matrix_aware_optimizer_muon_amd import Plan
+    W = [WL.device_weight(w, i, dev) for i in range(len(w.shapes))]
+    M = [torch.zeros_like(x) for x in W]
+    plan = Plan(w.shapes, w.grad_dtype, w.ns_dtype)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+    return W, M, plan, ws
+
+
+def host(t):
+    import torch
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def test_qwen_28_layers_sampled():
+    import torch
+    w = WL.config(4)
+    dev = torch.device("cuda:0")
+    W, M, plan, ws = setup(w, dev, torch)
+    G = [WL.device_grad(w, i, 0, dev) for i in range(len(w.shapes))]
+    sample = [0, 1, 4, 6, 195]  # layer 0: q, k, gate, down; layer 27: down
+    O = [torch.empty_like(W[i]) if i in sample else None for i in range(len(w.shapes))]
+    before = {i: (host(W[i]), host(M[i]), host(G[i])) for i in sample}
+    ptr = lambda L: [x.data_ptr() if x is not None else 0 for x in L]
+    plan.step_ptrs(ptr(W), ptr(M), ptr(G), w.lr, w.wd, ws.data_ptr(), ws.numel(),
+                   torch.cuda.current_stream().cuda_stream, ptr(O))
+    torch.cuda.synchronize()
+    for i in sample:
+        Wh, Mh, Gh = before[i]
+        m, n = w.shapes[i]
+        Wo, Mo, Oo = OR.muon_step(Wh, Mh, Gh, w.lr, w.wd, form="gram")
+        Og = host(O[i])
+        e = rel(Og, Oo)
+        print(f"qwen28 matrix {i} {m}x{n}: NS rel err {e:.3e}")
+        assert e <= 2e-2
+        assert rel(host(M[i]), Mo) <= 1e-6
+        assert rel(host(W[i]), OR.apply_update(Wh, Og, w.lr, w.wd, OR.update_scale(m, n))) <= 1e-5
+
+
+def test_dit_periodic_rownorm_sampled():
+    import torch
+    w = WL.config(5)
+    dev = torch.device("cuda:0")
+    W, M, plan, ws = setup(w, dev, torch)
+    sample = [0, 4, 5, 239]  # block 0: 4096^2, 16384x4096, 4096x16384; block 39: 4096x16384
+    O = [torch.empty_like(W[i]) if i in sample else None for i in range(len(w.shapes))]
+    ptr = lambda L: [x.data_ptr() if x is not None else 0 for x in L]
+    st = torch.cuda.current_stream().cuda_stream
+    G = [torch.empty_like(x) for x in W]
+    for t in range(2):  # refresh at t = 0, RowNorm at t = 1 (K = 5)
+        for i in range(len(w.shapes)):
+            WL.device_grad(w, i, t, dev, out=G[i])
+        before = {i: (host(W[i]), host(M[i]), host(G[i])) for i in sample}
+        fn = plan.step_ptrs if t % w.refresh_period == 0 else plan.rownorm_ptrs
+        fn(ptr(W), ptr(M), ptr(G), w.lr, w.wd, ws.data_ptr(), ws.numel(), st, ptr(O))
+        torch.cuda.synchronize()
+        for i in sample:
+            Wh, Mh, Gh = before[i]
+            m, n = w.shapes[i]
+            if t == 0:
+                Wo, Mo, Oo = OR.muon_step(Wh, Mh, Gh, w.lr, w.wd, form="gram")
+                e = rel(host(O[i]), Oo)
+                print(f"dit refresh matrix {i} {m}x{n}: NS rel err {e:.3e}")
+                assert e <= 2e-2
+                assert rel(host(W[i]), OR.apply_update(Wh, host(O[i]), w.lr, w.wd,
+                                                        OR.update_scale(m, n))) <= 1e-5
+            else:
+                Wo, Mo, Ro = OR.rownorm_step(Wh, Mh, Gh, w.lr, w.wd)
+                e = rel(host(O[i]), Ro)
+                print(f"dit rownorm matrix {i} {m}x{n}: rel err {e:.3e}")
+                assert e <= 1e-6
+                assert rel(host(W[i]), Wo) <= 1e-6
+            assert rel(host(M[i]), Mo) <= 1e-6
