@@ -189,6 +189,8 @@ def main():
             e["gbs"] = round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1)
         kernels[k] = e
     roofline = None
+    from matrix_aware_optimizer_muon_amd.profiling import read_traffic
+    traffic = read_traffic(w.name, ROOT)
     if ktimes:
         dom = max(ktimes, key=lambda k: ktimes[k]["ms"])
         v = ktimes[dom]
@@ -196,15 +198,19 @@ def main():
             peak = PEAK_MFMA_F32 if w.ns_dtype == "f32" else PEAK_MFMA_16BIT
             ach = v["flops"] / (v["ms"] * 1e-3) / 1e12
             roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                        "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                        "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                        "traffic": round(sum(traffic[dom]), 0) if dom in traffic else None,
                         "ms_per_launch": round(v["ms"] / v["launches"], 5),
-                        "share_of_step": round(v["ms"] / sum(x["ms"] for x in ktimes.values()), 3)}
+                        "share_of_step": round(v["ms"] / sum(x["ms"] for x in ktimes.values()), 3),
+                        "algorithmic_bytes_per_launch": round(v["bytes"] / v["launches"], 0)}
         else:
             ach = v["bytes"] / (v["ms"] * 1e-3) / 1e9
             roofline = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM,
-                        "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "traffic": None,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4),
+                        "traffic": round(sum(traffic[dom]), 0) if dom in traffic else None,
                         "ms_per_launch": round(v["ms"] / v["launches"], 5),
-                        "share_of_step": round(v["ms"] / sum(x["ms"] for x in ktimes.values()), 3)}
+                        "share_of_step": round(v["ms"] / sum(x["ms"] for x in ktimes.values()), 3),
+                        "algorithmic_bytes_per_launch": round(v["bytes"] / v["launches"], 0)}
 
     out = {
         "metric": METRIC,

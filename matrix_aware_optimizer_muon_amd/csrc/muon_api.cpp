@@ -484,7 +484,12 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       // lower triangle): SYRK r^2 c, each r x r product r^3, final 2 r^2 c
       const double r2 = (double)B.r * B.r, r3 = r2 * B.r, cc = (double)B.c;
       const double rcf = (double)B.r * B.c;
-      const double hes = f32path ? 4.0 : 2.0;
+      // algorithmic bytes per r x r element: operand reads (each operand read
+      // once), the identity-term input (lower triangle, read once) and the
+      // outputs (both triangles); the 256-tile path keeps only fp16 copies
+      const double op_b = f32path ? 4.0 : 2.0;
+      const double in_b = f32path ? 2.0 : (B.dma ? 1.0 : 2.0);
+      const double out_b = f32path ? 4.0 : (B.dma ? 2.0 : 6.0);
 
       PrepParams pp{};
       pp.table = d_table + ch.first;
@@ -554,7 +559,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       g.triangular = 1;
       g.tiles_per_prod = ntri;
       g.products = 1;
-      st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (xes * rcf + r2 * (4 + (f32path ? 0 : 2))) * nm,
+      st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (xes * rcf + r2 * out_b) * nm,
                  [&] { return gemm(g, EPI_SYRK); });
       if (st != MUON_OK) return st;
 
@@ -568,7 +573,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         g.Qh_src = Qh[src];
         // P~ = b G + c G^2 (and Q1 = a I + P~ on the first iteration)
         rr_setup(Gh, Gh, Gh, 1);
-        st = timed(p, stream, MUON_K_POLY, r3 * nm, r2 * (hes + 4 + hes) * nm,
+        st = timed(p, stream, MUON_K_POLY, r3 * nm, r2 * (op_b + in_b + out_b * (k == 0 ? 2 : 1)) * nm,
                    [&] { return gemm(g, EPI_POLY); });
         if (st != MUON_OK) return st;
         const bool need_q = k > 0;
@@ -586,7 +591,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
             g.prod_base = 1;
           }
           const int np = g.products;
-          st = timed(p, stream, MUON_K_PQPG, r3 * np * nm, r2 * (hes + np * (hes + 4 + 4 + hes)) * nm,
+          st = timed(p, stream, MUON_K_PQPG, r3 * np * nm, r2 * (op_b + np * (op_b + in_b + out_b)) * nm,
                      [&] { return gemm(g, EPI_PQPG); });
           g.prod_base = 0;
           if (st != MUON_OK) return st;
@@ -594,7 +599,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         if (need_h) {
           // G_k = a H + P~ H
           rr_setup(Ph, Hh, Hh, 1);
-          st = timed(p, stream, MUON_K_PH, r3 * nm, r2 * (hes + hes + 4 + 4 + hes) * nm,
+          st = timed(p, stream, MUON_K_PH, r3 * nm, r2 * (2 * op_b + in_b + out_b) * nm,
                      [&] { return gemm(g, EPI_PH); });
           if (st != MUON_OK) return st;
         }
@@ -633,7 +638,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       fg.tiles_m = fg.Mdim / B.bt;
       fg.tiles_n = fg.Ndim / B.bt;
       fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
-      st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + hes * r2 + 8.0 * rcf) * nm,
+      st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + op_b * r2 + 8.0 * rcf) * nm,
                  [&] { return gemm(fg, EPI_FINAL); });
       if (st != MUON_OK) return st;
     }

@@ -1,0 +1,145 @@
+"""Measurement support: turn rocprofv3 counter CSVs into the per-kernel-class
+HBM traffic table that bench.py reads, and fingerprint the kernel sources so
+a stale table is not used after the kernels change.
+
+Usage (host side, after the counter runs):
+  python -m matrix_aware_optimizer_muon_amd.profiling traffic \
+      --fetch F.csv --write W.csv --copy-fetch CF.csv --copy-write CW.csv \
+      --copy-bytes N --workload NAME --command "..." > profiles/hbm_traffic_NAME.md
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/gemm_epilogue.hpp",
+                  "csrc/elementwise.hip", "csrc/common.hpp", "csrc/kernels.h")
+EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final"}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_class(name: str) -> str | None:
+    """Map a demangled kernel name to the launch-profiler class."""
+    m = re.search(r"gemm_dma_kernel<(\d+), (\d+)", name) or re.search(
+        r"gemm_kernel<(\d+), \d+, (\d+)", name)
+    if m:
+        return EPI_CLASS[int(m.group(2))]
+    for key, cls in (("prep_tile_kernel", "prep"), ("norm_finalize", "norm"),
+                     ("rownorm_rows", "rownorm"), ("rownorm_colsum", "colsum"),
+                     ("rownorm_colfinal", "colfinal"), ("rownorm_colapply", "colapply")):
+        if key in name:
+            return cls
+    return None
+
+
+def _read(path: str, counter: str):
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def traffic_table(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_bytes):
+    """Per class: (launches, fetch bytes per launch, write bytes per launch),
+    with FETCH_SIZE / WRITE_SIZE (KiB) scaled so that a plain copy of
+    `copy_bytes` reads and writes exactly `copy_bytes`."""
+    def copy_scale(path, counter):
+        per = _read(path, counter)
+        vals = [v for k, vs in per.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs]
+        if not vals:
+            raise SystemExit(f"no copy kernel in {path}")
+        return copy_bytes / (max(vals) * 1024.0)
+    sf = copy_scale(copy_fetch_csv, "FETCH_SIZE")
+    sw = copy_scale(copy_write_csv, "WRITE_SIZE")
+    out = {}
+    for counter, path, scale, idx in (("FETCH_SIZE", fetch_csv, sf, 1), ("WRITE_SIZE", write_csv, sw, 2)):
+        for k, vs in _read(path, counter).items():
+            cls = kernel_class(k)
+            if cls is None:
+                continue
+            e = out.setdefault(cls, [0, 0.0, 0.0])
+            if idx == 1:
+                e[0] += len(vs)
+            e[idx] += sum(vs) * 1024.0 * scale
+    return {c: (n, f / n, w / n) for c, (n, f, w) in out.items() if n}, sf, sw
+
+
+def read_traffic(workload: str, root: str):
+    """(fetch_bytes_per_launch, write_bytes_per_launch) per class from the
+    committed table, or {} if absent or taken from other kernel sources."""
+    path = os.path.join(root, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read()
+    m = re.search(r"kernel source hash: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != source_hash():
+        return {}
+    out = {}
+    for line in text.splitlines():
+        mm = re.match(r"\|\s*(\w+)\s*\|\s*(\d+)\s*\|\s*([\d.e+-]+)\s*\|\s*([\d.e+-]+)\s*\|", line)
+        if mm:
+            out[mm.group(1)] = (float(mm.group(3)) * 1e9, float(mm.group(4)) * 1e9)
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--workload", "--command"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    sub.add_parser("hash")
+    k = sub.add_parser("trace")
+    k.add_argument("--stats", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "hash":
+        print(source_hash())
+        return
+    if a.cmd == "trace":
+        rows = list(csv.DictReader(open(a.stats)))
+        print(f"# Kernel trace: {a.title}\n")
+        print("Command (GPU box, repo root):\n")
+        print(f"```\n{a.command}\n```\n")
+        print(f"kernel source hash: `{source_hash()}`\n")
+        print("| kernel | class | calls | total ms | avg ms | % |")
+        print("|---|---|---:|---:|---:|---:|")
+        for r in rows:
+            name = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
+            if len(name) > 70:
+                name = name[:67] + "..."
+            cls = kernel_class(r["Name"]) or "-"
+            print(f"| `{name}` | {cls} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                  f"{float(r['AverageNs']) / 1e6:.4f} | {float(r['Percentage']):.2f} |")
+        return
+    table, sf, sw = traffic_table(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
+    print(f"# HBM traffic per launch: {a.workload}\n")
+    print("Counter runs (GPU box, repo root), one refresh step each:\n")
+    print(f"```\n{a.command}\n```\n")
+    print(f"Scale factors from a plain device copy of {a.copy_bytes} bytes: "
+          f"FETCH_SIZE x {sf:.3f}, WRITE_SIZE x {sw:.3f}.\n")
+    print(f"kernel source hash: `{source_hash()}`\n")
+    print("| class | launches | fetch GB/launch | write GB/launch |")
+    print("|---|---:|---:|---:|")
+    for c, (n, f, w) in sorted(table.items()):
+        print(f"| {c} | {n} | {f / 1e9:.4f} | {w / 1e9:.4f} |")
+
+
+if __name__ == "__main__":
+    main()
