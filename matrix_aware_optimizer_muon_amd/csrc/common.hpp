@@ -58,6 +58,18 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
   return x * q + (x < rem ? x : rem) + slot;
 }
 
+// Streaming (non-temporal) 16-byte global access for data touched once per
+// step (M, G, W, the X0 copies): keeps it from displacing reusable lines.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 nt_load4(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void nt_store4(float* p, float4 v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, (f32x4*)p);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);

@@ -53,7 +53,7 @@ __device__ __forceinline__ float4 load_g4(const void* G, size_t idx, bool vec, i
 }
 
 __device__ __forceinline__ float4 load_f4(const float* p, bool vec, int valid) {
-  if (vec) return *(const float4*)p;
+  if (vec) return nt_load4(p);
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   if (valid > 0) v.x = p[0];
   if (valid > 1) v.y = p[1];
@@ -64,7 +64,7 @@ __device__ __forceinline__ float4 load_f4(const float* p, bool vec, int valid) {
 
 __device__ __forceinline__ void store_f4(float* p, float4 v, bool vec, int valid) {
   if (vec) {
-    *(float4*)p = v;
+    nt_store4(p, v);
     return;
   }
   if (valid > 0) p[0] = v.x;
@@ -143,12 +143,12 @@ __global__ void __launch_bounds__(256) prep_tile_kernel(const PrepParams p, int 
       }
       const size_t xo = xbase + (size_t)i * p.n_pad + j;
       if (XF32) {
-        *(float4*)((float*)p.X + xo) = u;
+        nt_store4((float*)p.X + xo, u);
       } else {
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_bits(u.x) | ((uint32_t)f32_to_bf16_bits(u.y) << 16);
-        pk.y = (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16);
-        *(uint2*)((uint16_t*)p.X + xo) = pk;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 pk = {(uint32_t)f32_to_bf16_bits(u.x) | ((uint32_t)f32_to_bf16_bits(u.y) << 16),
+                          (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16)};
+        __builtin_nontemporal_store(pk, (u32x2*)((uint16_t*)p.X + xo));
       }
       tile[rl][c4 + 0] = u.x;
       tile[rl][c4 + 1] = u.y;
@@ -165,17 +165,17 @@ __global__ void __launch_bounds__(256) prep_tile_kernel(const PrepParams p, int 
       float* xp = (float*)p.XT + xo;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *(float4*)(xp + 4 * q) = make_float4(tile[i0 + 4 * q][jl], tile[i0 + 4 * q + 1][jl],
-                                             tile[i0 + 4 * q + 2][jl], tile[i0 + 4 * q + 3][jl]);
+        nt_store4(xp + 4 * q, make_float4(tile[i0 + 4 * q][jl], tile[i0 + 4 * q + 1][jl],
+                                          tile[i0 + 4 * q + 2][jl], tile[i0 + 4 * q + 3][jl]));
     } else {
       uint32_t w[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
         w[q] = (uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q][jl]) |
                ((uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q + 1][jl]) << 16);
-      uint4* xp = (uint4*)((uint16_t*)p.XT + xo);
-      xp[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      xp[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      u32x4* xp = (u32x4*)((uint16_t*)p.XT + xo);
+      __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, xp);
+      __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, xp + 1);
     }
   }
   const float tot = block_sum<256>(ss, red);
@@ -222,40 +222,77 @@ hipError_t launch_norm_finalize(const PrepParams& p, int nmat, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// RowNorm, m <= n: one workgroup per row; U cached in registers (CH float4
-// chunks per thread), or re-read from M' and G when CH == 0 (very wide rows).
-template <bool GBF16, int CH>
-__global__ void __launch_bounds__(256) rownorm_rows_kernel(const RowNormParams p, int vec) {
-  __shared__ float red[4];
+// RowNorm, m <= n: one workgroup of NT threads per row.  Every load of the
+// row (M, G and W) is issued before the row reduction, so its latency is not
+// paid twice; U stays in registers (CH float4 chunks per thread).  Rows wider
+// than NT*CH*4 take the generic path that re-reads M' and G (CH == 0).
+template <int BS>
+__device__ __forceinline__ float block_sum_n(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < BS / 64; ++w) s += red[w];
+  return s;
+}
+
+template <bool GBF16, int CH, int NT>
+__global__ void __launch_bounds__(NT) rownorm_rows_kernel(const RowNormParams p, int vec) {
+  __shared__ float red[NT / 64];
   const int mat = blockIdx.x / p.m;
   const int row = blockIdx.x - mat * p.m;
   const MatPtrs mp = p.table[mat];
   const size_t base = (size_t)row * p.n;
   const int nc = (p.n + 3) / 4;
   float ss = 0.f;
-  float4 ucache[CH > 0 ? CH : 1];
-#pragma unroll
-  for (int k = 0; k < (CH > 0 ? CH : 1); ++k) ucache[k] = make_float4(0.f, 0.f, 0.f, 0.f);
   if constexpr (CH > 0) {
+    float4 mm[CH], gg[CH], ww[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-      const int c = threadIdx.x + 256 * k;
+      const int c = threadIdx.x + NT * k;
       if (c < nc) {
         const int col = c * 4, valid = p.n - col;
         const bool v4 = vec && valid >= 4;
-        const float4 m = load_f4(mp.M + base + col, v4, valid);
-        const float4 g = load_g4<GBF16>(mp.G, base + col, v4, valid);
+        mm[k] = load_f4(mp.M + base + col, v4, valid);
+        gg[k] = load_g4<GBF16>(mp.G, base + col, v4, valid);
+        ww[k] = load_f4(mp.W + base + col, v4, valid);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = threadIdx.x + NT * k;
+      if (c < nc) {
+        const int col = c * 4, valid = p.n - col;
+        const bool v4 = vec && valid >= 4;
         float4 mn;
-        const float4 u = momentum4(m, g, p.mu, p.nesterov, &mn);
+        mm[k] = momentum4(mm[k], gg[k], p.mu, p.nesterov, &mn);  // mm now holds U
         store_f4(mp.M + base + col, mn, v4, valid);
-        ucache[k] = u;
-        ss += u.x * u.x + u.y * u.y;
-        if (valid > 2) ss += u.z * u.z;
-        if (valid > 3) ss += u.w * u.w;
+        ss += mm[k].x * mm[k].x + mm[k].y * mm[k].y + mm[k].z * mm[k].z + mm[k].w * mm[k].w;
+      }
+    }
+    const float inv = 1.0f / fmaxf(sqrtf(block_sum_n<NT>(ss, red)), p.eps);
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int c = threadIdx.x + NT * k;
+      if (c < nc) {
+        const int col = c * 4, valid = p.n - col;
+        const bool v4 = vec && valid >= 4;
+        const float4 u = mm[k];
+        const float4 r = make_float4(u.x * inv, u.y * inv, u.z * inv, u.w * inv);
+        float4 w = ww[k];
+        w.x = p.decay * w.x - p.step * r.x;
+        w.y = p.decay * w.y - p.step * r.y;
+        w.z = p.decay * w.z - p.step * r.z;
+        w.w = p.decay * w.w - p.step * r.w;
+        store_f4(mp.W + base + col, w, v4, valid);
+        if (mp.O) store_f4(mp.O + base + col, r, v4, valid);
       }
     }
   } else {
-    for (int c = threadIdx.x; c < nc; c += 256) {
+    for (int c = threadIdx.x; c < nc; c += NT) {
       const int col = c * 4, valid = p.n - col;
       const bool v4 = vec && valid >= 4;
       const float4 m = load_f4(mp.M + base + col, v4, valid);
@@ -263,34 +300,11 @@ __global__ void __launch_bounds__(256) rownorm_rows_kernel(const RowNormParams p
       float4 mn;
       const float4 u = momentum4(m, g, p.mu, p.nesterov, &mn);
       store_f4(mp.M + base + col, mn, v4, valid);
-      ss += u.x * u.x + u.y * u.y;
-      if (valid > 2) ss += u.z * u.z;
-      if (valid > 3) ss += u.w * u.w;
+      ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
     }
-  }
-  const float tot = block_sum<256>(ss, red);
-  const float inv = 1.0f / fmaxf(sqrtf(tot), p.eps);
-  auto apply = [&](int col, float4 u) {
-    const int valid = p.n - col;
-    const bool v4 = vec && valid >= 4;
-    const float4 r = make_float4(u.x * inv, u.y * inv, u.z * inv, u.w * inv);
-    float4 w = load_f4(mp.W + base + col, v4, valid);
-    w.x = p.decay * w.x - p.step * r.x;
-    w.y = p.decay * w.y - p.step * r.y;
-    w.z = p.decay * w.z - p.step * r.z;
-    w.w = p.decay * w.w - p.step * r.w;
-    store_f4(mp.W + base + col, w, v4, valid);
-    if (mp.O) store_f4(mp.O + base + col, r, v4, valid);
-  };
-  if constexpr (CH > 0) {
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int c = threadIdx.x + 256 * k;
-      if (c < nc) apply(c * 4, ucache[k]);
-    }
-  } else {
-    __syncthreads();  // M' of this row is visible to the re-read below
-    for (int c = threadIdx.x; c < nc; c += 256) {
+    const float inv = 1.0f / fmaxf(sqrtf(block_sum_n<NT>(ss, red)), p.eps);
+    // each thread re-reads exactly the chunks it wrote above
+    for (int c = threadIdx.x; c < nc; c += NT) {
       const int col = c * 4, valid = p.n - col;
       const bool v4 = vec && valid >= 4;
       const float4 mn = load_f4(mp.M + base + col, v4, valid);
@@ -298,7 +312,14 @@ __global__ void __launch_bounds__(256) rownorm_rows_kernel(const RowNormParams p
       const float4 u = p.nesterov ? make_float4(p.mu * mn.x + g.x, p.mu * mn.y + g.y,
                                                 p.mu * mn.z + g.z, p.mu * mn.w + g.w)
                                   : mn;
-      apply(col, u);
+      const float4 r = make_float4(u.x * inv, u.y * inv, u.z * inv, u.w * inv);
+      float4 w = load_f4(mp.W + base + col, v4, valid);
+      w.x = p.decay * w.x - p.step * r.x;
+      w.y = p.decay * w.y - p.step * r.y;
+      w.z = p.decay * w.z - p.step * r.z;
+      w.w = p.decay * w.w - p.step * r.w;
+      store_f4(mp.W + base + col, w, v4, valid);
+      if (mp.O) store_f4(mp.O + base + col, r, v4, valid);
     }
   }
 }
@@ -321,7 +342,28 @@ __global__ void __launch_bounds__(256) rownorm_colsum_kernel(const RowNormParams
   const bool v4 = vec && valid >= 4;
   float4 ss = make_float4(0.f, 0.f, 0.f, 0.f);
   const int r0 = rb * RN_ROWS, r1 = min(p.m, r0 + RN_ROWS);
-  for (int row = r0; row < r1; ++row) {
+  constexpr int UR = 4;  // rows per iteration (loads in flight)
+  int row = r0;
+  for (; row + UR <= r1; row += UR) {
+    float4 m[UR], g[UR];
+#pragma unroll
+    for (int q = 0; q < UR; ++q) {
+      const size_t idx = (size_t)(row + q) * p.n + col;
+      m[q] = load_f4(mp.M + idx, v4, valid);
+      g[q] = load_g4<GBF16>(mp.G, idx, v4, valid);
+    }
+#pragma unroll
+    for (int q = 0; q < UR; ++q) {
+      float4 mn;
+      const float4 u = momentum4(m[q], g[q], p.mu, p.nesterov, &mn);
+      store_f4(mp.M + (size_t)(row + q) * p.n + col, mn, v4, valid);
+      ss.x += u.x * u.x;
+      ss.y += u.y * u.y;
+      ss.z += u.z * u.z;
+      ss.w += u.w * u.w;
+    }
+  }
+  for (; row < r1; ++row) {
     const size_t idx = (size_t)row * p.n + col;
     const float4 m = load_f4(mp.M + idx, v4, valid);
     const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
@@ -363,21 +405,36 @@ __global__ void __launch_bounds__(256) rownorm_colapply_kernel(const RowNormPara
   const bool v4 = vec && valid >= 4;
   const float4 sc = load_f4(p.colscale + (size_t)mat * p.n + col, v4, valid);
   const int r0 = rb * RN_ROWS, r1 = min(p.m, r0 + RN_ROWS);
-  for (int row = r0; row < r1; ++row) {
-    const size_t idx = (size_t)row * p.n + col;
-    const float4 mn = load_f4(mp.M + idx, v4, valid);
-    const float4 g = load_g4<GBF16>(mp.G, idx, v4, valid);
+  auto apply = [&](size_t idx, float4 mn, float4 g, float4 w) {
     const float4 u = p.nesterov ? make_float4(p.mu * mn.x + g.x, p.mu * mn.y + g.y,
                                               p.mu * mn.z + g.z, p.mu * mn.w + g.w)
                                 : mn;
     const float4 r = make_float4(u.x * sc.x, u.y * sc.y, u.z * sc.z, u.w * sc.w);
-    float4 w = load_f4(mp.W + idx, v4, valid);
     w.x = p.decay * w.x - p.step * r.x;
     w.y = p.decay * w.y - p.step * r.y;
     w.z = p.decay * w.z - p.step * r.z;
     w.w = p.decay * w.w - p.step * r.w;
     store_f4(mp.W + idx, w, v4, valid);
     if (mp.O) store_f4(mp.O + idx, r, v4, valid);
+  };
+  constexpr int UR = 4;  // rows per iteration (loads in flight)
+  int row = r0;
+  for (; row + UR <= r1; row += UR) {
+    float4 mn[UR], g[UR], w[UR];
+#pragma unroll
+    for (int q = 0; q < UR; ++q) {
+      const size_t idx = (size_t)(row + q) * p.n + col;
+      mn[q] = load_f4(mp.M + idx, v4, valid);
+      g[q] = load_g4<GBF16>(mp.G, idx, v4, valid);
+      w[q] = load_f4(mp.W + idx, v4, valid);
+    }
+#pragma unroll
+    for (int q = 0; q < UR; ++q) apply((size_t)(row + q) * p.n + col, mn[q], g[q], w[q]);
+  }
+  for (; row < r1; ++row) {
+    const size_t idx = (size_t)row * p.n + col;
+    apply(idx, load_f4(mp.M + idx, v4, valid), load_g4<GBF16>(mp.G, idx, v4, valid),
+          load_f4(mp.W + idx, v4, valid));
   }
 }
 
@@ -395,12 +452,13 @@ hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int v
     if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
     const int nc = (p.n + 3) / 4;
     const dim3 g((uint32_t)blocks);
-#define RN_ROWS_LAUNCH(GB)                                                                    \
-  do {                                                                                        \
-    if (nc <= 256) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 1>), g, b, 0, s, p, vec);      \
-    else if (nc <= 1024) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 4>), g, b, 0, s, p, vec); \
-    else if (nc <= 4096) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 16>), g, b, 0, s, p, vec); \
-    else hipLaunchKernelGGL((rownorm_rows_kernel<GB, 0>), g, b, 0, s, p, vec);                \
+#define RN_ROWS_LAUNCH(GB)                                                                      \
+  do {                                                                                          \
+    if (nc <= 256) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 1, 256>), g, dim3(256), 0, s, p, vec);  \
+    else if (nc <= 1024) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 4, 256>), g, dim3(256), 0, s, p, vec); \
+    else if (nc <= 2048) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 4, 512>), g, dim3(512), 0, s, p, vec); \
+    else if (nc <= 4096) hipLaunchKernelGGL((rownorm_rows_kernel<GB, 4, 1024>), g, dim3(1024), 0, s, p, vec); \
+    else hipLaunchKernelGGL((rownorm_rows_kernel<GB, 0, 1024>), g, dim3(1024), 0, s, p, vec);  \
   } while (0)
     if (grad_bf16) RN_ROWS_LAUNCH(true); else RN_ROWS_LAUNCH(false);
 #undef RN_ROWS_LAUNCH

@@ -242,7 +242,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const int gi = gr0 + e * RPI + (tid >> 6);
-        win[e] = (wvec && gi < p.out_rows) ? *(const float4*)(mp.W + (size_t)gi * p.out_cols + gj)
+        win[e] = (wvec && gi < p.out_rows) ? nt_load4(mp.W + (size_t)gi * p.out_cols + gj)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     } else if constexpr (EPI != EPI_SYRK) {
@@ -280,8 +280,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
             const float inv = p.inv_norm[mat];
             const float4 o = make_float4(av.x * inv, av.y * inv, av.z * inv, av.w * inv);
             const size_t idx = (size_t)gi * p.out_cols + gj;
-            *(float4*)(mp.W + idx) = f4_axpy(p.decay, win[e], -p.step, o);
-            if (mp.O) *(float4*)(mp.O + idx) = o;
+            nt_store4(mp.W + idx, f4_axpy(p.decay, win[e], -p.step, o));
+            if (mp.O) nt_store4(mp.O + idx, o);
           }
         } else {
           epilogue_final4(p, mat, gi, gj, av);
