@@ -46,6 +46,48 @@ __device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) 
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Tile traversal orders.  Consecutive tile ids run concurrently on one XCD
+// (after xcd_remap), so the order decides how many operand panels the ~32
+// tiles in flight there share through its L2.
+//
+// Full grid: groups of GH tile rows, column by column inside a group, so 32
+// consecutive tiles cover 8 rows x 4 columns (12 operand panels) instead of
+// one row x 32 columns (33 panels) as in row-major order.
+__device__ __forceinline__ void full_tile_grouped(int t, int tiles_m, int tiles_n, int* ti, int* tj) {
+  constexpr int GH = 8;
+  const int g = t / (GH * tiles_n);
+  const int u = t - g * GH * tiles_n;
+  const int h = min(GH, tiles_m - g * GH);
+  *ti = g * GH + u % h;
+  *tj = u / h;
+}
+
+// Lower-triangular grid (T x T tiles, I >= J): super-rows of SH tile rows,
+// walked column by column; the diagonal block of a super-row comes last.
+__device__ __forceinline__ void tri_tile_grouped(int t, int T, int* ti, int* tj) {
+  constexpr int SH = 4;
+  // tiles before super-row s: (SH s)(SH s + 1)/2
+  int s = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f) / SH;
+  while (s > 0 && (SH * s) * (SH * s + 1) / 2 > t) --s;
+  while ((SH * (s + 1)) * (SH * (s + 1) + 1) / 2 <= t && SH * (s + 1) < T) ++s;
+  int u = t - (SH * s) * (SH * s + 1) / 2;
+  const int h = min(SH, T - SH * s);
+  const int r0 = SH * s;
+  if (u < h * r0) {
+    *tj = u / h;
+    *ti = r0 + u % h;
+    return;
+  }
+  u -= h * r0;
+  int d = 0;
+  while (u >= h - d) {
+    u -= h - d;
+    ++d;
+  }
+  *tj = r0 + d;
+  *ti = r0 + d + u;
+}
+
 template <int KIND>
 __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) {
   if constexpr (KIND == 0) {
@@ -91,15 +133,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   t -= pi * p.tiles_per_prod;
   const int prod = pi + p.prod_base;
   int ti, tj;
-  if (p.triangular) {
-    ti = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    while (ti * (ti + 1) / 2 > t) --ti;
-    tj = t - ti * (ti + 1) / 2;
-  } else {
-    ti = t / p.tiles_n;
-    tj = t - ti * p.tiles_n;
-  }
+  if (p.triangular) tri_tile_grouped(t, p.tiles_m, &ti, &tj);
+  else full_tile_grouped(t, p.tiles_m, p.tiles_n, &ti, &tj);
   const int row0A = ti * DT, row0B = tj * DT;
   const char* Ab = (const char*)p.A + (size_t)mat * p.a_stride * 2;
   const char* Bb = pi ? (const char*)p.B2 + (size_t)mat * p.b2_stride * 2
