@@ -127,6 +127,20 @@ def main(argv=None):
             cls = kernel_class(r["Name"]) or "-"
             print(f"| `{name}` | {cls} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
                   f"{float(r['AverageNs']) / 1e6:.4f} | {float(r['Percentage']):.2f} |")
+        per = collections.OrderedDict()
+        for r in rows:
+            cls = kernel_class(r["Name"])
+            if cls is None:
+                continue
+            e = per.setdefault(cls, [0, 0.0])
+            e[0] += int(r["Calls"])
+            e[1] += float(r["TotalDurationNs"])
+        print("\nPer launch-profiler class (every launch of the class, all shapes; the "
+              "figure bench.py's roofline ms_per_launch is compared with):\n")
+        print("| class | launches | total ms | avg ms per launch |")
+        print("|---|---:|---:|---:|")
+        for cls, (n, ns) in sorted(per.items(), key=lambda kv: -kv[1][1]):
+            print(f"| {cls} | {n} | {ns / 1e6:.3f} | {ns / n / 1e6:.4f} |")
         return
     table, sf, sw = traffic_table(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
     print(f"# HBM traffic per launch: {a.workload}\n")
