@@ -191,6 +191,17 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 
   u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
+  // Identity-term harvest (POLY, PQPG, PH).  The term X(m, n) that the
+  // epilogue adds is symmetric, and X(n, m) is this tile's own B operand at
+  // K = m: stages hk0 .. hk0+3 hold the wave's 128 rows m, stage hk0 + i
+  // the 32 rows of MFMA block row i.  While such a stage is resident each
+  // lane reads its 4 x FN x 4 values (8 bytes per 4 consecutive m) and adds
+  // gamma * X to the accumulators, so the epilogue reads no r x r input.
+  constexpr bool HARVEST = EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH;
+  float gam = 0.0f;
+  if constexpr (HARVEST) gam = rr_gamma<EPI>(p);
+  const int hk0 = row0A / DBK + wm * 4;
+
   // prologue: stages 0..3 in flight, wait for stage 0
 #pragma unroll
   for (int st = 0; st < DSTAGES; ++st)
@@ -215,6 +226,17 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     for (int f = 0; f < FM; ++f) fa1[f] = *(const u32x4*)(sb + offA[1][f]);
 #pragma unroll
     for (int f = 0; f < FN; ++f) fb1[f] = *(const u32x4*)(sb + offB[1][f]);
+    const int hs = kt - hk0;
+    uint2 hv[FN][4];
+    if (HARVEST && (unsigned)hs < 4u) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int rb = wn * WTN + j * 32 + l32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          hv[j][g] = *(const uint2*)(sb + OPB + rb * ROWB + ((g ^ swz4(rb)) << 4) + 8 * h);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 1; i < FM; ++i)
@@ -224,6 +246,20 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     // stage kt+1 landed for this wave (stages kt+2, kt+3 may still fly) and
     // this wave's reads of stage kt are done; then publish / retire
     __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 0));
+    if (HARVEST && (unsigned)hs < 4u) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (i != hs) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const _Float16* x = (const _Float16*)&hv[j][g];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += gam * (float)x[e];
+          }
+      }
+    }
     barrier();
     {  // next stage's first half (unused after the last step; in LDS bounds)
       const char* sn = smem + ((kt + 1) & (DSTAGES - 1)) * STAGEB;
@@ -249,10 +285,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 
   // Epilogue through LDS, 128 rows per round.  The fp32 tile is staged with
   // its 16-byte column chunks XOR-swizzled by (row / 4) (see epi_off), which
-  // makes both passes below conflict free with 16-byte LDS accesses.  At the
-  // start of a round all of its global inputs (the fp16 identity-term
-  // operand, or W for the final product) are requested at once, so their
-  // latency overlaps the staging.  Row pass: each thread takes four
+  // makes both passes below conflict free with 16-byte LDS accesses.  The
+  // r x r products read no global input here (their identity term is already
+  // in the accumulators); the final product requests all of a round's W rows
+  // at once, so their latency overlaps the staging.  Row pass: each thread takes four
   // consecutive columns (64 threads per tile row) and writes the primary
   // value back; mirror pass (symmetric results, strictly-lower elements): a
   // thread reads a 4 x 4 block, transposes it in registers and writes four
@@ -261,6 +297,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     return il * DT + ((((jc >> 2) ^ ((il >> 2) & 63)) << 2) | (jc & 3));
   };
   const bool diag = p.triangular && ti == tj;
+  float beta = 0.0f;
+  if constexpr (EPI != EPI_FINAL) beta = rr_beta<EPI>(p, mat, prod);
   const int jl = (tid & 63) * 4;
   const int gj = row0B + jl;
   constexpr int RPI = NT / 64;   // tile rows per row-pass iteration
@@ -268,7 +306,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int gr0 = row0A + round * RR;
-    uint2 hin[EPI == EPI_FINAL || EPI == EPI_SYRK ? 1 : PER];
     float4 win[EPI == EPI_FINAL ? PER : 1];
     bool wvec = false;
     if constexpr (EPI == EPI_FINAL) {
@@ -279,15 +316,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
         const int gi = gr0 + e * RPI + (tid >> 6);
         win[e] = (wvec && gi < p.out_rows) ? nt_load4(mp.W + (size_t)gi * p.out_cols + gj)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    } else if constexpr (EPI != EPI_SYRK) {
-      if (!diag) {
-        float inv_scale;
-        const uint16_t* src = (const uint16_t*)rr_input<EPI>(p, prod, &inv_scale);
-        const size_t base = (size_t)mat * p.rr_stride + gj;
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          hin[e] = *(const uint2*)(src + base + (size_t)(gr0 + e * RPI + (tid >> 6)) * p.ldr);
       }
     }
     if (wm == round) {
@@ -327,7 +355,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       for (int e = 0; e < PER; ++e) {
         const int il = e * RPI + (tid >> 6);
         float4* sp = (float4*)(stile + epi_off(il, jl));
-        *sp = epilogue_rr4_pre<EPI>(p, mat, prod, gr0 + il, gj, *sp, hin[EPI == EPI_SYRK ? 0 : e]);
+        *sp = epilogue_rr4_acc<EPI>(p, mat, prod, gr0 + il, gj, beta, *sp);
       }
     } else {
       // diagonal tile: element-wise lower-triangle mask
@@ -340,7 +368,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
         float a4[4] = {av.x, av.y, av.z, av.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (gi >= gj + k) a4[k] = epilogue_rr1<EPI>(p, mat, prod, gi, gj + k, a4[k]);
+          if (gi >= gj + k) a4[k] = epilogue_rr1_acc<EPI>(p, mat, prod, gi, gj + k, beta, a4[k]);
         *sp = make_float4(a4[0], a4[1], a4[2], a4[3]);
       }
     }

@@ -77,18 +77,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int mat, int prod,
 }
 
 // ---------------------------------------------------------------------------
-// fp16-only epilogues of the 256-tile path: the r x r inputs of the identity
-// terms are read from the fp16 operand copies (no fp32 master copies), four
-// consecutive elements per call.  `prim` receives the value the mirrored
-// stores are derived from.
-
-__device__ __forceinline__ float4 ld_h4(const void* base, size_t o, float inv_scale) {
-  const uint2 u = *(const uint2*)((const uint16_t*)base + o);
-  const _Float16* h = (const _Float16*)&u;
-  return make_float4((float)h[0] * inv_scale, (float)h[1] * inv_scale, (float)h[2] * inv_scale,
-                     (float)h[3] * inv_scale);
-}
-
+// fp16-only epilogues of the 256-tile path (no fp32 master copies of the
+// r x r results), four consecutive elements per call.
 __device__ __forceinline__ void st_h4(void* base, size_t o, float4 v, float scale) {
   uint2 u;
   u.x = (uint32_t)f32_to_f16_bits(v.x * scale) | ((uint32_t)f32_to_f16_bits(v.y * scale) << 16);
@@ -108,7 +98,7 @@ __device__ __forceinline__ float4 f4_axpy(float a, float4 x, float b, float4 y) 
 }
 
 // Store the outputs that derive from `v` at (gi, gj..gj+3) of an r x r
-// result; `diag` adds a*I to the Q output of the first iteration.
+// result; `q` is the Q output of POLY on the first iteration (a I + P~).
 template <int EPI>
 __device__ __forceinline__ void store_rr4(const GemmParams& p, size_t o, int prod, float4 v,
                                           float4 q) {
@@ -130,11 +120,34 @@ __device__ __forceinline__ void store_rr4(const GemmParams& p, size_t o, int pro
   }
 }
 
-// Scalar forms for the diagonal tiles (lower-triangle masking per element).
-__device__ __forceinline__ float ld_h1(const void* base, size_t o, float inv_scale) {
-  return (float)__builtin_bit_cast(_Float16, ((const uint16_t*)base)[o]) * inv_scale;
+// The 256-tile kernels fold the identity term of each r x r product into
+// the accumulators while the product runs (acc += gamma * X, X the raw fp16
+// identity-term operand), so the epilogue only scales: v = beta * acc.
+//   SYRK  G0 = X0 X0^T / ||U||^2                 beta = 1/||U||^2
+//   POLY  P~ = b G + c G^2,  acc = sG^2 G^2       beta = c/sG^2,       gamma = b sG / c
+//   PQPG  H  = a G + P~ G,   acc = sP sG P~ G     beta = 1/(sP sG),    gamma = a sP
+//         Q' = a Q + P~ Q,   acc = sP sQ P~ Q     beta = 1/(sP sQ),    gamma = a sP
+//   PH    G' = a H + P~ H,   acc = sP sH P~ H     beta = 1/(sP sH),    gamma = a sP
+template <int EPI>
+__device__ __forceinline__ float rr_beta(const GemmParams& p, int mat, int prod) {
+  if constexpr (EPI == EPI_SYRK) {
+    const float inv = p.inv_norm[mat];
+    return inv * inv;
+  } else if constexpr (EPI == EPI_POLY) {
+    return p.c * (1.0f / (p.sG * p.sG));
+  } else if constexpr (EPI == EPI_PQPG) {
+    return prod == 1 ? 1.0f / (p.sP * p.sG) : 1.0f / (p.sP * p.sQ);
+  } else {
+    return 1.0f / (p.sP * p.sH);
+  }
+}
+template <int EPI>
+__device__ __forceinline__ float rr_gamma(const GemmParams& p) {
+  if constexpr (EPI == EPI_POLY) return p.b * p.sG / p.c;
+  else return p.a * p.sP;
 }
 
+// Scalar store for the diagonal tiles (lower-triangle masking per element).
 template <int EPI>
 __device__ __forceinline__ void store_rr1(const GemmParams& p, size_t o, int prod, float v,
                                           float q) {
@@ -149,119 +162,33 @@ __device__ __forceinline__ void store_rr1(const GemmParams& p, size_t o, int pro
     else ((uint16_t*)p.Qh_dst)[o] = p.last ? f32_to_bf16_bits(v) : f32_to_f16_bits(v * p.sQ);
   }
 }
-
 template <int EPI>
 __device__ __forceinline__ void store_rr1(const GemmParams& p, size_t o, int prod, float v) {
   store_rr1<EPI>(p, o, prod, v, v);
 }
 
+// Value at (gi, gj) of a diagonal tile from its (identity-folded)
+// accumulator; stores it and returns it.
 template <int EPI>
-__device__ __forceinline__ float epilogue_rr1(const GemmParams& p, int mat, int prod, int gi,
-                                              int gj, float acc) {
+__device__ __forceinline__ float epilogue_rr1_acc(const GemmParams& p, int mat, int prod, int gi,
+                                                  int gj, float beta, float acc) {
   const size_t o = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
-  float v, q;
-  if constexpr (EPI == EPI_SYRK) {
-    const float inv = p.inv_norm[mat];
-    v = acc * inv * inv;
-    q = v;
-  } else if constexpr (EPI == EPI_POLY) {
-    v = p.b * ld_h1(p.Gh, o, 1.0f / p.sG) + p.c * (1.0f / (p.sG * p.sG)) * acc;
-    q = v + ((p.first && gi == gj) ? p.a : 0.0f);
-  } else if constexpr (EPI == EPI_PQPG) {
-    if (prod == 1) v = p.a * ld_h1(p.Gh, o, 1.0f / p.sG) + (1.0f / (p.sP * p.sG)) * acc;
-    else v = p.a * ld_h1(p.Qh_src, o, 1.0f / p.sQ) + (1.0f / (p.sP * p.sQ)) * acc;
-    q = v;
-  } else {
-    v = p.a * ld_h1(p.Hh, o, 1.0f / p.sH) + (1.0f / (p.sP * p.sH)) * acc;
-    q = v;
-  }
+  const float v = beta * acc;
+  float q = v;
+  if constexpr (EPI == EPI_POLY) q = v + ((p.first && gi == gj) ? p.a : 0.0f);
   store_rr1<EPI>(p, o, prod, v, q);
   return v;
 }
 
-// Row pass: compute from the accumulators at (gi, gj..gj+3), store, return
-// the primary value.
+// Row pass of an off-diagonal tile: values at (gi, gj..gj+3), stored; the
+// primary values are returned for the mirrored stores (Q1 = P~ off the
+// diagonal).
 template <int EPI>
-__device__ __forceinline__ float4 epilogue_rr4(const GemmParams& p, int mat, int prod, int gi,
-                                               int gj, float4 acc) {
+__device__ __forceinline__ float4 epilogue_rr4_acc(const GemmParams& p, int mat, int prod, int gi,
+                                                   int gj, float beta, float4 acc) {
   const size_t o = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
-  float4 v, q;
-  if constexpr (EPI == EPI_SYRK) {
-    const float inv = p.inv_norm[mat];
-    v = f4_axpy(inv * inv, acc, 0.0f, acc);
-    q = v;
-  } else if constexpr (EPI == EPI_POLY) {
-    const float4 g = ld_h4(p.Gh, o, 1.0f / p.sG);
-    v = f4_axpy(p.b, g, p.c * (1.0f / (p.sG * p.sG)), acc);
-    q = v;
-    if (p.first) {
-      if (gi == gj + 0) q.x += p.a;
-      if (gi == gj + 1) q.y += p.a;
-      if (gi == gj + 2) q.z += p.a;
-      if (gi == gj + 3) q.w += p.a;
-    }
-  } else if constexpr (EPI == EPI_PQPG) {
-    if (prod == 1) {
-      const float4 g = ld_h4(p.Gh, o, 1.0f / p.sG);
-      v = f4_axpy(p.a, g, 1.0f / (p.sP * p.sG), acc);
-    } else {
-      const float4 qs = ld_h4(p.Qh_src, o, 1.0f / p.sQ);
-      v = f4_axpy(p.a, qs, 1.0f / (p.sP * p.sQ), acc);
-    }
-    q = v;
-  } else {  // EPI_PH
-    const float4 hh = ld_h4(p.Hh, o, 1.0f / p.sH);
-    v = f4_axpy(p.a, hh, 1.0f / (p.sP * p.sH), acc);
-    q = v;
-  }
-  store_rr4<EPI>(p, o, prod, v, q);
-  return v;
-}
-
-// Row pass with the identity-term input already loaded (4 raw fp16 values).
-__device__ __forceinline__ float4 h4_from_raw(uint2 u, float inv_scale) {
-  const _Float16* h = (const _Float16*)&u;
-  return make_float4((float)h[0] * inv_scale, (float)h[1] * inv_scale, (float)h[2] * inv_scale,
-                     (float)h[3] * inv_scale);
-}
-
-template <int EPI>
-__device__ __forceinline__ const void* rr_input(const GemmParams& p, int prod, float* inv_scale) {
-  if constexpr (EPI == EPI_POLY) {
-    *inv_scale = 1.0f / p.sG;
-    return p.Gh;
-  } else if constexpr (EPI == EPI_PQPG) {
-    *inv_scale = prod == 1 ? 1.0f / p.sG : 1.0f / p.sQ;
-    return prod == 1 ? p.Gh : p.Qh_src;
-  } else {  // EPI_PH
-    *inv_scale = 1.0f / p.sH;
-    return p.Hh;
-  }
-}
-
-template <int EPI>
-__device__ __forceinline__ float4 epilogue_rr4_pre(const GemmParams& p, int mat, int prod, int gi,
-                                                   int gj, float4 acc, uint2 raw) {
-  const size_t o = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
-  float4 v, q;
-  if constexpr (EPI == EPI_SYRK) {
-    const float inv = p.inv_norm[mat];
-    v = f4_axpy(inv * inv, acc, 0.0f, acc);
-    q = v;
-  } else if constexpr (EPI == EPI_POLY) {
-    v = f4_axpy(p.b, h4_from_raw(raw, 1.0f / p.sG), p.c * (1.0f / (p.sG * p.sG)), acc);
-    q = v;
-    if (p.first) {  // off-diagonal tile: Q1 = P~ there
-    }
-  } else if constexpr (EPI == EPI_PQPG) {
-    if (prod == 1) v = f4_axpy(p.a, h4_from_raw(raw, 1.0f / p.sG), 1.0f / (p.sP * p.sG), acc);
-    else v = f4_axpy(p.a, h4_from_raw(raw, 1.0f / p.sQ), 1.0f / (p.sP * p.sQ), acc);
-    q = v;
-  } else {  // EPI_PH
-    v = f4_axpy(p.a, h4_from_raw(raw, 1.0f / p.sH), 1.0f / (p.sP * p.sH), acc);
-    q = v;
-  }
-  store_rr4<EPI>(p, o, prod, v, q);
+  const float4 v = f4_axpy(beta, acc, 0.0f, acc);
+  store_rr4<EPI>(p, o, prod, v, v);
   return v;
 }
 
