@@ -118,9 +118,14 @@ muon_status validate_hp(const muon_hparams& hp) {
   return MUON_OK;
 }
 
-int choose_tile(int64_t r, bool f32path) {
+int choose_tile(int64_t r, int64_t count, bool f32path) {
   if (r <= 64) return 64;
-  if (f32path || r <= 768) return 128;
+  if (f32path || r <= 768) {
+    // small-tile path: 64-wide tiles when 128-wide ones would leave most of
+    // the 256 compute units idle (under two lower-triangle tiles per CU)
+    const int64_t t = (r + 127) / 128;
+    return count * (t * (t + 1) / 2) < 512 ? 64 : 128;
+  }
   return 256;
 }
 
@@ -322,7 +327,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       B.transposed = B.m > B.n;
       B.r = std::min(B.m, B.n);
       B.c = std::max(B.m, B.n);
-      B.bt = choose_tile(B.r, f32path);
+      B.bt = choose_tile(B.r, (int64_t)members[b].size(), f32path);
       B.r_pad = round_up(B.r, B.bt);
       B.c_pad = round_up(B.c, B.bt);
       B.first = (int)p->order.size();
