@@ -39,10 +39,13 @@ constexpr int wait_imm(int vm, int lgkm) {
 typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef const __attribute__((address_space(1))) void gbl_ptr_t;
 
-// 16-byte chunk swizzle of a 64-byte row: conflict free for the MFMA
-// fragment reads under both 8-lane (32 banks) and 16-lane (64 banks) LDS
-// service groups.
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte chunk swizzle of a 64-byte row for the MFMA fragment reads (lane
+// l32 reads row base + l32, chunk 2s + h).  Chosen by measurement on gfx950
+// with eight waves reading concurrently: (r ^ (r >> 3)) & 3 sustains ~200
+// B/clk/CU of ds_read_b128 and shows no bank-conflict cycles, where
+// ((r >> 1) ^ (r >> 3)) & 3 reached ~120 B/clk/CU with ~3.5 conflict cycles
+// per read.
+__device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 3)) & 3; }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
@@ -121,7 +124,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   float* stile = reinterpret_cast<float*>(smem);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WGN, wn = wave % WGN;
   const int h = lane >> 5, l32 = lane & 31;
 
@@ -195,8 +199,9 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   // epilogue adds is symmetric, and X(n, m) is this tile's own B operand at
   // K = m: stages hk0 .. hk0+3 hold the wave's 128 rows m, stage hk0 + i
   // the 32 rows of MFMA block row i.  While such a stage is resident each
-  // lane reads its 4 x FN x 4 values (8 bytes per 4 consecutive m) and adds
-  // gamma * X to the accumulators, so the epilogue reads no r x r input.
+  // lane reads the 16-byte chunks holding its FN x 4 groups of 4 consecutive
+  // m (half h of each chunk) and adds gamma * X to the accumulators, so the
+  // epilogue reads no r x r input.
   constexpr bool HARVEST = EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH;
   float gam = 0.0f;
   if constexpr (HARVEST) gam = rr_gamma<EPI>(p);
@@ -227,14 +232,14 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
     for (int f = 0; f < FN; ++f) fb1[f] = *(const u32x4*)(sb + offB[1][f]);
     const int hs = kt - hk0;
-    uint2 hv[FN][4];
+    u32x4 hv[FN][4];  // whole 16-byte chunks; this lane's 4 values are half h
     if (HARVEST && (unsigned)hs < 4u) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int rb = wn * WTN + j * 32 + l32;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          hv[j][g] = *(const uint2*)(sb + OPB + rb * ROWB + ((g ^ swz4(rb)) << 4) + 8 * h);
+          hv[j][g] = *(const u32x4*)(sb + OPB + rb * ROWB + ((g ^ swz4(rb)) << 4));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -254,7 +259,12 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const _Float16* x = (const _Float16*)&hv[j][g];
+            const uint32_t w0 = h ? hv[j][g][2] : hv[j][g][0];
+            const uint32_t w1 = h ? hv[j][g][3] : hv[j][g][1];
+            const _Float16 x[4] = {__builtin_bit_cast(_Float16, (uint16_t)w0),
+                                   __builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)),
+                                   __builtin_bit_cast(_Float16, (uint16_t)w1),
+                                   __builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16))};
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += gam * (float)x[e];
           }
