@@ -102,6 +102,42 @@ __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) 
   }
 }
 
+__device__ __forceinline__ uint2 pack_h4(float4 v, float scale) {
+  return make_uint2(
+      (uint32_t)f32_to_f16_bits(v.x * scale) | ((uint32_t)f32_to_f16_bits(v.y * scale) << 16),
+      (uint32_t)f32_to_f16_bits(v.z * scale) | ((uint32_t)f32_to_f16_bits(v.w * scale) << 16));
+}
+__device__ __forceinline__ uint2 pack_b4(float4 v) {
+  return make_uint2((uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
+                    (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
+}
+
+// Store elements [lo, hi) of four packed 16-bit values at base + o (one
+// 8-byte store when all four go).
+__device__ __forceinline__ void store16x4(uint16_t* base, size_t o, uint2 v, int lo, int hi) {
+  if (lo == 0 && hi == 4) {
+    *(uint2*)(base + o) = v;
+    return;
+  }
+  const uint16_t e[4] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16)};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (k >= lo && k < hi) base[o + k] = e[k];
+}
+
+// Q1 = a I + P~ from four staged P~ values (fp16, scaled by 1/inv_sp):
+// element `dk` (if 0..3) lies on the diagonal.  Output in Q's format.
+__device__ __forceinline__ uint2 q_from_p(uint2 pv, float inv_sp, const GemmParams& p, int dk) {
+  const _Float16* hp = (const _Float16*)&pv;
+  float4 qv = make_float4((float)hp[0] * inv_sp, (float)hp[1] * inv_sp, (float)hp[2] * inv_sp,
+                          (float)hp[3] * inv_sp);
+  if (dk == 0) qv.x += p.a;
+  if (dk == 1) qv.y += p.a;
+  if (dk == 2) qv.z += p.a;
+  if (dk == 3) qv.w += p.a;
+  return p.last ? pack_b4(qv) : pack_h4(qv, p.sQ);
+}
+
 }  // namespace
 
 // NW = 4: waves in 2 x 2, each 128 x 128 (4 x 4 MFMA blocks, one wave per SIMD)
@@ -293,55 +329,46 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
   __syncthreads();
 
-  // Epilogue through LDS, 128 rows per round.  The fp32 tile is staged with
-  // its 16-byte column chunks XOR-swizzled by (row / 4) (see epi_off), which
-  // makes both passes below conflict free with 16-byte LDS accesses.  The
-  // r x r products read no global input here (their identity term is already
-  // in the accumulators); the final product requests all of a round's W rows
-  // at once, so their latency overlaps the staging.  Row pass: each thread takes four
-  // consecutive columns (64 threads per tile row) and writes the primary
-  // value back; mirror pass (symmetric results, strictly-lower elements): a
-  // thread reads a 4 x 4 block, transposes it in registers and writes four
-  // consecutive elements into each of four mirrored rows.
-  auto epi_off = [](int il, int jc) {
-    return il * DT + ((((jc >> 2) ^ ((il >> 2) & 63)) << 2) | (jc & 3));
-  };
-  const bool diag = p.triangular && ti == tj;
-  float beta = 0.0f;
-  if constexpr (EPI != EPI_FINAL) beta = rr_beta<EPI>(p, mat, prod);
-  const int jl = (tid & 63) * 4;
-  const int gj = row0B + jl;
-  constexpr int RPI = NT / 64;   // tile rows per row-pass iteration
-  constexpr int PER = RR / RPI;  // row-pass iterations per round
+  if constexpr (EPI == EPI_FINAL) {
+    // Final product: the fp32 tile goes through LDS in two rounds of 128
+    // rows, its 16-byte column chunks XOR-swizzled by (row / 4) (epi_off) so
+    // that the staging writes and the row reads are conflict free.  All of a
+    // round's W rows are requested before the staging, so their latency
+    // overlaps it; each thread then updates four consecutive columns of a row
+    // (64 threads per tile row).
+    auto epi_off = [](int il, int jc) {
+      return il * DT + ((((jc >> 2) ^ ((il >> 2) & 63)) << 2) | (jc & 3));
+    };
+    const int jl = (tid & 63) * 4;
+    const int gj = row0B + jl;
+    constexpr int RPI = NT / 64;   // tile rows per row-pass iteration
+    constexpr int PER = RR / RPI;  // row-pass iterations per round
+    const MatPtrs mp = p.table[mat];
+    const float inv = p.inv_norm[mat];
+    const bool wvec = p.vec && gj + 4 <= p.out_cols;
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int gr0 = row0A + round * RR;
-    float4 win[EPI == EPI_FINAL ? PER : 1];
-    bool wvec = false;
-    if constexpr (EPI == EPI_FINAL) {
-      const MatPtrs mp = p.table[mat];
-      wvec = p.vec && gj + 4 <= p.out_cols;
+    for (int round = 0; round < 2; ++round) {
+      const int gr0 = row0A + round * RR;
+      float4 win[PER];
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const int gi = gr0 + e * RPI + (tid >> 6);
         win[e] = (wvec && gi < p.out_rows) ? nt_load4(mp.W + (size_t)gi * p.out_cols + gj)
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-    }
-    if (wm == round) {
+      if (wm == round) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int jc = wn * WTN + j * 32 + l32;
-            stile[epi_off(il, jc)] = acc[i][j][v];
-          }
-    }
-    __syncthreads();
-    if constexpr (EPI == EPI_FINAL) {
+            for (int v = 0; v < 16; ++v) {
+              const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+              const int jc = wn * WTN + j * 32 + l32;
+              stile[epi_off(il, jc)] = acc[i][j][v];
+            }
+      }
+      __syncthreads();
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const int il = e * RPI + (tid >> 6);
@@ -349,8 +376,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
         const int gi = gr0 + il;
         if (wvec) {
           if (gi < p.out_rows) {
-            const MatPtrs mp = p.table[mat];
-            const float inv = p.inv_norm[mat];
             const float4 o = make_float4(av.x * inv, av.y * inv, av.z * inv, av.w * inv);
             const size_t idx = (size_t)gi * p.out_cols + gj;
             nt_store4(mp.W + idx, f4_axpy(p.decay, win[e], -p.step, o));
@@ -360,59 +385,93 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
           epilogue_final4(p, mat, gi, gj, av);
         }
       }
-    } else if (!diag) {
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const int il = e * RPI + (tid >> 6);
-        float4* sp = (float4*)(stile + epi_off(il, jl));
-        *sp = epilogue_rr4_acc<EPI>(p, mat, prod, gr0 + il, gj, beta, *sp);
-      }
-    } else {
-      // diagonal tile: element-wise lower-triangle mask
-#pragma unroll 1
-      for (int e = 0; e < PER; ++e) {
-        const int il = e * RPI + (tid >> 6);
-        float4* sp = (float4*)(stile + epi_off(il, jl));
-        const float4 av = *sp;
-        const int gi = gr0 + il;
-        float a4[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (gi >= gj + k) a4[k] = epilogue_rr1_acc<EPI>(p, mat, prod, gi, gj + k, beta, a4[k]);
-        *sp = make_float4(a4[0], a4[1], a4[2], a4[3]);
-      }
-    }
-    if constexpr (EPI != EPI_FINAL) {
       __syncthreads();
-      const int il0 = (tid & 31) * 4;
-      constexpr int CG = NT / 32;  // 4-column groups per iteration
-#pragma unroll 1
-      for (int e = 0; e < DT / 4 / CG; ++e) {
-        const int jc0 = ((tid >> 5) + CG * e) * 4;
-        float4 r[4];
+    }
+  } else {
+    // Symmetric r x r results.  Every wave converts its accumulators to the
+    // 16-bit output format (v = beta * acc, scaled fp16 or bf16) and stages
+    // the whole tile once, column-major, in the freed operand ring: T[c] holds
+    // column c of the tile as 64 chunks of 4 rows (8 bytes), chunk q stored at
+    // slot q ^ f(c) (t_off), which keeps the staging writes and both read
+    // passes below free of bank conflicts.  After one barrier:
+    //   rows:    lane L of an iteration reads the 4 x 4 block of columns
+    //            4L..4L+3 x rows 4q..4q+3, transposes it in registers and
+    //            writes 4 rows (each store instruction is one 512-byte row)
+    //   mirror:  T[c] is row c of the mirrored block, copied out as is
+    // Diagonal tiles store the lower triangle directly and mirror the strictly
+    // lower part; POLY on the first iteration also writes Q1 = a I + P~,
+    // derived from the staged P~ (power-of-two rescale).
+    auto t_off = [](int c, int q) { return c * 512 + ((q ^ (((c >> 2) ^ ((c & 3) << 3)) & 31)) << 3); };
+    const bool diag = p.triangular && ti == tj;
+    const float beta = rr_beta<EPI>(p, mat, prod);
+    uint16_t* out1;
+    float sc1;
+    bool bf1 = false;
+    if constexpr (EPI == EPI_SYRK || EPI == EPI_PH) {
+      out1 = (uint16_t*)p.Gh;
+      sc1 = p.sG;
+    } else if constexpr (EPI == EPI_POLY) {
+      out1 = (uint16_t*)p.Ph;
+      sc1 = p.sP;
+    } else if (prod == 1) {
+      out1 = (uint16_t*)p.Hh;
+      sc1 = p.sH;
+    } else {
+      out1 = (uint16_t*)p.Qh_dst;
+      sc1 = p.sQ;
+      bf1 = p.last;
+    }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = *(const float4*)(stile + epi_off(il0 + q, jc0));
-        const float4 c[4] = {make_float4(r[0].x, r[1].x, r[2].x, r[3].x),
-                             make_float4(r[0].y, r[1].y, r[2].y, r[3].y),
-                             make_float4(r[0].z, r[1].z, r[2].z, r[3].z),
-                             make_float4(r[0].w, r[1].w, r[2].w, r[3].w)};
-        const int gi0 = gr0 + il0;
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int gjm = row0B + jc0 + k;
-          const size_t o = (size_t)mat * p.rr_stride + (size_t)gjm * p.ldr + gi0;
-          if (!diag) {
-            store_rr4<EPI>(p, o, prod, c[k], c[k]);
-          } else {
-            const float a4[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (gi0 + q > gjm) store_rr1<EPI>(p, o + q, prod, a4[q]);
-          }
+        for (int g = 0; g < 4; ++g) {
+          const float4 v = make_float4(beta * acc[i][j][4 * g], beta * acc[i][j][4 * g + 1],
+                                       beta * acc[i][j][4 * g + 2], beta * acc[i][j][4 * g + 3]);
+          *(uint2*)(smem + t_off(wn * WTN + 32 * j + l32, wm * 32 + 8 * i + 2 * g + h)) =
+              bf1 ? pack_b4(v) : pack_h4(v, sc1);
         }
+    __syncthreads();
+    const bool qout = EPI == EPI_POLY && p.first;
+    uint16_t* out2 = (uint16_t*)p.Qh_dst;
+    const float inv_s1 = 1.0f / sc1;
+    const size_t mb = (size_t)mat * p.rr_stride;
+    constexpr int QPW = 64 / NW;  // row-chunk iterations per wave
+#pragma unroll 2
+    for (int it = 0; it < QPW; ++it) {
+      const int q = wave * QPW + it;
+      uint2 b[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[k] = *(const uint2*)(smem + t_off(4 * lane + k, q));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint2 row =
+            e < 2 ? make_uint2(__builtin_amdgcn_perm(b[1].x, b[0].x, sel),
+                               __builtin_amdgcn_perm(b[3].x, b[2].x, sel))
+                  : make_uint2(__builtin_amdgcn_perm(b[1].y, b[0].y, sel),
+                               __builtin_amdgcn_perm(b[3].y, b[2].y, sel));
+        const int il = 4 * q + e, jc = 4 * lane;
+        const size_t o = mb + (size_t)(row0A + il) * p.ldr + (row0B + jc);
+        // diagonal tile: columns jc + k with k <= il - jc are on or below it
+        const int n = diag ? min(max(il - jc + 1, 0), 4) : 4;
+        store16x4(out1, o, row, 0, n);
+        if (qout) store16x4(out2, o, q_from_p(row, inv_s1, p, diag ? il - jc : -1), 0, n);
       }
     }
-    __syncthreads();
+    constexpr int CPW = 256 / NW;  // mirrored rows per wave
+#pragma unroll 4
+    for (int it = 0; it < CPW; ++it) {
+      const int jc = wave * CPW + it;
+      const uint2 v = *(const uint2*)(smem + t_off(jc, lane));
+      const int il0 = 4 * lane;
+      const size_t o = mb + (size_t)(row0B + jc) * p.ldr + (row0A + il0);
+      // diagonal tile: rows il0 + e > jc only (strictly lower in the tile)
+      const int s0 = diag ? min(max(jc - il0 + 1, 0), 4) : 0;
+      store16x4(out1, o, v, s0, 4);
+      if (qout) store16x4(out2, o, q_from_p(v, inv_s1, p, -1), s0, 4);
+    }
   }
 }
 

@@ -77,47 +77,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int mat, int prod,
 }
 
 // ---------------------------------------------------------------------------
-// fp16-only epilogues of the 256-tile path (no fp32 master copies of the
-// r x r results), four consecutive elements per call.
-__device__ __forceinline__ void st_h4(void* base, size_t o, float4 v, float scale) {
-  uint2 u;
-  u.x = (uint32_t)f32_to_f16_bits(v.x * scale) | ((uint32_t)f32_to_f16_bits(v.y * scale) << 16);
-  u.y = (uint32_t)f32_to_f16_bits(v.z * scale) | ((uint32_t)f32_to_f16_bits(v.w * scale) << 16);
-  *(uint2*)((uint16_t*)base + o) = u;
-}
-
-__device__ __forceinline__ void st_b4(void* base, size_t o, float4 v) {
-  uint2 u;
-  u.x = (uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16);
-  u.y = (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16);
-  *(uint2*)((uint16_t*)base + o) = u;
-}
-
+// Helpers of the 256-tile path (gemm_dma.hip), which keeps no fp32 master
+// copies of the r x r results.
 __device__ __forceinline__ float4 f4_axpy(float a, float4 x, float b, float4 y) {
   return make_float4(a * x.x + b * y.x, a * x.y + b * y.y, a * x.z + b * y.z, a * x.w + b * y.w);
-}
-
-// Store the outputs that derive from `v` at (gi, gj..gj+3) of an r x r
-// result; `q` is the Q output of POLY on the first iteration (a I + P~).
-template <int EPI>
-__device__ __forceinline__ void store_rr4(const GemmParams& p, size_t o, int prod, float4 v,
-                                          float4 q) {
-  if constexpr (EPI == EPI_SYRK || EPI == EPI_PH) {
-    st_h4(p.Gh, o, v, p.sG);
-  } else if constexpr (EPI == EPI_POLY) {
-    st_h4(p.Ph, o, v, p.sP);
-    if (p.first) {
-      if (p.last) st_b4(p.Qh_dst, o, q);
-      else st_h4(p.Qh_dst, o, q, p.sQ);
-    }
-  } else {  // EPI_PQPG
-    if (prod == 1) {
-      st_h4(p.Hh, o, v, p.sH);
-    } else {
-      if (p.last) st_b4(p.Qh_dst, o, v);
-      else st_h4(p.Qh_dst, o, v, p.sQ);
-    }
-  }
 }
 
 // The 256-tile kernels fold the identity term of each r x r product into
@@ -145,51 +108,6 @@ template <int EPI>
 __device__ __forceinline__ float rr_gamma(const GemmParams& p) {
   if constexpr (EPI == EPI_POLY) return p.b * p.sG / p.c;
   else return p.a * p.sP;
-}
-
-// Scalar store for the diagonal tiles (lower-triangle masking per element).
-template <int EPI>
-__device__ __forceinline__ void store_rr1(const GemmParams& p, size_t o, int prod, float v,
-                                          float q) {
-  if constexpr (EPI == EPI_SYRK || EPI == EPI_PH) {
-    ((uint16_t*)p.Gh)[o] = f32_to_f16_bits(v * p.sG);
-  } else if constexpr (EPI == EPI_POLY) {
-    ((uint16_t*)p.Ph)[o] = f32_to_f16_bits(v * p.sP);
-    if (p.first)
-      ((uint16_t*)p.Qh_dst)[o] = p.last ? f32_to_bf16_bits(q) : f32_to_f16_bits(q * p.sQ);
-  } else {
-    if (prod == 1) ((uint16_t*)p.Hh)[o] = f32_to_f16_bits(v * p.sH);
-    else ((uint16_t*)p.Qh_dst)[o] = p.last ? f32_to_bf16_bits(v) : f32_to_f16_bits(v * p.sQ);
-  }
-}
-template <int EPI>
-__device__ __forceinline__ void store_rr1(const GemmParams& p, size_t o, int prod, float v) {
-  store_rr1<EPI>(p, o, prod, v, v);
-}
-
-// Value at (gi, gj) of a diagonal tile from its (identity-folded)
-// accumulator; stores it and returns it.
-template <int EPI>
-__device__ __forceinline__ float epilogue_rr1_acc(const GemmParams& p, int mat, int prod, int gi,
-                                                  int gj, float beta, float acc) {
-  const size_t o = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
-  const float v = beta * acc;
-  float q = v;
-  if constexpr (EPI == EPI_POLY) q = v + ((p.first && gi == gj) ? p.a : 0.0f);
-  store_rr1<EPI>(p, o, prod, v, q);
-  return v;
-}
-
-// Row pass of an off-diagonal tile: values at (gi, gj..gj+3), stored; the
-// primary values are returned for the mirrored stores (Q1 = P~ off the
-// diagonal).
-template <int EPI>
-__device__ __forceinline__ float4 epilogue_rr4_acc(const GemmParams& p, int mat, int prod, int gi,
-                                                   int gj, float beta, float4 acc) {
-  const size_t o = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
-  const float4 v = f4_axpy(beta, acc, 0.0f, acc);
-  store_rr4<EPI>(p, o, prod, v, v);
-  return v;
 }
 
 // Final product: O = acc / ||U||, W <- decay W - step O at (gi, gj..gj+3).
