@@ -64,6 +64,20 @@ typedef enum {
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
 
+/* How the Newton-Schulz iteration of eq. (2) ("Infra Optimizers",
+ * Background) is evaluated.  Both compute the same X_N in exact arithmetic.
+ *   MUON_FORM_GRAM:   in the r x r Gram space ("DMuon" 2.2): one SYRK
+ *                     G0 = X0 X0^T, the recursion on r x r polynomials of G0,
+ *                     one final product Q X0.  3 r^2 c + 17 r^3 flops.
+ *   MUON_FORM_DIRECT: eq. (2) on X itself, N times A = X X^T (SYRK),
+ *                     P~ = b A + c A^2, X <- a X + P~ X.  15 r^2 c + 5 r^3
+ *                     flops.  16-bit path only (ns_dtype MUON_BF16): X is
+ *                     kept as scaled fp16 in both layouts; every product
+ *                     uses 256-wide tiles.
+ *   MUON_FORM_AUTO:   the cheaper of the two by flop count, which is the
+ *                     Gram form for every shape (c >= r; equal cost at c = r). */
+typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } muon_formulation;
+
 /* Hyper-parameters fixed at plan time.  muon_default_hparams fills the
  * values the pages give: mu = 0.95 and N = 5 ("Infra Optimizers", Scaling Up
  * Muon), a = 3.4445, b = -4.7750, c = 2.0315 (Background, eq. (2)), the 0.2
@@ -91,6 +105,7 @@ typedef struct {
                                   library default (16 GiB).  Buckets of
                                   same-shape matrices are split into chunks
                                   that fit; a single matrix always fits.     */
+  muon_formulation formulation; /* see above; 0 = MUON_FORM_AUTO            */
 } muon_plan_desc;
 
 /* Fill *hp with the defaults listed above.  Returns MUON_ERR_INVALID_ARGUMENT
@@ -102,7 +117,8 @@ muon_status muon_default_hparams(muon_hparams* hp);
  * Transformers" 3.1) and lay out the workspace.  Host only: no device work,
  * no device allocation.  On success *plan owns host memory only and
  * *workspace_bytes (nullable) receives the workspace size needed by both
- * step calls. */
+ * step calls.  MUON_ERR_UNSUPPORTED for MUON_FORM_DIRECT with ns_dtype
+ * MUON_F32; MUON_ERR_INVALID_ARGUMENT for an unknown formulation. */
 muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* workspace_bytes);
 
 /* Release a plan.  NULL is accepted.  The caller must ensure no work using
@@ -115,7 +131,8 @@ muon_status muon_plan_workspace_size(muon_plan_t plan, size_t* workspace_bytes);
 /* Number of same-shape buckets and launch chunks the planner formed. */
 muon_status muon_plan_info(muon_plan_t plan, int64_t* num_buckets, int64_t* num_chunks);
 
-/* Newton-Schulz (refresh) step for every planned matrix:
+/* Newton-Schulz (refresh) step for every planned matrix (Gram form shown;
+ * the direct form evaluates the same X_N by iterating eq. (2) on X):
  *   M  <- mu*M + G                                   ("Infra Optimizers" eq. (1))
  *   U   = mu*M + G  (updated M; U = M if nesterov=0)  (Background, Nesterov)
  *   X0  = O(U) / ||U||_F,  O = transpose iff m > n     (eq. (2) preamble; DiT 3.1)
@@ -157,7 +174,10 @@ typedef enum {
   MUON_K_COLSUM = 8,      /* RowNorm m > n: M update + column sums        */
   MUON_K_COLFINAL = 9,    /* RowNorm m > n: column scale                 */
   MUON_K_COLAPPLY = 10,   /* RowNorm m > n: apply                         */
-  MUON_K_COUNT = 11
+  MUON_K_XCAST = 11,      /* direct form: X0 = U / ||U|| as scaled fp16   */
+  MUON_K_XUPD = 12,       /* direct form: X <- a X + P~ X (both layouts)  */
+  MUON_K_WUPD = 13,       /* direct form: weight update from X_N          */
+  MUON_K_COUNT = 14
 } muon_kernel_class;
 
 /* Launch profiler (measurement support, off by default).  While enabled,

@@ -27,7 +27,8 @@ EXPORTED = ("muon_default_hparams", "muon_plan", "muon_plan_destroy", "muon_plan
             "muon_plan_info", "muon_step_batched", "rownorm_step", "muon_plan_set_profiling",
             "muon_plan_kernel_times", "muon_status_string")
 KERNEL_CLASSES = ("prep", "norm", "syrk", "poly", "pqpg", "ph", "final", "rownorm", "colsum",
-                  "colfinal", "colapply")
+                  "colfinal", "colapply", "xcast", "xupd", "wupd")
+FORMULATIONS = {"auto": 0, "gram": 1, "direct": 2}
 
 
 class MuonError(RuntimeError):
@@ -47,7 +48,7 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [("num_matrices", ctypes.c_int64), ("rows", ctypes.POINTER(ctypes.c_int64)),
                 ("cols", ctypes.POINTER(ctypes.c_int64)), ("grad_dtype", ctypes.c_int),
                 ("ns_dtype", ctypes.c_int), ("hp", Hparams),
-                ("max_workspace_bytes", ctypes.c_int64)]
+                ("max_workspace_bytes", ctypes.c_int64), ("formulation", ctypes.c_int)]
 
 
 _lib = None
@@ -107,10 +108,12 @@ def _ptr_array(ptrs: Sequence[Optional[int]]):
 class Plan:
     """A planned set of matrices (muon_plan).  `shapes` is a list of (m, n).
 
-    grad_dtype / ns_dtype are "f32" or "bf16"."""
+    grad_dtype / ns_dtype are "f32" or "bf16"; formulation is "auto", "gram"
+    or "direct" (or the muon_formulation value)."""
 
     def __init__(self, shapes: Sequence[tuple], grad_dtype: str = "f32", ns_dtype: str = "bf16",
-                 hp: Optional[Hparams] = None, max_workspace_bytes: int = 0):
+                 hp: Optional[Hparams] = None, max_workspace_bytes: int = 0,
+                 formulation: str = "auto"):
         lib = load()
         self._lib = lib
         self.shapes = [(int(m), int(n)) for m, n in shapes]
@@ -125,6 +128,7 @@ class Plan:
         desc.ns_dtype = {"f32": MUON_F32, "bf16": MUON_BF16}[ns_dtype]
         desc.hp = hp if hp is not None else default_hparams()
         desc.max_workspace_bytes = int(max_workspace_bytes)
+        desc.formulation = FORMULATIONS[formulation] if isinstance(formulation, str) else int(formulation)
         self.hp = desc.hp
         self.grad_dtype, self.ns_dtype = grad_dtype, ns_dtype
         handle = ctypes.c_void_p()

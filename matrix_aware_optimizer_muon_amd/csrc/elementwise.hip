@@ -482,4 +482,74 @@ hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int v
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Direct form.  X0 cast: each thread converts 8 consecutive elements (one
+// 16-byte load, one 16-byte store) of one of the two layouts in place.
+__global__ void __launch_bounds__(256) xcast_kernel(const XcastParams p) {
+  const int64_t per_buf = p.elems / 8;
+  const int64_t blocks_per_buf = (per_buf + 255) / 256;
+  const int64_t b = blockIdx.x;
+  const int mat = (int)(b / (2 * blocks_per_buf));
+  const int64_t rem = b - (int64_t)mat * 2 * blocks_per_buf;
+  const int which = rem >= blocks_per_buf ? 1 : 0;
+  const int64_t chunk = (rem - which * blocks_per_buf) * 256 + threadIdx.x;
+  if (chunk >= per_buf) return;
+  uint16_t* base = (uint16_t*)(which ? p.Xt : p.Xn) + (size_t)mat * p.x_stride + (size_t)chunk * 8;
+  const float sc = p.inv_norm[mat] * p.sx;
+  const u32x4 in = *(const u32x4*)base;
+  u32x4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = __uint_as_float(in[k] << 16), hi = __uint_as_float(in[k] & 0xffff0000u);
+    out[k] = (uint32_t)f32_to_f16_bits(lo * sc) | ((uint32_t)f32_to_f16_bits(hi * sc) << 16);
+  }
+  *(u32x4*)base = out;
+}
+
+hipError_t launch_xcast(const XcastParams& p, int nmat, hipStream_t s) {
+  if (p.elems % 8) return hipErrorInvalidValue;
+  const uint64_t blocks = (uint64_t)nmat * 2 * (uint64_t)((p.elems / 8 + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xcast_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// Weight update from X_N: 4 columns per thread, a 1024-column strip of one
+// row per workgroup.
+__global__ void __launch_bounds__(256) wupd_kernel(const WupdParams p, int vec) {
+  const int cblocks = (p.n + 1023) / 1024;
+  const int per_mat = cblocks * p.m;
+  const int mat = blockIdx.x / per_mat;
+  const int bl = blockIdx.x - mat * per_mat;
+  const int row = bl / cblocks, cb = bl - row * cblocks;
+  const int col = cb * 1024 + threadIdx.x * 4;
+  if (col >= p.n) return;
+  const int valid = p.n - col;
+  const bool v4 = vec && valid >= 4;
+  const MatPtrs mp = p.table[mat];
+  const uint16_t* xr = (const uint16_t*)p.X + (size_t)mat * p.x_stride + (size_t)row * p.n_pad + col;
+  // the X row is padded to n_pad (a multiple of 256): 4 elements always readable
+  const uint2 xv = *(const uint2*)xr;
+  const _Float16* xh = (const _Float16*)&xv;
+  const float4 o = make_float4((float)xh[0] * p.inv_sx, (float)xh[1] * p.inv_sx,
+                               (float)xh[2] * p.inv_sx, (float)xh[3] * p.inv_sx);
+  const size_t idx = (size_t)row * p.n + col;
+  float4 w = load_f4(mp.W + idx, v4, valid);
+  w.x = p.decay * w.x - p.step * o.x;
+  w.y = p.decay * w.y - p.step * o.y;
+  w.z = p.decay * w.z - p.step * o.z;
+  w.w = p.decay * w.w - p.step * o.w;
+  store_f4(mp.W + idx, w, v4, valid);
+  if (mp.O) store_f4(mp.O + idx, o, v4, valid);
+}
+
+hipError_t launch_wupd(const WupdParams& p, int nmat, int vec, hipStream_t s) {
+  const uint64_t blocks = (uint64_t)nmat * (uint64_t)p.m * (uint64_t)((p.n + 1023) / 1024);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffffull || p.n_pad % 4 || p.n > p.n_pad) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wupd_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p, vec);
+  return hipGetLastError();
+}
+
 }  // namespace muon

@@ -1,7 +1,7 @@
 // 256 x 256 MFMA GEMM C = A * B^T with a four-stage LDS ring filled by
 // direct global->LDS loads (gfx950 global_load_lds_dwordx4), for the large
-// products of the Gram-space Newton-Schulz step (SYRK, the r x r recursion
-// and the final product; epilogues in gemm_epilogue.hpp).
+// products of the Newton-Schulz step: SYRK, the r x r recursion and the final
+// product of the Gram form, and the direct form's X' = a X + P~ X (XUPD).
 //
 // Both operands are K-contiguous (the prep kernel writes X0 and X0^T).
 // 8 wave64 (two per SIMD) in 2 x 4, each owning 128 x 64 = 4 x 2 blocks of
@@ -238,7 +238,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   // lane reads the 16-byte chunks holding its FN x 4 groups of 4 consecutive
   // m (half h of each chunk) and adds gamma * X to the accumulators, so the
   // epilogue reads no r x r input.
-  constexpr bool HARVEST = EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH;
+  constexpr bool HARVEST = EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH || EPI == EPI_XUPD;
   float gam = 0.0f;
   if constexpr (HARVEST) gam = rr_gamma<EPI>(p);
   const int hk0 = row0A / DBK + wm * 4;
@@ -388,7 +388,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       __syncthreads();
     }
   } else {
-    // Symmetric r x r results.  Every wave converts its accumulators to the
+    // Symmetric r x r results (and the direct form's X' = a X + P~ X, whose
+    // transposed block goes to the X'^T buffer).  Every wave converts its accumulators to the
     // 16-bit output format (v = beta * acc, scaled fp16 or bf16) and stages
     // the whole tile once, column-major, in the freed operand ring: T[c] holds
     // column c of the tile as 64 chunks of 4 rows (8 bytes), chunk q stored at
@@ -407,7 +408,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     uint16_t* out1;
     float sc1;
     bool bf1 = false;
-    if constexpr (EPI == EPI_SYRK || EPI == EPI_PH) {
+    if constexpr (EPI == EPI_XUPD) {
+      out1 = (uint16_t*)p.Yn;
+      sc1 = p.sX;
+    } else if constexpr (EPI == EPI_SYRK || EPI == EPI_PH) {
       out1 = (uint16_t*)p.Gh;
       sc1 = p.sG;
     } else if constexpr (EPI == EPI_POLY) {
@@ -436,7 +440,17 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     const bool qout = EPI == EPI_POLY && p.first;
     uint16_t* out2 = (uint16_t*)p.Qh_dst;
     const float inv_s1 = 1.0f / sc1;
-    const size_t mb = (size_t)mat * p.rr_stride;
+    // rows go to out1 (ld ldp), the transposed block to outm (ld ldm): the
+    // same symmetric buffer for r x r results, X' and X'^T for XUPD
+    uint16_t* outm = out1;
+    int ldp = p.ldr, ldm = p.ldr;
+    size_t mb = (size_t)mat * p.rr_stride;
+    if constexpr (EPI == EPI_XUPD) {
+      outm = (uint16_t*)p.Yt;
+      ldp = p.ldyn;
+      ldm = p.ldyt;
+      mb = (size_t)mat * p.y_stride;
+    }
     constexpr int QPW = 64 / NW;  // row-chunk iterations per wave
 #pragma unroll 2
     for (int it = 0; it < QPW; ++it) {
@@ -453,7 +467,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
                   : make_uint2(__builtin_amdgcn_perm(b[1].y, b[0].y, sel),
                                __builtin_amdgcn_perm(b[3].y, b[2].y, sel));
         const int il = 4 * q + e, jc = 4 * lane;
-        const size_t o = mb + (size_t)(row0A + il) * p.ldr + (row0B + jc);
+        const size_t o = mb + (size_t)(row0A + il) * ldp + (row0B + jc);
         // diagonal tile: columns jc + k with k <= il - jc are on or below it
         const int n = diag ? min(max(il - jc + 1, 0), 4) : 4;
         store16x4(out1, o, row, 0, n);
@@ -466,10 +480,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       const int jc = wave * CPW + it;
       const uint2 v = *(const uint2*)(smem + t_off(jc, lane));
       const int il0 = 4 * lane;
-      const size_t o = mb + (size_t)(row0B + jc) * p.ldr + (row0A + il0);
+      const size_t o = mb + (size_t)(row0B + jc) * ldm + (row0A + il0);
       // diagonal tile: rows il0 + e > jc only (strictly lower in the tile)
       const int s0 = diag ? min(max(jc - il0 + 1, 0), 4) : 0;
-      store16x4(out1, o, v, s0, 4);
+      store16x4(outm, o, v, s0, 4);
       if (qout) store16x4(out2, o, q_from_p(v, inv_s1, p, -1), s0, 4);
     }
   }
@@ -493,7 +507,9 @@ static hipError_t launch_dma_one(const GemmParams& p, int nmat, hipStream_t s) {
 
 hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s) {
   switch (epi) {
-    case EPI_SYRK: return launch_dma_one<0, EPI_SYRK>(p, nmat, s);
+    case EPI_SYRK:
+      return p.xkind ? launch_dma_one<1, EPI_SYRK>(p, nmat, s) : launch_dma_one<0, EPI_SYRK>(p, nmat, s);
+    case EPI_XUPD: return launch_dma_one<1, EPI_XUPD>(p, nmat, s);
     case EPI_POLY: return launch_dma_one<1, EPI_POLY>(p, nmat, s);
     case EPI_PQPG: return launch_dma_one<1, EPI_PQPG>(p, nmat, s);
     case EPI_PH: return launch_dma_one<1, EPI_PH>(p, nmat, s);

@@ -91,11 +91,16 @@ __device__ __forceinline__ float4 f4_axpy(float a, float4 x, float b, float4 y) 
 //   PQPG  H  = a G + P~ G,   acc = sP sG P~ G     beta = 1/(sP sG),    gamma = a sP
 //         Q' = a Q + P~ Q,   acc = sP sQ P~ Q     beta = 1/(sP sQ),    gamma = a sP
 //   PH    G' = a H + P~ H,   acc = sP sH P~ H     beta = 1/(sP sH),    gamma = a sP
+//   XUPD  X' = a X + P~ X,   acc = sP sX P~ X     beta = 1/(sP sX),    gamma = a sP
+//         (direct form; SYRK there runs on fp16 X: beta = 1/sX^2)
 template <int EPI>
 __device__ __forceinline__ float rr_beta(const GemmParams& p, int mat, int prod) {
   if constexpr (EPI == EPI_SYRK) {
+    if (p.syrk_scale > 0.0f) return p.syrk_scale;
     const float inv = p.inv_norm[mat];
     return inv * inv;
+  } else if constexpr (EPI == EPI_XUPD) {
+    return 1.0f / (p.sP * p.sX);
   } else if constexpr (EPI == EPI_POLY) {
     return p.c * (1.0f / (p.sG * p.sG));
   } else if constexpr (EPI == EPI_PQPG) {

@@ -14,7 +14,7 @@ struct MatPtrs {
   float* O;  // nullable direction output
 };
 
-enum Epi : int { EPI_SYRK = 0, EPI_POLY = 1, EPI_PQPG = 2, EPI_PH = 3, EPI_FINAL = 4 };
+enum Epi : int { EPI_SYRK = 0, EPI_POLY = 1, EPI_PQPG = 2, EPI_PH = 3, EPI_FINAL = 4, EPI_XUPD = 5 };
 enum OpType : int { OP_BF16 = 0, OP_F32 = 1 };
 
 // Parameters of one batched GEMM launch C = A * B^T over a chunk of
@@ -54,6 +54,14 @@ struct GemmParams {
   float decay;             // 1 - lr*wd
   float step;              // lr * scale_coeff * sqrt(max(m, n))
   int vec;                 // W / O rows allow 16-byte access
+  // direct form
+  int xkind;               // SYRK operand type: 0 bf16, 1 fp16
+  float syrk_scale;        // SYRK result scale; 0: 1/||U||^2
+  float sX;                // fp16 scale of X
+  void* Yn;                // EPI_XUPD: X' natural layout (r_pad x c_pad, ld ldyn)
+  void* Yt;                // EPI_XUPD: X' transposed (c_pad x r_pad, ld ldyt)
+  int ldyn, ldyt;
+  int64_t y_stride;        // elements between matrices (both)
 };
 
 hipError_t launch_gemm(const GemmParams& p, int epi, int op, int bt, int nmat, hipStream_t s);
@@ -91,6 +99,30 @@ struct RowNormParams {
   float* colscale;         // tall case: [nmat][n]
   int row_blocks;
 };
+
+// ---- direct form ("Infra Optimizers" eq. (2) iterated on X) --------------
+// X0 = U / ||U|| as fp16 scaled by sx, in place over both U layouts of the
+// chunk (natural m_pad x n_pad and transposed n_pad x m_pad, bf16 on entry).
+struct XcastParams {
+  void* Xn;                // natural layout, matrix 0 of the chunk
+  void* Xt;                // transposed layout
+  int64_t x_stride;        // elements between matrices (both buffers)
+  int64_t elems;           // m_pad * n_pad (a multiple of 8)
+  const float* inv_norm;   // [nmat]
+  float sx;
+};
+hipError_t launch_xcast(const XcastParams& p, int nmat, hipStream_t s);
+
+// W <- decay W - step O with O = X_N / sx read from the natural-layout
+// buffer (m_pad x n_pad, fp16); O_out receives O when non-null.
+struct WupdParams {
+  const MatPtrs* table;
+  const void* X;           // natural layout of X_N, matrix 0 of the chunk
+  int64_t x_stride;
+  int m, n, n_pad;
+  float inv_sx, decay, step;
+};
+hipError_t launch_wupd(const WupdParams& p, int nmat, int vec, hipStream_t s);
 
 enum RowNormPhase : int { RN_PHASE_ROWS = 0, RN_PHASE_COLSUM = 1, RN_PHASE_COLFINAL = 2, RN_PHASE_COLAPPLY = 3 };
 hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int vec, int phase,

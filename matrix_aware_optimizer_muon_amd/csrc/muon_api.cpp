@@ -42,6 +42,10 @@ constexpr int kRing = 4;                      // pinned descriptor staging slots
 // [-2.81, 0], of H = P G in [0, 5.0], of Q = P_k...P_1 in [0, a^N]; entries
 // are bounded by the largest eigenvalue in magnitude.
 constexpr float kSG = 16384.0f, kSP = 16384.0f, kSH = 8192.0f, kSQ = 64.0f;
+// Direct form: X kept as fp16 scaled by kSX.  X0 = U / ||U||_F has entries of
+// RMS 1/sqrt(r c); every later X has spectral norm <= 1.2025, which bounds
+// its entries (x kSX <= 308).
+constexpr float kSX = 256.0f;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -56,6 +60,7 @@ struct Bucket {
   int64_t m_pad, n_pad;  // padded natural shape (m_pad x n_pad)
   bool transposed;
   bool dma;  // 256-tile direct-to-LDS path with fp16-only r x r buffers
+  bool direct;  // direct form (eq. (2) on X)
   int bt;
   int first, count;  // range in plan order
   std::vector<Chunk> chunks;
@@ -82,6 +87,7 @@ struct muon_plan_s {
   int64_t nmat = 0;
   muon_dtype grad_dtype = MUON_F32;
   muon_dtype ns_dtype = MUON_BF16;
+  int formulation = MUON_FORM_GRAM;  // resolved: GRAM or DIRECT
   muon_hparams hp{};
   std::vector<int64_t> rows, cols;
   std::vector<int> order;  // plan position -> caller index
@@ -287,6 +293,10 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
   if (desc->grad_dtype != MUON_F32 && desc->grad_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
   if (desc->ns_dtype != MUON_F32 && desc->ns_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
   if (desc->max_workspace_bytes < 0) return MUON_ERR_INVALID_ARGUMENT;
+  const int form = (int)desc->formulation;
+  if (form != MUON_FORM_AUTO && form != MUON_FORM_GRAM && form != MUON_FORM_DIRECT)
+    return MUON_ERR_INVALID_ARGUMENT;
+  if (form == MUON_FORM_DIRECT && desc->ns_dtype == MUON_F32) return MUON_ERR_UNSUPPORTED;
   muon_status st = validate_hp(desc->hp);
   if (st != MUON_OK) return st;
   for (int64_t i = 0; i < desc->num_matrices; ++i) {
@@ -304,6 +314,9 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
     p->rows.assign(desc->rows, desc->rows + desc->num_matrices);
     p->cols.assign(desc->cols, desc->cols + desc->num_matrices);
     const bool f32path = desc->ns_dtype == MUON_F32;
+    // AUTO: the Gram form never needs more flops (3 r^2 c + 17 r^3 against
+    // 15 r^2 c + 5 r^3 for c >= r)
+    p->formulation = form == MUON_FORM_DIRECT ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
     const int64_t cap = desc->max_workspace_bytes > 0 ? desc->max_workspace_bytes : kDefaultCap;
 
     // buckets in order of first appearance
@@ -327,7 +340,8 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       B.transposed = B.m > B.n;
       B.r = std::min(B.m, B.n);
       B.c = std::max(B.m, B.n);
-      B.bt = choose_tile(B.r, (int64_t)members[b].size(), f32path);
+      B.direct = p->formulation == MUON_FORM_DIRECT;
+      B.bt = B.direct ? 256 : choose_tile(B.r, (int64_t)members[b].size(), f32path);
       B.r_pad = round_up(B.r, B.bt);
       B.c_pad = round_up(B.c, B.bt);
       B.first = (int)p->order.size();
@@ -343,7 +357,9 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
           f32path ? 5 * (int64_t)align256((size_t)(rr * 4))
                   : (B.dma ? 0 : 4 * (int64_t)align256((size_t)(rr * 4))) +
                         5 * (int64_t)align256((size_t)(rr * 2));
-      B.scratch_per_mat = 2 * (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes)) + rr_bytes;
+      const int64_t xb = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes));
+      // direct form: X and X^T twice (double buffered) plus A and P~ in fp16
+      B.scratch_per_mat = B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) : 2 * xb + rr_bytes;
       int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
       per_chunk = std::min<int64_t>(per_chunk, B.count);
       const int64_t nchunks = (B.count + per_chunk - 1) / per_chunk;
@@ -459,9 +475,16 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       }
       void* Gh;
       void* Ph;
-      void* Qh[2];
-      void* Hh;
-      if (f32path) {
+      void* Qh[2] = {nullptr, nullptr};
+      void* Hh = nullptr;
+      void* Xn2 = nullptr;
+      void* Xt2 = nullptr;
+      if (B.direct) {
+        Xn2 = take(xbytes);
+        Xt2 = take(xbytes);
+        Gh = take(h16b);
+        Ph = take(h16b);
+      } else if (f32path) {
         Gh = Gf;
         Ph = take(f32b);
         Qh[0] = Qf[0];
@@ -553,6 +576,89 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         g.tiles_per_prod = ntri;
         g.products = products;
       };
+
+      if (B.direct) {
+        // X0 = U / ||U||, in place, as fp16 scaled by kSX
+        XcastParams xc{};
+        xc.Xn = Xnat;
+        xc.Xt = Xtr;
+        xc.x_stride = x_stride;
+        xc.elems = B.m_pad * B.n_pad;
+        xc.inv_norm = d_inv + ch.first;
+        xc.sx = kSX;
+        st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
+                   [&] { return launch_xcast(xc, nm, stream); });
+        if (st != MUON_OK) return st;
+        void* Xn[2] = {Xnat, Xn2};
+        void* Xt[2] = {Xtr, Xt2};
+        g.xkind = 1;
+        g.syrk_scale = 1.0f / (kSX * kSX);
+        g.sX = kSX;
+        g.first = g.last = 0;
+        const int tm = (int)(B.r_pad / 256), tn = (int)(B.c_pad / 256);
+        for (int k = 0; k < N; ++k) {
+          const int cur = k & 1, nx = cur ^ 1;
+          void* Xk = B.transposed ? Xt[cur] : Xn[cur];    // r_pad x c_pad
+          void* XTk = B.transposed ? Xn[cur] : Xt[cur];   // c_pad x r_pad
+          // A = X X^T (lower tiles, mirrored)
+          g.A = g.B = g.B2 = Xk;
+          g.a_stride = g.b_stride = g.b2_stride = x_stride;
+          g.lda = g.ldb = (int)B.c_pad;
+          g.Mdim = g.Ndim = (int)B.r_pad;
+          g.Kdim = (int)B.c_pad;
+          g.tiles_m = g.tiles_n = T;
+          g.triangular = 1;
+          g.tiles_per_prod = ntri;
+          g.products = 1;
+          st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (2.0 * rcf + 2.0 * r2) * nm,
+                     [&] { return gemm(g, EPI_SYRK); });
+          if (st != MUON_OK) return st;
+          // P~ = b A + c A^2
+          rr_setup(Gh, Gh, Gh, 1);
+          st = timed(p, stream, MUON_K_POLY, r3 * nm, 4.0 * r2 * nm, [&] { return gemm(g, EPI_POLY); });
+          if (st != MUON_OK) return st;
+          // X' = a X + P~ X, written in both layouts
+          GemmParams xg = g;
+          xg.A = Ph;
+          xg.a_stride = h_stride;
+          xg.lda = (int)B.r_pad;
+          xg.B = xg.B2 = XTk;
+          xg.b_stride = xg.b2_stride = x_stride;
+          xg.ldb = (int)B.r_pad;
+          xg.Mdim = (int)B.r_pad;
+          xg.Ndim = (int)B.c_pad;
+          xg.Kdim = (int)B.r_pad;
+          xg.tiles_m = tm;
+          xg.tiles_n = tn;
+          xg.triangular = 0;
+          xg.tiles_per_prod = tm * tn;
+          xg.products = 1;
+          xg.Yn = B.transposed ? Xt[nx] : Xn[nx];
+          xg.Yt = B.transposed ? Xn[nx] : Xt[nx];
+          xg.ldyn = (int)B.c_pad;
+          xg.ldyt = (int)B.r_pad;
+          xg.y_stride = x_stride;
+          st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + 6.0 * rcf) * nm,
+                     [&] { return gemm(xg, EPI_XUPD); });
+          if (st != MUON_OK) return st;
+        }
+        // W <- (1 - lr wd) W - lr s O^-1(X_N): the natural-layout buffer of
+        // the last pair holds O^-1(X_N) in W's layout
+        WupdParams wp{};
+        wp.table = d_table + ch.first;
+        wp.X = Xn[N & 1];
+        wp.x_stride = x_stride;
+        wp.m = (int)B.m;
+        wp.n = (int)B.n;
+        wp.n_pad = (int)B.n_pad;
+        wp.inv_sx = 1.0f / kSX;
+        wp.decay = (float)(1.0 - (double)lr * wd);
+        wp.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
+        st = timed(p, stream, MUON_K_WUPD, 0.0, 10.0 * (double)B.m * B.n * nm,
+                   [&] { return launch_wupd(wp, nm, vec, stream); });
+        if (st != MUON_OK) return st;
+        continue;
+      }
 
       // G0 = X0 X0^T / ||U||^2
       g.A = g.B = g.B2 = X;

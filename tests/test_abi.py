@@ -119,3 +119,34 @@ def test_workspace_size_query_matches_plan():
     n = ctypes.c_size_t()
     assert L.load().muon_plan_workspace_size(p._handle, ctypes.byref(n)) == L.MUON_OK
     assert n.value == p.workspace_bytes > 0
+
+
+def test_formulation_choice_and_validation():
+    # AUTO and GRAM plan the same Gram-space workspace; DIRECT keeps X and
+    # X^T twice plus two r x r buffers, all on 256-wide tiles.
+    shapes = [(1024, 1024), (600, 1000), (1000, 600)]
+    auto = L.Plan(shapes, formulation="auto")
+    gram = L.Plan(shapes, formulation="gram")
+    direct = L.Plan(shapes, formulation="direct")
+    assert auto.workspace_bytes == gram.workspace_bytes
+    assert direct.info() == gram.info() == (3, 3)
+    r_pad = {(1024, 1024): 1024, (600, 1000): 768, (1000, 600): 768}
+    c_pad = {(1024, 1024): 1024, (600, 1000): 1024, (1000, 600): 1024}
+    per_mat = [4 * r_pad[s] * c_pad[s] * 2 + 2 * r_pad[s] ** 2 * 2 for s in shapes]
+    assert direct.workspace_bytes >= max(per_mat)
+    # unknown formulation; direct form on the fp32 path
+    assert plan_status([(64, 64)], formulation=3) == L.MUON_ERR_INVALID_ARGUMENT
+    assert plan_status([(64, 64)], formulation=-1) == L.MUON_ERR_INVALID_ARGUMENT
+    with pytest.raises(L.MuonError) as e:
+        L.Plan([(64, 64)], "f32", "f32", formulation="direct")
+    assert e.value.status == L.MUON_ERR_UNSUPPORTED
+    L.Plan([(64, 64)], "f32", "f32", formulation="gram")
+
+
+def test_kernel_class_enum_matches_binding():
+    text = open(HEADER).read()
+    names = re.findall(r"MUON_K_(\w+)\s*=\s*(\d+)", text)
+    classes = {n.lower(): int(v) for n, v in names if n != "COUNT"}
+    count = int(dict(names)["COUNT"])
+    assert count == len(L.KERNEL_CLASSES)
+    assert [k for k, _ in sorted(classes.items(), key=lambda kv: kv[1])] == list(L.KERNEL_CLASSES)

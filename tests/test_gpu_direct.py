@@ -1,0 +1,74 @@
+"""GPU parity of the direct formulation (MUON_FORM_DIRECT: eq. (2) of
+"Infra Optimizers" iterated on X itself, N times A = X X^T, P~ = b A + c A^2,
+X <- a X + P~ X) against the float64 oracle's direct routine, through the C
+ABI.  Same bars as the Gram path on the bf16-MFMA path: NS output <= 2e-2
+relative Frobenius, the update epilogue <= 1e-5 against the oracle's update
+applied to the GPU's own output, momentum <= 1e-6."""
+import numpy as np
+import pytest
+
+from matrix_aware_optimizer_muon_amd.workloads import bf16_round
+from oracle import muon_oracle as OR
+from tests.gpu_common import rel, run
+from tests.test_gpu_parity import LR, WD, check_ns, seeded
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import matrix_aware_optimizer_muon_amd as pkg
+    pkg.load()
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (5, 3), (3, 5), (200, 200), (256, 256), (130, 70),
+                                   (515, 129), (129, 515), (1024, 1024), (600, 1000), (1000, 600)])
+def test_direct_shapes(shape):
+    W, M, G = seeded([shape], 7 + shape[0] * 3 + shape[1], mscale=1e-3)
+    check_ns([shape], W, M, G, "bf16", label=f"direct {shape}", formulation="direct")
+
+
+def test_direct_several_buckets_bf16_grads():
+    shapes = [(256, 256)] * 5 + [(384, 1280), (1280, 384)] * 2 + [(1000, 1000)]
+    W, M, G = seeded(shapes, 11, mscale=1e-3)
+    G = [bf16_round(g) for g in G]
+    check_ns(shapes, W, M, G, "bf16", grad_dtype="bf16", label="direct buckets",
+             formulation="direct")
+
+
+@pytest.mark.parametrize("steps", [1, 2, 5])
+def test_direct_iteration_counts(steps):
+    # odd and even N end in different X buffers of the double-buffered pair
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    hp = default_hparams()
+    hp.ns_steps = steps
+    shapes = [(300, 700), (700, 300)]
+    W, M, G = seeded(shapes, 20 + steps, mscale=1e-3)
+    (Wg, Mg, Og), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", hp=hp, formulation="direct")
+    ohp = OR.Hyper(ns_steps=steps)
+    for i, (m, n) in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=ohp, form="direct")
+        assert rel(Og[i], Oo) <= 2e-2, (steps, i, rel(Og[i], Oo))
+        assert rel(Mg[i], Mo) <= 1e-6
+
+
+def test_direct_is_deterministic_and_close_to_gram():
+    shapes = [(512, 512), (768, 1536)]
+    W, M, G = seeded(shapes, 31, mscale=1e-3)
+    (W1, _, O1), _ = run(shapes, W, M, G, LR, WD, formulation="direct")
+    (W2, _, O2), _ = run(shapes, W, M, G, LR, WD, formulation="direct")
+    (_, _, Og), _ = run(shapes, W, M, G, LR, WD, formulation="gram")
+    for i in range(len(shapes)):
+        assert np.array_equal(W1[i], W2[i]) and np.array_equal(O1[i], O2[i])
+        # both formulations are within 2e-2 of the same exact result
+        assert rel(O1[i], Og[i]) <= 4e-2
+
+
+def test_direct_full_size_square_pair():
+    # two 3584^2 matrices (the q / o projections of the Qwen2.5-7B layer)
+    shapes = [(3584, 3584)] * 2
+    W, M, G = seeded(shapes, 41)
+    check_ns(shapes, W, M, G, "bf16", label="direct 3584^2", formulation="direct")
