@@ -27,17 +27,21 @@ METRIC = "Muon step ms + achieved MFMA TFLOP/s on Qwen2.5-7B-shaped matrix set"
 PEAK_MFMA_16BIT = 2500.0   # TFLOP/s, MI355X dense bf16 / fp16
 PEAK_MFMA_F32 = 157.3      # TFLOP/s, MI355X dense fp32 matrix
 PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
-GEMM_CLASSES = ("syrk", "poly", "pqpg", "ph", "final")
+GEMM_CLASSES = ("syrk", "poly", "pqpg", "ph", "final", "xupd")
 
 
-def ns_flops(shapes) -> float:
-    """Algorithmic flops of the Gram-space step as this library evaluates it:
-    SYRK r^2 c + (17 r x r products of r^3 each for N = 5) + final 2 r^2 c,
-    symmetric products counted on the lower triangle."""
+def ns_flops(shapes, formulation: str = "gram") -> float:
+    """Algorithmic flops of one step as this library evaluates it, symmetric
+    products counted on the lower triangle.  Gram form: SYRK r^2 c + 17 r x r
+    products of r^3 (N = 5) + final 2 r^2 c.  Direct form: per iteration SYRK
+    r^2 c + A^2 r^3 + X update 2 r^2 c."""
     tot = 0.0
     for m, n in shapes:
         r, c = min(m, n), max(m, n)
-        tot += 3.0 * r * r * c + 17.0 * r ** 3
+        if formulation == "direct":
+            tot += 15.0 * r * r * c + 5.0 * r ** 3
+        else:
+            tot += 3.0 * r * r * c + 17.0 * r ** 3
     return tot
 
 
@@ -49,7 +53,7 @@ def make_device_inputs(w, dev, torch):
     return W, M, G
 
 
-def cpu_baseline(w, sample_shapes_max: int = 3):
+def cpu_baseline(w, form: str = "gram", sample_shapes_max: int = 3):
     """Time the float64 oracle on one matrix per distinct shape (largest
     first, at most `sample_shapes_max` shapes, ~10-30 s of CPU work) and
     extrapolate to the whole matrix set by count."""
@@ -78,7 +82,7 @@ def cpu_baseline(w, sample_shapes_max: int = 3):
         per_shape[(r, c)] = time.perf_counter() - t0
     covered = sum(counts[k] for k in keys)
     total_s = sum(per_shape[k] * counts[k] for k in keys)
-    covered_flops = sum(ns_flops([k]) * counts[k] for k in keys)
+    covered_flops = sum(ns_flops([k], form) * counts[k] for k in keys)
     sample = ", ".join(f"{c}x{r} ({per_shape[(r, c)]:.1f} s)" for r, c in keys)
     return {
         "value": covered_flops / total_s / 1e12,
@@ -99,6 +103,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = Qwen2.5-7B, 28 layers)")
+    ap.add_argument("--formulation", choices=("auto", "gram", "direct"), default="auto",
+                    help="Newton-Schulz evaluation (auto = gram: never more flops)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch event timing")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -128,7 +134,11 @@ def main():
     dev = torch.device("cuda:0")
     lib_path = pkg.load()._name
     W, M, G = make_device_inputs(w, dev, torch)
-    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype)
+    form = "direct" if args.formulation == "direct" else "gram"
+    if form == "direct" and w.ns_dtype != "bf16":
+        print("the direct form runs on the 16-bit path only", file=sys.stderr)
+        sys.exit(2)
+    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype, formulation=form)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -175,7 +185,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     refresh_ms = [m for m, k in zip(step_ms, kinds) if k == "refresh"]
     rownorm_ms = [m for m, k in zip(step_ms, kinds) if k == "rownorm"]
-    F = ns_flops(w.shapes)
+    F = ns_flops(w.shapes, form)
     n_refresh = len(refresh_ms)
     value = F * n_refresh / (wall) / 1e12 if n_refresh else 0.0
 
@@ -225,7 +235,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian W, G; random init, no checkpoints)",
-        "config": {"workload": w.name, "matrices": len(w.shapes), "params": w.numel(),
+        "config": {"workload": w.name, "formulation": form, "matrices": len(w.shapes), "params": w.numel(),
                    "grad_dtype": w.grad_dtype, "ns_dtype": w.ns_dtype,
                    "refresh_period": K, "algorithmic_tflop_per_refresh": round(F / 1e12, 4)},
         "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
@@ -239,7 +249,7 @@ def main():
         out["rownorm_ms"] = round(sum(rownorm_ms) / len(rownorm_ms), 4)
         out["cycle_ms"] = round(out["refresh_ms"] + (K - 1) * out["rownorm_ms"], 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, form)
     print(json.dumps(out), flush=True)
 
 

@@ -20,7 +20,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/gemm_epilogue.hpp",
                   "csrc/elementwise.hip", "csrc/common.hpp", "csrc/kernels.h")
-EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final"}
+EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final", 5: "xupd"}
 
 
 def source_hash() -> str:
@@ -37,7 +37,8 @@ def kernel_class(name: str) -> str | None:
         r"gemm_kernel<(\d+), \d+, (\d+)", name)
     if m:
         return EPI_CLASS[int(m.group(2))]
-    for key, cls in (("prep_tile_kernel", "prep"), ("norm_finalize", "norm"),
+    for key, cls in (("xcast_kernel", "xcast"), ("wupd_kernel", "wupd"),
+                     ("prep_tile_kernel", "prep"), ("norm_finalize", "norm"),
                      ("rownorm_rows", "rownorm"), ("rownorm_colsum", "colsum"),
                      ("rownorm_colfinal", "colfinal"), ("rownorm_colapply", "colapply")):
         if key in name:
