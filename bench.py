@@ -30,15 +30,16 @@ PEAK_HBM = 8000.0          # GB/s, MI355X HBM3E
 GEMM_CLASSES = ("syrk", "poly", "pqpg", "ph", "final", "xupd")
 
 
-def ns_flops(shapes, formulation: str = "gram") -> float:
+def ns_flops(shapes, formulation: str = "auto") -> float:
     """Algorithmic flops of one step as this library evaluates it, symmetric
     products counted on the lower triangle.  Gram form: SYRK r^2 c + 17 r x r
     products of r^3 (N = 5) + final 2 r^2 c.  Direct form: per iteration SYRK
-    r^2 c + A^2 r^3 + X update 2 r^2 c."""
+    r^2 c + A^2 r^3 + X update 2 r^2 c.  "auto" takes the direct form for
+    squares (where both count 20 r^3)."""
     tot = 0.0
     for m, n in shapes:
         r, c = min(m, n), max(m, n)
-        if formulation == "direct":
+        if formulation == "direct" or (formulation == "auto" and m == n):
             tot += 15.0 * r * r * c + 5.0 * r ** 3
         else:
             tot += 3.0 * r * r * c + 17.0 * r ** 3
@@ -53,7 +54,7 @@ def make_device_inputs(w, dev, torch):
     return W, M, G
 
 
-def cpu_baseline(w, form: str = "gram", sample_shapes_max: int = 3):
+def cpu_baseline(w, form: str = "auto", sample_shapes_max: int = 3):
     """Time the float64 oracle on one matrix per distinct shape (largest
     first, at most `sample_shapes_max` shapes, ~10-30 s of CPU work) and
     extrapolate to the whole matrix set by count."""
@@ -104,7 +105,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = Qwen2.5-7B, 28 layers)")
     ap.add_argument("--formulation", choices=("auto", "gram", "direct"), default="auto",
-                    help="Newton-Schulz evaluation (auto = gram: never more flops)")
+                    help="Newton-Schulz evaluation (auto: direct for square matrices, else gram)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch event timing")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -134,10 +135,12 @@ def main():
     dev = torch.device("cuda:0")
     lib_path = pkg.load()._name
     W, M, G = make_device_inputs(w, dev, torch)
-    form = "direct" if args.formulation == "direct" else "gram"
+    form = args.formulation
     if form == "direct" and w.ns_dtype != "bf16":
         print("the direct form runs on the 16-bit path only", file=sys.stderr)
         sys.exit(2)
+    if form == "auto" and w.ns_dtype != "bf16":
+        form = "gram"
     plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype, formulation=form)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)

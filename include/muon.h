@@ -74,8 +74,10 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     flops.  16-bit path only (ns_dtype MUON_BF16): X is
  *                     kept as scaled fp16 in both layouts; every product
  *                     uses 256-wide tiles.
- *   MUON_FORM_AUTO:   the cheaper of the two by flop count, which is the
- *                     Gram form for every shape (c >= r; equal cost at c = r). */
+ *   MUON_FORM_AUTO:   per bucket: the direct form for square matrices on
+ *                     the 16-bit path (equal flops, 20 r^3, in fewer and
+ *                     larger products), the Gram form otherwise (fewer flops
+ *                     whenever c > r). */
 typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } muon_formulation;
 
 /* Hyper-parameters fixed at plan time.  muon_default_hparams fills the

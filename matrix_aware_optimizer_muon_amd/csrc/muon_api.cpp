@@ -87,7 +87,7 @@ struct muon_plan_s {
   int64_t nmat = 0;
   muon_dtype grad_dtype = MUON_F32;
   muon_dtype ns_dtype = MUON_BF16;
-  int formulation = MUON_FORM_GRAM;  // resolved: GRAM or DIRECT
+  int formulation = MUON_FORM_AUTO;  // as requested; resolved per bucket
   muon_hparams hp{};
   std::vector<int64_t> rows, cols;
   std::vector<int> order;  // plan position -> caller index
@@ -314,9 +314,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
     p->rows.assign(desc->rows, desc->rows + desc->num_matrices);
     p->cols.assign(desc->cols, desc->cols + desc->num_matrices);
     const bool f32path = desc->ns_dtype == MUON_F32;
-    // AUTO: the Gram form never needs more flops (3 r^2 c + 17 r^3 against
-    // 15 r^2 c + 5 r^3 for c >= r)
-    p->formulation = form == MUON_FORM_DIRECT ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
+    p->formulation = form;
     const int64_t cap = desc->max_workspace_bytes > 0 ? desc->max_workspace_bytes : kDefaultCap;
 
     // buckets in order of first appearance
@@ -340,7 +338,12 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       B.transposed = B.m > B.n;
       B.r = std::min(B.m, B.n);
       B.c = std::max(B.m, B.n);
-      B.direct = p->formulation == MUON_FORM_DIRECT;
+      // AUTO: the direct form for square matrices on the 16-bit path (the
+      // same 20 r^3 flops as the Gram form, in fewer and larger products:
+      // measured 2-10 % faster, 3.6x on 64 x 512^2), the Gram form otherwise
+      // (3 r^2 c + 17 r^3 against 15 r^2 c + 5 r^3 flops for c > r)
+      B.direct = p->formulation == MUON_FORM_DIRECT ||
+                 (p->formulation == MUON_FORM_AUTO && !f32path && B.m == B.n);
       B.bt = B.direct ? 256 : choose_tile(B.r, (int64_t)members[b].size(), f32path);
       B.r_pad = round_up(B.r, B.bt);
       B.c_pad = round_up(B.c, B.bt);

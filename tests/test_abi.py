@@ -122,13 +122,21 @@ def test_workspace_size_query_matches_plan():
 
 
 def test_formulation_choice_and_validation():
-    # AUTO and GRAM plan the same Gram-space workspace; DIRECT keeps X and
-    # X^T twice plus two r x r buffers, all on 256-wide tiles.
+    # AUTO plans the Gram form for non-square buckets and the direct form for
+    # squares; DIRECT keeps X and X^T twice plus two r x r buffers, all on
+    # 256-wide tiles.
+    rect = [(600, 1000), (1000, 600)]
+    assert L.Plan(rect, formulation="auto").workspace_bytes == \
+        L.Plan(rect, formulation="gram").workspace_bytes
+    sq = [(1024, 1024)] * 2
+    assert L.Plan(sq, formulation="auto").workspace_bytes == \
+        L.Plan(sq, formulation="direct").workspace_bytes != L.Plan(sq, formulation="gram").workspace_bytes
+    # on the fp32 path AUTO stays with the Gram form
+    assert L.Plan(sq, "f32", "f32", formulation="auto").workspace_bytes == \
+        L.Plan(sq, "f32", "f32", formulation="gram").workspace_bytes
     shapes = [(1024, 1024), (600, 1000), (1000, 600)]
-    auto = L.Plan(shapes, formulation="auto")
     gram = L.Plan(shapes, formulation="gram")
     direct = L.Plan(shapes, formulation="direct")
-    assert auto.workspace_bytes == gram.workspace_bytes
     assert direct.info() == gram.info() == (3, 3)
     r_pad = {(1024, 1024): 1024, (600, 1000): 768, (1000, 600): 768}
     c_pad = {(1024, 1024): 1024, (600, 1000): 1024, (1000, 600): 1024}

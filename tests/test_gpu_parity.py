@@ -262,3 +262,10 @@ def test_qwen_layer_full_size(idx):
     assert e <= 2e-2
     assert rel(Mg[idx], Mo) <= 1e-6
     assert rel(Wg[idx], OR.apply_update(W[idx], Og[idx], w.lr, w.wd, OR.update_scale(m, nn))) <= 1e-5
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (200, 200), (256, 256), (1024, 1024)])
+def test_gram_form_on_squares(shape):
+    # AUTO takes the direct form for squares; the Gram form stays available
+    W, M, G = seeded([shape], 3 + shape[0], mscale=1e-3)
+    check_ns([shape], W, M, G, "bf16", label=f"gram {shape}", formulation="gram")
