@@ -152,6 +152,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   constexpr int DPS = 2 * DMA_PER_OP;            // per wave per stage (vmcnt units)
   constexpr int NMF = FM * FN;                   // MFMAs per half stage
   static_assert(NMF == 2 * DPS, "two MFMAs per DMA instruction");
+  static_assert((FM - 1) * FN >= DPS, "first-half MFMAs carry DPS / 2 DMA instructions");
   constexpr int RR = 128;
   constexpr int SMEM_OPS = DSTAGES * STAGEB;
   constexpr int SMEM_EPI = RR * DT * 4;
@@ -243,12 +244,21 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   if constexpr (HARVEST) gam = rr_gamma<EPI>(p);
   const int hk0 = row0A / DBK + wm * 4;
 
-  // prologue: stages 0..3 in flight, wait for stage 0
+  // Refill schedule: the DMAs of a stage go out in two halves, so that
+  // every MFMA run of an iteration carries the same share of them.  Stage
+  // kt+4's first DPS/2 instructions (A blocks) are issued in the second half
+  // of iteration kt, into the buffer released by that iteration's barrier;
+  // its other DPS/2 (B blocks) in the first half of iteration kt+1.  Issued
+  // all at once, the 8 waves' refills queued at the CU's address unit and
+  // held up the MFMAs behind them in each wave.
+  // prologue: stages 0..2 and the first half of stage 3 in flight, wait for
+  // stage 0
 #pragma unroll
   for (int st = 0; st < DSTAGES; ++st)
 #pragma unroll
-    for (int q = 0; q < DPS; ++q) dma(q, st, st);
-  __builtin_amdgcn_s_waitcnt(wait_imm(3 * DPS, 15));
+    for (int q = 0; q < DPS; ++q)
+      if (st < DSTAGES - 1 || q < DPS / 2) dma(q, st, st);
+  __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS + DPS / 2, 15));
   barrier();
 #pragma unroll
   for (int f = 0; f < FM; ++f) fa0[f] = *(const u32x4*)(smem + offA[0][f]);
@@ -279,13 +289,21 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the rest of the first half, with the second half of stage kt+3's DMAs
+    // (its buffer was released at the previous iteration's barrier): one
+    // DMA instruction after every two MFMAs
 #pragma unroll
-    for (int i = 1; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) mfma<KIND>(fa0[i], fb0[j], acc[i][j]);
+    for (int n = 0; n < (FM - 1) * FN; ++n) {
+      mfma<KIND>(fa0[1 + n / FN], fb0[n % FN], acc[1 + n / FN][n % FN]);
+      if (n % 2 == 1 && n / 2 < DPS / 2) {
+        dma(DPS / 2 + n / 2, (kt + DSTAGES - 1) & (DSTAGES - 1), kt + DSTAGES - 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
-    // stage kt+1 landed for this wave (stages kt+2, kt+3 may still fly) and
-    // this wave's reads of stage kt are done; then publish / retire
+    // stage kt+1 landed for this wave (the later DMAs, 2 * DPS of them, may
+    // still fly) and this wave's reads of stage kt are done; then publish /
+    // retire
     __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 0));
     if (HARVEST && (unsigned)hs < 4u) {
 #pragma unroll
@@ -315,14 +333,14 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       for (int f = 0; f < FN; ++f) fb0[f] = *(const u32x4*)(sn + offB[0][f]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // second half, with the refill of this stage's buffer (stage kt+4)
-    // interleaved: two MFMAs per DMA instruction
+    // second half, with the first half of the refill of this stage's buffer
+    // (stage kt+4): one DMA instruction after every four MFMAs
 #pragma unroll
     for (int g = 0; g < DPS; ++g) {
       mfma<KIND>(fa1[(2 * g) / FN], fb1[(2 * g) % FN], acc[(2 * g) / FN][(2 * g) % FN]);
       mfma<KIND>(fa1[(2 * g + 1) / FN], fb1[(2 * g + 1) % FN],
                  acc[(2 * g + 1) / FN][(2 * g + 1) % FN]);
-      dma(g, buf, kt + DSTAGES);
+      if (g % 2 == 0) dma(g / 2, buf, kt + DSTAGES);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
