@@ -46,6 +46,12 @@ def ns_flops(shapes, formulation: str = "auto") -> float:
     return tot
 
 
+def plan_flops_per_shape(plan) -> dict:
+    """Algorithmic flops of one matrix of each planned shape (m, n), with the
+    formulation the planner (or a tuning hint) chose for its bucket."""
+    return {tuple(b["shape"]): ns_flops([b["shape"]], b["formulation"]) for b in plan.buckets()}
+
+
 def make_device_inputs(w, dev, torch):
     from matrix_aware_optimizer_muon_amd import workloads as WL
     W = [WL.device_weight(w, i, dev) for i in range(len(w.shapes))]
@@ -54,7 +60,7 @@ def make_device_inputs(w, dev, torch):
     return W, M, G
 
 
-def cpu_baseline(w, form: str = "auto", sample_shapes_max: int = 3):
+def cpu_baseline(w, flops_per_shape: dict, sample_shapes_max: int = 3):
     """Time the float64 oracle on one matrix per distinct shape (largest
     first, at most `sample_shapes_max` shapes, ~10-30 s of CPU work) and
     extrapolate to the whole matrix set by count."""
@@ -83,7 +89,7 @@ def cpu_baseline(w, form: str = "auto", sample_shapes_max: int = 3):
         per_shape[(r, c)] = time.perf_counter() - t0
     covered = sum(counts[k] for k in keys)
     total_s = sum(per_shape[k] * counts[k] for k in keys)
-    covered_flops = sum(ns_flops([k], form) * counts[k] for k in keys)
+    covered_flops = sum(flops_per_shape[tuple(s)] for s in w.shapes if (min(s), max(s)) in per_shape)
     sample = ", ".join(f"{c}x{r} ({per_shape[(r, c)]:.1f} s)" for r, c in keys)
     return {
         "value": covered_flops / total_s / 1e12,
@@ -106,6 +112,11 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="workload 1..5 (4 = Qwen2.5-7B, 28 layers)")
     ap.add_argument("--formulation", choices=("auto", "gram", "direct"), default="auto",
                     help="Newton-Schulz evaluation (auto: direct for square matrices, else gram)")
+    ap.add_argument("--tuned", action="store_true",
+                    help="per-shape tile / formulation from the tuning cache (shapes it lacks "
+                         "are tuned first, on the device)")
+    ap.add_argument("--tune-cache", default=None,
+                    help="tuning cache file (default: the one shipped with the package)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch event timing")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -141,7 +152,15 @@ def main():
         sys.exit(2)
     if form == "auto" and w.ns_dtype != "bf16":
         form = "gram"
-    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype, formulation=form)
+    hints = None
+    if args.tuned:
+        from matrix_aware_optimizer_muon_amd import tune as TU
+        cache = TU.load_cache(args.tune_cache or TU.SHIPPED_CACHE)
+        cache = TU.tune(w.shapes, w.grad_dtype, w.ns_dtype, cache,
+                        log=lambda msg: print("tune: " + msg, file=sys.stderr, flush=True))
+        hints = TU.hints_for(w.shapes, w.grad_dtype, w.ns_dtype, cache)
+        torch.cuda.synchronize()
+    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype, formulation=form, hints=hints)
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -188,7 +207,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     refresh_ms = [m for m, k in zip(step_ms, kinds) if k == "refresh"]
     rownorm_ms = [m for m, k in zip(step_ms, kinds) if k == "rownorm"]
-    F = ns_flops(w.shapes, form)
+    per_shape = plan_flops_per_shape(plan)
+    F = sum(per_shape[tuple(s)] for s in w.shapes)
     n_refresh = len(refresh_ms)
     value = F * n_refresh / (wall) / 1e12 if n_refresh else 0.0
 
@@ -238,7 +258,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.ns_dtype == "bf16" else "f32",
         "data": "synthetic (seeded Gaussian W, G; random init, no checkpoints)",
-        "config": {"workload": w.name, "formulation": form, "matrices": len(w.shapes), "params": w.numel(),
+        "config": {"workload": w.name, "formulation": form, "tuned": bool(args.tuned),
+                   "matrices": len(w.shapes), "params": w.numel(),
                    "grad_dtype": w.grad_dtype, "ns_dtype": w.ns_dtype,
                    "refresh_period": K, "algorithmic_tflop_per_refresh": round(F / 1e12, 4)},
         "step_ms_median": round(sorted(step_ms)[len(step_ms) // 2], 4),
@@ -246,13 +267,15 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "library": os.path.relpath(lib_path, ROOT),
+        "plan": [{"shape": list(b["shape"]), "count": b["count"], "tile": b["tile"],
+                  "formulation": b["formulation"]} for b in plan.buckets()],
     }
     if refresh_ms and rownorm_ms:
         out["refresh_ms"] = round(sum(refresh_ms) / len(refresh_ms), 4)
         out["rownorm_ms"] = round(sum(rownorm_ms) / len(rownorm_ms), 4)
         out["cycle_ms"] = round(out["refresh_ms"] + (K - 1) * out["rownorm_ms"], 4)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, form)
+        out["cpu_baseline"] = cpu_baseline(w, per_shape)
     print(json.dumps(out), flush=True)
 
 

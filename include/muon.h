@@ -80,6 +80,27 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     whenever c > r). */
 typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } muon_formulation;
 
+/* Per-shape override of the planner's choices for one bucket (the matrices
+ * of exactly rows x cols): the shape-adaptive tuning hook.  "DMuon" 2.4
+ * searches tile configurations per target and matrix shape and caches the
+ * winners; 2.3 times every distinct shape at initialisation.  Here a tuner
+ * (tune.py) times the candidate settings of each shape on the device and
+ * passes the winners back through these hints.
+ *   tile:        0 = the planner's rule; 64 or 128 = the small-tile kernels;
+ *                256 = the 256-wide tile kernels (ns_dtype MUON_BF16 only).
+ *   formulation: MUON_FORM_AUTO = the plan-wide setting decides; GRAM or
+ *                DIRECT force the form for this bucket (DIRECT needs
+ *                ns_dtype MUON_BF16 and a tile of 0 or 256).
+ * Hints whose shape matches no planned matrix are ignored.  Two hints for
+ * the same shape, or a tile / formulation outside these values, give
+ * MUON_ERR_INVALID_ARGUMENT; combinations the kernels do not provide give
+ * MUON_ERR_UNSUPPORTED. */
+typedef struct {
+  int64_t rows, cols;
+  int tile;
+  muon_formulation formulation;
+} muon_bucket_hint;
+
 /* Hyper-parameters fixed at plan time.  muon_default_hparams fills the
  * values the pages give: mu = 0.95 and N = 5 ("Infra Optimizers", Scaling Up
  * Muon), a = 3.4445, b = -4.7750, c = 2.0315 (Background, eq. (2)), the 0.2
@@ -108,6 +129,8 @@ typedef struct {
                                   same-shape matrices are split into chunks
                                   that fit; a single matrix always fits.     */
   muon_formulation formulation; /* see above; 0 = MUON_FORM_AUTO            */
+  const muon_bucket_hint* hints; /* nullable host array [num_hints]; copied   */
+  int64_t num_hints;             /* 0 = no hints                              */
 } muon_plan_desc;
 
 /* Fill *hp with the defaults listed above.  Returns MUON_ERR_INVALID_ARGUMENT
@@ -132,6 +155,21 @@ muon_status muon_plan_workspace_size(muon_plan_t plan, size_t* workspace_bytes);
 
 /* Number of same-shape buckets and launch chunks the planner formed. */
 muon_status muon_plan_info(muon_plan_t plan, int64_t* num_buckets, int64_t* num_chunks);
+
+/* What the planner decided for bucket `index` (0 .. num_buckets-1, in order
+ * of first appearance of each shape). */
+typedef struct {
+  int64_t rows, cols;        /* the shape of the bucket's matrices           */
+  int64_t count;             /* matrices in the bucket                       */
+  int64_t chunks;            /* launch chunks (workspace cap)                */
+  int tile;                  /* 64, 128 or 256                               */
+  muon_formulation formulation; /* MUON_FORM_GRAM or MUON_FORM_DIRECT        */
+  int transposed;            /* 1 iff rows > cols (X0 = U^T)                 */
+} muon_bucket_info;
+
+/* Fill *info for one bucket.  MUON_ERR_INVALID_ARGUMENT for a NULL plan or
+ * info, or an index out of range. */
+muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_info* info);
 
 /* Newton-Schulz (refresh) step for every planned matrix (Gram form shown;
  * the direct form evaluates the same X_N by iterating eq. (2) on X):

@@ -24,7 +24,7 @@ MUON_F32 = 0
 MUON_BF16 = 1
 
 EXPORTED = ("muon_default_hparams", "muon_plan", "muon_plan_destroy", "muon_plan_workspace_size",
-            "muon_plan_info", "muon_step_batched", "rownorm_step", "muon_plan_set_profiling",
+            "muon_plan_info", "muon_plan_bucket_info", "muon_step_batched", "rownorm_step", "muon_plan_set_profiling",
             "muon_plan_kernel_times", "muon_status_string")
 KERNEL_CLASSES = ("prep", "norm", "syrk", "poly", "pqpg", "ph", "final", "rownorm", "colsum",
                   "colfinal", "colapply", "xcast", "xupd", "wupd")
@@ -44,11 +44,23 @@ class Hparams(ctypes.Structure):
                 ("rownorm_eps", ctypes.c_float)]
 
 
+class BucketHint(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("tile", ctypes.c_int),
+                ("formulation", ctypes.c_int)]
+
+
+class BucketInfo(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("count", ctypes.c_int64),
+                ("chunks", ctypes.c_int64), ("tile", ctypes.c_int), ("formulation", ctypes.c_int),
+                ("transposed", ctypes.c_int)]
+
+
 class PlanDesc(ctypes.Structure):
     _fields_ = [("num_matrices", ctypes.c_int64), ("rows", ctypes.POINTER(ctypes.c_int64)),
                 ("cols", ctypes.POINTER(ctypes.c_int64)), ("grad_dtype", ctypes.c_int),
                 ("ns_dtype", ctypes.c_int), ("hp", Hparams),
-                ("max_workspace_bytes", ctypes.c_int64), ("formulation", ctypes.c_int)]
+                ("max_workspace_bytes", ctypes.c_int64), ("formulation", ctypes.c_int),
+                ("hints", ctypes.POINTER(BucketHint)), ("num_hints", ctypes.c_int64)]
 
 
 _lib = None
@@ -69,6 +81,7 @@ def load() -> ctypes.CDLL:
     lib.muon_plan_destroy.argtypes = [P]
     lib.muon_plan_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.muon_plan_info.argtypes = [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.muon_plan_bucket_info.argtypes = [P, ctypes.c_int64, ctypes.POINTER(BucketInfo)]
     step_args = [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P), ctypes.c_float,
                  ctypes.c_float, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
     lib.muon_step_batched.argtypes = step_args
@@ -79,7 +92,8 @@ def load() -> ctypes.CDLL:
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     for name in ("muon_default_hparams", "muon_plan", "muon_plan_destroy",
-                 "muon_plan_workspace_size", "muon_plan_info", "muon_step_batched",
+                 "muon_plan_workspace_size", "muon_plan_info", "muon_plan_bucket_info",
+                 "muon_step_batched",
                  "rownorm_step", "muon_plan_set_profiling", "muon_plan_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -109,11 +123,13 @@ class Plan:
     """A planned set of matrices (muon_plan).  `shapes` is a list of (m, n).
 
     grad_dtype / ns_dtype are "f32" or "bf16"; formulation is "auto", "gram"
-    or "direct" (or the muon_formulation value)."""
+    or "direct" (or the muon_formulation value).  `hints` maps a shape (m, n)
+    to {"tile": 0|64|128|256, "formulation": "auto"|"gram"|"direct"}
+    (muon_bucket_hint)."""
 
     def __init__(self, shapes: Sequence[tuple], grad_dtype: str = "f32", ns_dtype: str = "bf16",
                  hp: Optional[Hparams] = None, max_workspace_bytes: int = 0,
-                 formulation: str = "auto"):
+                 formulation: str = "auto", hints: Optional[dict] = None):
         lib = load()
         self._lib = lib
         self.shapes = [(int(m), int(n)) for m, n in shapes]
@@ -129,6 +145,14 @@ class Plan:
         desc.hp = hp if hp is not None else default_hparams()
         desc.max_workspace_bytes = int(max_workspace_bytes)
         desc.formulation = FORMULATIONS[formulation] if isinstance(formulation, str) else int(formulation)
+        items = list((hints or {}).items())
+        harr = (BucketHint * max(len(items), 1))()
+        for i, ((m, n), h) in enumerate(items):
+            f = h.get("formulation", "auto")
+            harr[i] = BucketHint(int(m), int(n), int(h.get("tile", 0)),
+                                 FORMULATIONS[f] if isinstance(f, str) else int(f))
+        desc.hints = ctypes.cast(harr, ctypes.POINTER(BucketHint)) if items else None
+        desc.num_hints = len(items)
         self.hp = desc.hp
         self.grad_dtype, self.ns_dtype = grad_dtype, ns_dtype
         handle = ctypes.c_void_p()
@@ -145,6 +169,20 @@ class Plan:
         if st != MUON_OK:
             raise MuonError(st, "muon_plan_info")
         return int(nb.value), int(nc.value)
+
+    def buckets(self) -> list:
+        """The planner's decision per bucket (muon_plan_bucket_info)."""
+        names = {v: k for k, v in FORMULATIONS.items()}
+        out = []
+        for i in range(self.info()[0]):
+            b = BucketInfo()
+            st = self._lib.muon_plan_bucket_info(self._handle, i, ctypes.byref(b))
+            if st != MUON_OK:
+                raise MuonError(st, "muon_plan_bucket_info")
+            out.append({"shape": (int(b.rows), int(b.cols)), "count": int(b.count),
+                        "chunks": int(b.chunks), "tile": int(b.tile),
+                        "formulation": names[int(b.formulation)], "transposed": bool(b.transposed)})
+        return out
 
     def _call(self, fn, name, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream, out):
         n = len(self.shapes)

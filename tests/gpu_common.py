@@ -23,12 +23,12 @@ def to_dev(x, dtype="f32"):
 
 
 def run(shapes, W, M, G, lr, wd, grad_dtype="f32", ns_dtype="bf16", hp=None, rownorm=False,
-        max_ws=0, want_out=True, plan=None, steps_grads=None, formulation="auto"):
+        max_ws=0, want_out=True, plan=None, steps_grads=None, formulation="auto", hints=None):
     """One call of muon_step_batched (or rownorm_step) on fresh device copies.
     Returns host arrays (W', M', O) and the plan."""
     import torch
     if plan is None:
-        plan = Plan(shapes, grad_dtype, ns_dtype, hp, max_ws, formulation=formulation)
+        plan = Plan(shapes, grad_dtype, ns_dtype, hp, max_ws, formulation=formulation, hints=hints)
     Wd = [to_dev(w) for w in W]
     Md = [to_dev(m) for m in M]
     Gd = [to_dev(g, grad_dtype) for g in G]

@@ -158,3 +158,82 @@ def test_kernel_class_enum_matches_binding():
     count = int(dict(names)["COUNT"])
     assert count == len(L.KERNEL_CLASSES)
     assert [k for k, _ in sorted(classes.items(), key=lambda kv: kv[1])] == list(L.KERNEL_CLASSES)
+
+
+def test_bucket_info_reports_the_planner_rule():
+    shapes = [(256, 1024), (1024, 256), (256, 1024), (1024, 1024), (1000, 300), (3584, 18944)]
+    b = L.Plan(shapes).buckets()
+    assert [x["shape"] for x in b] == [(256, 1024), (1024, 256), (1024, 1024), (1000, 300),
+                                       (3584, 18944)]
+    assert [x["count"] for x in b] == [2, 1, 1, 1, 1]
+    assert [x["transposed"] for x in b] == [False, True, False, True, False]
+    # squares take the direct form on the 16-bit path, 256-wide tiles above r = 768
+    assert [x["formulation"] for x in b] == ["gram", "gram", "direct", "gram", "gram"]
+    assert [x["tile"] for x in b] == [64, 64, 256, 64, 256]
+    assert all(x["chunks"] == 1 for x in b)
+    f = L.Plan(shapes, "f32", "f32").buckets()
+    assert all(x["formulation"] == "gram" and x["tile"] in (64, 128) for x in f)
+    lib = L.load()
+    info = L.BucketInfo()
+    plan = L.Plan(shapes)
+    assert lib.muon_plan_bucket_info(plan._handle, 5, ctypes.byref(info)) == L.MUON_ERR_INVALID_ARGUMENT
+    assert lib.muon_plan_bucket_info(plan._handle, -1, ctypes.byref(info)) == L.MUON_ERR_INVALID_ARGUMENT
+    assert lib.muon_plan_bucket_info(plan._handle, 0, None) == L.MUON_ERR_INVALID_ARGUMENT
+    assert lib.muon_plan_bucket_info(None, 0, ctypes.byref(info)) == L.MUON_ERR_INVALID_ARGUMENT
+
+
+def test_bucket_hints_override_tile_and_formulation():
+    shapes = [(3584, 18944), (1024, 1024), (384, 1000), (700, 300)]
+    hints = {(3584, 18944): {"tile": 128}, (1024, 1024): {"formulation": "gram"},
+             (384, 1000): {"tile": 256, "formulation": "gram"},
+             (700, 300): {"formulation": "direct"},
+             (5, 5): {"tile": 64}}                     # matches no matrix: ignored
+    b = {x["shape"]: x for x in L.Plan(shapes, hints=hints).buckets()}
+    assert (b[(3584, 18944)]["tile"], b[(3584, 18944)]["formulation"]) == (128, "gram")
+    assert (b[(1024, 1024)]["tile"], b[(1024, 1024)]["formulation"]) == (256, "gram")
+    assert (b[(384, 1000)]["tile"], b[(384, 1000)]["formulation"]) == (256, "gram")
+    assert (b[(700, 300)]["tile"], b[(700, 300)]["formulation"]) == (256, "direct")
+    # a 128-wide tile on a 3584-row bucket keeps fp32 master copies: more workspace
+    assert L.Plan([(3584, 18944)], hints={(3584, 18944): {"tile": 128}}).workspace_bytes > \
+        L.Plan([(3584, 18944)]).workspace_bytes
+    # the fp32 path takes 64 / 128 tile hints
+    f = L.Plan([(300, 700)], "f32", "f32", hints={(300, 700): {"tile": 128}}).buckets()
+    assert f[0]["tile"] == 128
+
+
+def test_bucket_hints_validation():
+    bad = L.MUON_ERR_INVALID_ARGUMENT
+    assert plan_status([(64, 64)], hints={(64, 64): {"tile": 32}}) == bad
+    assert plan_status([(64, 64)], hints={(64, 64): {"tile": -1}}) == bad
+    assert plan_status([(64, 64)], hints={(64, 64): {"formulation": 3}}) == bad
+    assert plan_status([(64, 64)], hints={(0, 64): {"tile": 64}}) == bad
+    # two hints for one shape
+    lib = L.load()
+    rows = (ctypes.c_int64 * 1)(64)
+    cols = (ctypes.c_int64 * 1)(64)
+    harr = (L.BucketHint * 2)(L.BucketHint(64, 64, 64, 1), L.BucketHint(64, 64, 128, 1))
+    desc = L.PlanDesc()
+    desc.num_matrices = 1
+    desc.rows = ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64))
+    desc.cols = ctypes.cast(cols, ctypes.POINTER(ctypes.c_int64))
+    desc.grad_dtype, desc.ns_dtype = L.MUON_F32, L.MUON_BF16
+    desc.hp = L.default_hparams()
+    desc.hints = ctypes.cast(harr, ctypes.POINTER(L.BucketHint))
+    handle = ctypes.c_void_p()
+    for n, want in ((2, bad), (-1, bad), (1, L.MUON_OK)):
+        desc.num_hints = n
+        st = lib.muon_plan(ctypes.byref(desc), ctypes.byref(handle), None)
+        assert st == want, (n, st)
+        if st == L.MUON_OK:
+            lib.muon_plan_destroy(handle)
+    desc.hints = None
+    desc.num_hints = 1
+    assert lib.muon_plan(ctypes.byref(desc), ctypes.byref(handle), None) == bad
+    # combinations the kernels do not provide
+    uns = L.MUON_ERR_UNSUPPORTED
+    assert plan_status([(64, 64)], grad_dtype="f32", ns_dtype="f32", hints={(64, 64): {"tile": 256}}) == uns
+    assert plan_status([(64, 64)], grad_dtype="f32", ns_dtype="f32",
+                       hints={(64, 64): {"formulation": "direct"}}) == uns
+    assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128}}) == uns   # direct needs 256
+    assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128, "formulation": "gram"}}) == 0
+    assert plan_status([(300, 700)], hints={(300, 700): {"tile": 64, "formulation": "direct"}}) == uns

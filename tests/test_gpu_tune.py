@@ -1,0 +1,63 @@
+"""GPU parity of the settings only per-shape hints reach (muon_bucket_hint:
+small tiles on large 16-bit buckets, 256-wide tiles on small ones, the Gram
+form on squares, the direct form on rectangles), and the tuner end to end.
+Same bars as the other parity tests: NS output <= 2e-2 relative Frobenius on
+the 16-bit path (<= 1e-5 on the weights of the fp32 path), momentum <= 1e-6,
+the update epilogue <= 1e-5 against the oracle applied to the GPU's output."""
+import pytest
+
+from tests.gpu_common import run
+from tests.test_gpu_parity import LR, WD, check_ns, seeded
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import matrix_aware_optimizer_muon_amd as pkg
+    pkg.load()
+
+
+@pytest.mark.parametrize("shape,hint", [
+    ((1024, 1536), {"tile": 128, "formulation": "gram"}),   # default: 256-wide tiles
+    ((1536, 1024), {"tile": 64, "formulation": "gram"}),
+    ((384, 1000), {"tile": 256, "formulation": "gram"}),    # default: small tiles
+    ((1000, 384), {"tile": 256, "formulation": "gram"}),
+    ((700, 300), {"formulation": "direct"}),                # default: Gram form
+    ((1000, 1000), {"tile": 128, "formulation": "gram"}),   # default: direct form
+    ((257, 257), {"tile": 256, "formulation": "gram"}),
+])
+def test_hinted_bucket_parity(shape, hint):
+    shapes = [shape] * 3
+    W, M, G = seeded(shapes, 40 + shape[0] + shape[1], mscale=1e-3)
+    form = "direct" if hint.get("formulation") == "direct" else "gram"
+    (_, _, _), plan = run(shapes, W, M, G, LR, WD, "f32", "bf16", hints={shape: hint}, want_out=False)
+    b = plan.buckets()[0]
+    assert b["tile"] == hint.get("tile", 256) and b["formulation"] == form
+    check_ns(shapes, W, M, G, "bf16", label=f"hint {shape} {hint}", hints={shape: hint})
+
+
+@pytest.mark.parametrize("tile", [64, 128])
+def test_hinted_fp32_path_parity(tile):
+    shapes = [(300, 700), (700, 300)]
+    W, M, G = seeded(shapes, 60 + tile, mscale=1e-3)
+    hints = {s: {"tile": tile} for s in shapes}
+    check_ns(shapes, W, M, G, "f32", label=f"fp32 tile {tile}", hints=hints)
+
+
+def test_tuner_end_to_end():
+    from matrix_aware_optimizer_muon_amd import tune as TU
+    shapes = [(512, 1024)] * 2 + [(640, 640)]
+    cache = TU.tune(shapes, "f32", "bf16", steps=2, warmup=1)
+    dev = TU.device_name()
+    for (m, n), count in TU.shape_counts(shapes).items():
+        e = cache["entries"][TU.cache_key(dev, "f32", "bf16", m, n, count)]
+        assert e["ms"] > 0 and e["ms"] == min(c["ms"] for c in e["candidates"])
+        assert len(e["candidates"]) == len(TU.candidates(m, n, "bf16"))
+    hints = TU.hints_for(shapes, "f32", "bf16", cache)
+    assert set(hints) == {(512, 1024), (640, 640)}
+    W, M, G = seeded(shapes, 77, mscale=1e-3)
+    check_ns(shapes, W, M, G, "bf16", label="tuned", hints=hints)
