@@ -18,8 +18,11 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+# The kernels and the planner (which decides the launches, tiles and forms
+# whose traffic a profile records).
 KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/gemm_epilogue.hpp",
-                  "csrc/elementwise.hip", "csrc/common.hpp", "csrc/kernels.h")
+                  "csrc/elementwise.hip", "csrc/common.hpp", "csrc/kernels.h",
+                  "csrc/muon_api.cpp")
 EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final", 5: "xupd"}
 
 
