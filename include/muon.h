@@ -28,7 +28,13 @@
  *     muon_plan reported, 256-byte aligned.  Its contents between calls are
  *     irrelevant (every call rewrites what it reads).
  *   - Calls enqueue work on `stream` and return without synchronising.
- *     Results are valid once the stream has reached that point.
+ *     Results are valid once the stream has reached that point.  When every
+ *     bucket of a plan is too small to fill the GPU on its own and their
+ *     scratch fits the cap together, muon_step_batched runs the buckets
+ *     concurrently on up to 4 internal streams of the plan (default
+ *     priority, created on the first such call, destroyed with the plan):
+ *     they wait for `stream` on entry and `stream` waits for all of them on
+ *     return, so the call behaves as one operation on `stream`.
  *   - Errors: all validation happens on the host before anything is
  *     enqueued.  On any status other than MUON_OK and MUON_ERR_HIP nothing
  *     was enqueued and no memory was touched.  MUON_ERR_HIP means a HIP

@@ -4,8 +4,11 @@
 // each bucket gets the short-side orientation of "Scaling Muon for DiT" 3.1
 // (transpose iff m > n), a GEMM tile size chosen from r = min(m, n), padded
 // sizes r_pad / c_pad (multiples of the tile, zero filled), and is split into
-// equal chunks whose Newton-Schulz scratch fits the workspace cap.  Chunks run
-// one after another on the caller's stream and reuse one scratch region.
+// equal chunks whose Newton-Schulz scratch fits the workspace cap.  Chunks of
+// a bucket run one after another and reuse one scratch region.  Buckets run
+// one after another on the caller's stream, or, when all of them are too
+// small to fill the device alone, concurrently on internal streams (fork /
+// join through events), each stream with its own scratch region.
 //
 // Per chunk the refresh step enqueues:
 //   prep (M update, U, ||U||^2 partials, X0 = O(U))  -> finalize (1/||U||)
@@ -32,6 +35,7 @@ using namespace muon;
 namespace {
 
 constexpr int64_t kDefaultCap = 16ll << 30;   // Newton-Schulz scratch cap (bytes)
+constexpr int kMaxSlots = 4;                   // internal streams for concurrent buckets
 constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
 constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
 constexpr int kRing = 4;                      // pinned descriptor staging slots
@@ -65,6 +69,7 @@ struct Bucket {
   int first, count;  // range in plan order
   std::vector<Chunk> chunks;
   int64_t scratch_per_mat;
+  size_t chunk_scratch;  // scratch of its largest chunk
   int prep_blocks;
   int rn_row_blocks;
 };
@@ -96,6 +101,16 @@ struct muon_plan_s {
   size_t off_table = 0, off_inv = 0, off_part = 0, off_colscale = 0, off_scratch = 0;
   size_t ws_bytes = 0;
   size_t max_scratch = 0;
+  // Concurrent buckets: bucket b runs on slot b % nslots, each slot with its
+  // own stream, scratch region and partial-sum region.  nslots == 1: every
+  // bucket on the caller's stream.  Streams and events are created on the
+  // first step call that needs them.
+  int nslots = 1;
+  std::vector<size_t> slot_scratch_off;  // bytes from off_scratch
+  size_t slot_part_floats = 0;           // floats per slot from off_part
+  std::vector<hipStream_t> slot_streams;
+  std::vector<hipEvent_t> slot_done;
+  hipEvent_t fork_ev = nullptr;
   // descriptor staging
   Slot ring[kRing];
   int next_slot = 0;
@@ -265,6 +280,40 @@ void release_profile(muon_plan_s* p) {
   p->tused = 0;
 }
 
+void release_slots(muon_plan_s* p) {
+  for (hipStream_t s : p->slot_streams) (void)hipStreamDestroy(s);
+  for (hipEvent_t e : p->slot_done) (void)hipEventDestroy(e);
+  if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
+  p->slot_streams.clear();
+  p->slot_done.clear();
+  p->fork_ev = nullptr;
+}
+
+// Internal streams (default priority) and their fork / join events.
+muon_status ensure_slots(muon_plan_s* p) {
+  if ((int)p->slot_streams.size() == p->nslots) return MUON_OK;
+  release_slots(p);
+  if (hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) != hipSuccess) {
+    p->fork_ev = nullptr;
+    return MUON_ERR_HIP;
+  }
+  for (int i = 0; i < p->nslots; ++i) {
+    hipStream_t s = nullptr;
+    hipEvent_t e = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+      release_slots(p);
+      return MUON_ERR_HIP;
+    }
+    p->slot_streams.push_back(s);
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+      release_slots(p);
+      return MUON_ERR_HIP;
+    }
+    p->slot_done.push_back(e);
+  }
+  return MUON_OK;
+}
+
 // Per-shape hints: values and duplicates checked here; whether a hint fits
 // its bucket's final form is checked when the bucket is planned.
 muon_status validate_hints(const muon_plan_desc* desc) {
@@ -423,7 +472,8 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       B.n_pad = B.transposed ? B.r_pad : B.c_pad;
       B.prep_blocks = prep_blocks_per_mat((int)B.m_pad, (int)B.n_pad);
       B.rn_row_blocks = rownorm_row_blocks((int)B.m, (int)B.n);
-      max_scratch = std::max(max_scratch, (size_t)(even * B.scratch_per_mat));
+      B.chunk_scratch = (size_t)(even * B.scratch_per_mat);
+      max_scratch = std::max(max_scratch, B.chunk_scratch);
       part_floats = std::max(part_floats, (size_t)even * (size_t)B.prep_blocks);
       if (B.transposed) {
         // RowNorm runs on whole buckets (no NS scratch needed)
@@ -431,13 +481,39 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
         colscale_floats = std::max(colscale_floats, (size_t)B.count * (size_t)B.n);
       }
     }
+    // Buckets too small to fill the device on their own (one launch chunk,
+    // every r x r product under two waves of tiles for the 256 compute
+    // units) run concurrently on up to kMaxSlots streams when their scratch
+    // regions fit the cap together; otherwise all run one after another.
+    const int nb = (int)p->buckets.size();
+    bool small = nb > 1;
+    for (const Bucket& B : p->buckets) {
+      const int64_t T = B.r_pad / B.bt;
+      if (B.chunks.size() != 1 || (int64_t)B.count * (T * (T + 1) / 2) >= 512) small = false;
+    }
+    int S = small ? std::min(nb, kMaxSlots) : 1;
+    std::vector<size_t> slot_bytes((size_t)S, 0);
+    for (int b = 0; b < nb; ++b)
+      slot_bytes[(size_t)(b % S)] = std::max(slot_bytes[(size_t)(b % S)],
+                                             align256(p->buckets[(size_t)b].chunk_scratch));
+    size_t total = 0;
+    for (size_t v : slot_bytes) total += v;
+    if (S > 1 && total > (size_t)cap) {
+      S = 1;
+      slot_bytes.assign(1, max_scratch);
+      total = max_scratch;
+    }
+    p->nslots = S;
+    p->slot_scratch_off.assign((size_t)S, 0);
+    for (int i = 1; i < S; ++i) p->slot_scratch_off[(size_t)i] = p->slot_scratch_off[(size_t)i - 1] + slot_bytes[(size_t)i - 1];
+    p->slot_part_floats = align256(sizeof(float) * std::max<size_t>(part_floats, 1)) / sizeof(float);
     p->off_table = 0;
     p->off_inv = align256(sizeof(MatPtrs) * (size_t)p->nmat);
     p->off_part = p->off_inv + align256(sizeof(float) * (size_t)p->nmat);
-    p->off_colscale = p->off_part + align256(sizeof(float) * std::max<size_t>(part_floats, 1));
+    p->off_colscale = p->off_part + sizeof(float) * p->slot_part_floats * (size_t)S;
     p->off_scratch = p->off_colscale + align256(sizeof(float) * std::max<size_t>(colscale_floats, 1));
-    p->max_scratch = max_scratch;
-    p->ws_bytes = p->off_scratch + max_scratch;
+    p->max_scratch = total;
+    p->ws_bytes = p->off_scratch + total;
   } catch (const std::bad_alloc&) {
     delete p;
     return MUON_ERR_INVALID_ARGUMENT;
@@ -451,6 +527,7 @@ muon_status muon_plan_destroy(muon_plan_t plan) {
   if (!plan) return MUON_OK;
   release_ring(plan);
   release_profile(plan);
+  release_slots(plan);
   delete plan;
   return MUON_OK;
 }
@@ -500,16 +577,30 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
   char* wsb = (char*)ws;
   const MatPtrs* d_table = (const MatPtrs*)(wsb + p->off_table);
   float* d_inv = (float*)(wsb + p->off_inv);
-  float* d_part = (float*)(wsb + p->off_part);
-  char* scratch = wsb + p->off_scratch;
   const bool f32path = p->ns_dtype == MUON_F32;
   const int op = f32path ? OP_F32 : OP_BF16;
   const int xes = f32path ? 4 : 2;
   const int gbf16 = p->grad_dtype == MUON_BF16 ? 1 : 0;
   const muon_hparams& hp = p->hp;
   const int N = hp.ns_steps;
+  const int S = p->nslots;
+  const hipStream_t caller = stream;
 
-  for (const Bucket& B : p->buckets) {
+  // fork: every slot stream waits for the table upload on the caller's stream
+  if (S > 1) {
+    st = ensure_slots(p);
+    if (st != MUON_OK) return st;
+    if (hipEventRecord(p->fork_ev, caller) != hipSuccess) return MUON_ERR_HIP;
+    for (hipStream_t s : p->slot_streams)
+      if (hipStreamWaitEvent(s, p->fork_ev, 0) != hipSuccess) return MUON_ERR_HIP;
+  }
+  auto run_buckets = [&]() -> muon_status {
+  for (size_t bi = 0; bi < p->buckets.size(); ++bi) {
+    const Bucket& B = p->buckets[bi];
+    const size_t slot = bi % (size_t)S;
+    const hipStream_t stream = S > 1 ? p->slot_streams[slot] : caller;
+    char* scratch = wsb + p->off_scratch + p->slot_scratch_off[slot];
+    float* d_part = (float*)(wsb + p->off_part) + p->slot_part_floats * slot;
     const int64_t rr = B.r_pad * B.r_pad;
     const int T = (int)(B.r_pad / B.bt);
     const int ntri = T * (T + 1) / 2;
@@ -822,6 +913,18 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
     }
   }
   return MUON_OK;
+  };
+  st = run_buckets();
+  // join: the caller's stream waits for every slot (also after a failed
+  // launch, so that no work of this call is left unordered)
+  if (S > 1) {
+    for (int i = 0; i < S; ++i) {
+      if (hipEventRecord(p->slot_done[(size_t)i], p->slot_streams[(size_t)i]) != hipSuccess ||
+          hipStreamWaitEvent(caller, p->slot_done[(size_t)i], 0) != hipSuccess)
+        st = MUON_ERR_HIP;
+    }
+  }
+  return st;
 }
 
 muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
