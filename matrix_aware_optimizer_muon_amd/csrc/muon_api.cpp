@@ -505,7 +505,8 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
     }
     p->nslots = S;
     p->slot_scratch_off.assign((size_t)S, 0);
-    for (int i = 1; i < S; ++i) p->slot_scratch_off[(size_t)i] = p->slot_scratch_off[(size_t)i - 1] + slot_bytes[(size_t)i - 1];
+    for (size_t i = 1; i < (size_t)S; ++i)
+      p->slot_scratch_off[i] = p->slot_scratch_off[i - 1] + slot_bytes[i - 1];
     p->slot_part_floats = align256(sizeof(float) * std::max<size_t>(part_floats, 1)) / sizeof(float);
     p->off_table = 0;
     p->off_inv = align256(sizeof(MatPtrs) * (size_t)p->nmat);
@@ -595,324 +596,324 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       if (hipStreamWaitEvent(s, p->fork_ev, 0) != hipSuccess) return MUON_ERR_HIP;
   }
   auto run_buckets = [&]() -> muon_status {
-  for (size_t bi = 0; bi < p->buckets.size(); ++bi) {
-    const Bucket& B = p->buckets[bi];
-    const size_t slot = bi % (size_t)S;
-    const hipStream_t stream = S > 1 ? p->slot_streams[slot] : caller;
-    char* scratch = wsb + p->off_scratch + p->slot_scratch_off[slot];
-    float* d_part = (float*)(wsb + p->off_part) + p->slot_part_floats * slot;
-    const int64_t rr = B.r_pad * B.r_pad;
-    const int T = (int)(B.r_pad / B.bt);
-    const int ntri = T * (T + 1) / 2;
-    for (const Chunk& ch : B.chunks) {
-      const int nm = ch.count;
-      // scratch layout for this chunk
-      size_t off = 0;
-      auto take = [&](size_t per_mat_bytes) {
-        char* q = scratch + off;
-        off += align256(per_mat_bytes) * (size_t)nm;
-        return q;
-      };
-      // per-matrix strides must be uniform: use the aligned per-matrix size
-      const size_t xbytes = align256((size_t)(B.r_pad * B.c_pad * xes));
-      const size_t f32b = align256((size_t)(rr * 4));
-      const size_t h16b = f32path ? f32b : align256((size_t)(rr * 2));
-      void* Xnat = take(xbytes);  // U, m_pad x n_pad
-      void* Xtr = take(xbytes);   // U^T, n_pad x m_pad
-      // X0 = O(U) is r_pad x c_pad (ld c_pad); X0^T is c_pad x r_pad (ld r_pad)
-      void* X = B.transposed ? Xtr : Xnat;
-      void* XT = B.transposed ? Xnat : Xtr;
-      float* Gf = nullptr;
-      float* Qf[2] = {nullptr, nullptr};
-      float* Hf = nullptr;
-      if (!B.dma) {
-        Gf = (float*)take(f32b);
-        Qf[0] = (float*)take(f32b);
-        Qf[1] = (float*)take(f32b);
-        Hf = (float*)take(f32b);
-      }
-      void* Gh;
-      void* Ph;
-      void* Qh[2] = {nullptr, nullptr};
-      void* Hh = nullptr;
-      void* Xn2 = nullptr;
-      void* Xt2 = nullptr;
-      if (B.direct) {
-        Xn2 = take(xbytes);
-        Xt2 = take(xbytes);
-        Gh = take(h16b);
-        Ph = take(h16b);
-      } else if (f32path) {
-        Gh = Gf;
-        Ph = take(f32b);
-        Qh[0] = Qf[0];
-        Qh[1] = Qf[1];
-        Hh = Hf;
-      } else {
-        Gh = take(h16b);
-        Ph = take(h16b);
-        Qh[0] = take(h16b);
-        Qh[1] = take(h16b);
-        Hh = take(h16b);
-      }
-      const int64_t x_stride = (int64_t)(xbytes / xes);
-      const int64_t rr_stride = (int64_t)(f32b / 4);
-      const int64_t h_stride = (int64_t)(h16b / (f32path ? 4 : 2));
-      // the epilogues index fp32 and 16-bit r x r buffers with one element
-      // stride; r_pad is a multiple of 64, so both are exactly r_pad^2
-      if (rr_stride != h_stride || rr_stride != rr) return MUON_ERR_HIP;
-      const int vec = chunk_vec(p, B, ch);
-      auto gemm = [&](const GemmParams& gp, int epi) {
-        return B.dma ? launch_gemm_dma(gp, epi, nm, stream)
-                     : launch_gemm(gp, epi, op, B.bt, nm, stream);
-      };
-      // algorithmic work per matrix (true sizes; symmetric products on the
-      // lower triangle): SYRK r^2 c, each r x r product r^3, final 2 r^2 c
-      const double r2 = (double)B.r * B.r, r3 = r2 * B.r, cc = (double)B.c;
-      const double rcf = (double)B.r * B.c;
-      // algorithmic bytes per r x r element: operand reads (each operand read
-      // once), the identity-term input (lower triangle, read once) and the
-      // outputs (both triangles); the 256-tile path keeps only fp16 copies
-      const double op_b = f32path ? 4.0 : 2.0;
-      const double in_b = f32path ? 2.0 : (B.dma ? 1.0 : 2.0);
-      const double out_b = f32path ? 4.0 : (B.dma ? 2.0 : 6.0);
+    for (size_t bi = 0; bi < p->buckets.size(); ++bi) {
+      const Bucket& B = p->buckets[bi];
+      const size_t slot = bi % (size_t)S;
+      const hipStream_t stream = S > 1 ? p->slot_streams[slot] : caller;
+      char* scratch = wsb + p->off_scratch + p->slot_scratch_off[slot];
+      float* d_part = (float*)(wsb + p->off_part) + p->slot_part_floats * slot;
+      const int64_t rr = B.r_pad * B.r_pad;
+      const int T = (int)(B.r_pad / B.bt);
+      const int ntri = T * (T + 1) / 2;
+      for (const Chunk& ch : B.chunks) {
+        const int nm = ch.count;
+        // scratch layout for this chunk
+        size_t off = 0;
+        auto take = [&](size_t per_mat_bytes) {
+          char* q = scratch + off;
+          off += align256(per_mat_bytes) * (size_t)nm;
+          return q;
+        };
+        // per-matrix strides must be uniform: use the aligned per-matrix size
+        const size_t xbytes = align256((size_t)(B.r_pad * B.c_pad * xes));
+        const size_t f32b = align256((size_t)(rr * 4));
+        const size_t h16b = f32path ? f32b : align256((size_t)(rr * 2));
+        void* Xnat = take(xbytes);  // U, m_pad x n_pad
+        void* Xtr = take(xbytes);   // U^T, n_pad x m_pad
+        // X0 = O(U) is r_pad x c_pad (ld c_pad); X0^T is c_pad x r_pad (ld r_pad)
+        void* X = B.transposed ? Xtr : Xnat;
+        void* XT = B.transposed ? Xnat : Xtr;
+        float* Gf = nullptr;
+        float* Qf[2] = {nullptr, nullptr};
+        float* Hf = nullptr;
+        if (!B.dma) {
+          Gf = (float*)take(f32b);
+          Qf[0] = (float*)take(f32b);
+          Qf[1] = (float*)take(f32b);
+          Hf = (float*)take(f32b);
+        }
+        void* Gh;
+        void* Ph;
+        void* Qh[2] = {nullptr, nullptr};
+        void* Hh = nullptr;
+        void* Xn2 = nullptr;
+        void* Xt2 = nullptr;
+        if (B.direct) {
+          Xn2 = take(xbytes);
+          Xt2 = take(xbytes);
+          Gh = take(h16b);
+          Ph = take(h16b);
+        } else if (f32path) {
+          Gh = Gf;
+          Ph = take(f32b);
+          Qh[0] = Qf[0];
+          Qh[1] = Qf[1];
+          Hh = Hf;
+        } else {
+          Gh = take(h16b);
+          Ph = take(h16b);
+          Qh[0] = take(h16b);
+          Qh[1] = take(h16b);
+          Hh = take(h16b);
+        }
+        const int64_t x_stride = (int64_t)(xbytes / xes);
+        const int64_t rr_stride = (int64_t)(f32b / 4);
+        const int64_t h_stride = (int64_t)(h16b / (f32path ? 4 : 2));
+        // the epilogues index fp32 and 16-bit r x r buffers with one element
+        // stride; r_pad is a multiple of 64, so both are exactly r_pad^2
+        if (rr_stride != h_stride || rr_stride != rr) return MUON_ERR_HIP;
+        const int vec = chunk_vec(p, B, ch);
+        auto gemm = [&](const GemmParams& gp, int epi) {
+          return B.dma ? launch_gemm_dma(gp, epi, nm, stream)
+                       : launch_gemm(gp, epi, op, B.bt, nm, stream);
+        };
+        // algorithmic work per matrix (true sizes; symmetric products on the
+        // lower triangle): SYRK r^2 c, each r x r product r^3, final 2 r^2 c
+        const double r2 = (double)B.r * B.r, r3 = r2 * B.r, cc = (double)B.c;
+        const double rcf = (double)B.r * B.c;
+        // algorithmic bytes per r x r element: operand reads (each operand read
+        // once), the identity-term input (lower triangle, read once) and the
+        // outputs (both triangles); the 256-tile path keeps only fp16 copies
+        const double op_b = f32path ? 4.0 : 2.0;
+        const double in_b = f32path ? 2.0 : (B.dma ? 1.0 : 2.0);
+        const double out_b = f32path ? 4.0 : (B.dma ? 2.0 : 6.0);
 
-      PrepParams pp{};
-      pp.table = d_table + ch.first;
-      pp.m = (int)B.m;
-      pp.n = (int)B.n;
-      pp.m_pad = (int)B.m_pad;
-      pp.n_pad = (int)B.n_pad;
-      pp.mu = hp.momentum;
-      pp.nesterov = hp.nesterov;
-      pp.X = Xnat;
-      pp.XT = Xtr;
-      pp.x_stride = x_stride;
-      pp.partials = d_part;
-      pp.blocks_per_mat = B.prep_blocks;
-      pp.inv_norm = d_inv + ch.first;
-      const double elems = (double)B.m * B.n * nm;
-      st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + 2 * xes), [&] {
-        return launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream);
-      });
-      if (st != MUON_OK) return st;
-      st = timed(p, stream, MUON_K_NORM, 0.0, 4.0 * B.prep_blocks * nm,
-                 [&] { return launch_norm_finalize(pp, nm, stream); });
-      if (st != MUON_OK) return st;
-
-      GemmParams g{};
-      g.rr_stride = rr_stride;
-      g.ldr = (int)B.r_pad;
-      g.a = hp.a;
-      g.b = hp.b;
-      g.c = hp.c;
-      if (f32path) {
-        g.sG = g.sP = g.sQ = g.sH = 1.0f;
-      } else {
-        g.sG = kSG;
-        g.sP = kSP;
-        g.sQ = kSQ;
-        g.sH = kSH;
-      }
-      g.inv_norm = d_inv + ch.first;
-      g.table = d_table + ch.first;
-      g.Gf = Gf;
-      g.Hf = Hf;
-      g.Gh = Gh;
-      g.Ph = Ph;
-      g.Hh = Hh;
-      g.products = 1;
-      auto rr_setup = [&](const void* A, const void* Bop, const void* B2, int products) {
-        g.A = A;
-        g.B = Bop;
-        g.B2 = B2;
-        g.a_stride = g.b_stride = g.b2_stride = h_stride;
-        g.lda = g.ldb = (int)B.r_pad;
-        g.Mdim = g.Ndim = g.Kdim = (int)B.r_pad;
-        g.tiles_m = g.tiles_n = T;
-        g.triangular = 1;
-        g.tiles_per_prod = ntri;
-        g.products = products;
-      };
-
-      if (B.direct) {
-        // X0 = U / ||U||, in place, as fp16 scaled by kSX
-        XcastParams xc{};
-        xc.Xn = Xnat;
-        xc.Xt = Xtr;
-        xc.x_stride = x_stride;
-        xc.elems = B.m_pad * B.n_pad;
-        xc.inv_norm = d_inv + ch.first;
-        xc.sx = kSX;
-        st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
-                   [&] { return launch_xcast(xc, nm, stream); });
+        PrepParams pp{};
+        pp.table = d_table + ch.first;
+        pp.m = (int)B.m;
+        pp.n = (int)B.n;
+        pp.m_pad = (int)B.m_pad;
+        pp.n_pad = (int)B.n_pad;
+        pp.mu = hp.momentum;
+        pp.nesterov = hp.nesterov;
+        pp.X = Xnat;
+        pp.XT = Xtr;
+        pp.x_stride = x_stride;
+        pp.partials = d_part;
+        pp.blocks_per_mat = B.prep_blocks;
+        pp.inv_norm = d_inv + ch.first;
+        const double elems = (double)B.m * B.n * nm;
+        st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + 2 * xes), [&] {
+          return launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream);
+        });
         if (st != MUON_OK) return st;
-        void* Xn[2] = {Xnat, Xn2};
-        void* Xt[2] = {Xtr, Xt2};
-        g.xkind = 1;
-        g.syrk_scale = 1.0f / (kSX * kSX);
-        g.sX = kSX;
-        g.first = g.last = 0;
-        const int tm = (int)(B.r_pad / 256), tn = (int)(B.c_pad / 256);
-        for (int k = 0; k < N; ++k) {
-          const int cur = k & 1, nx = cur ^ 1;
-          void* Xk = B.transposed ? Xt[cur] : Xn[cur];    // r_pad x c_pad
-          void* XTk = B.transposed ? Xn[cur] : Xt[cur];   // c_pad x r_pad
-          // A = X X^T (lower tiles, mirrored)
-          g.A = g.B = g.B2 = Xk;
-          g.a_stride = g.b_stride = g.b2_stride = x_stride;
-          g.lda = g.ldb = (int)B.c_pad;
-          g.Mdim = g.Ndim = (int)B.r_pad;
-          g.Kdim = (int)B.c_pad;
+        st = timed(p, stream, MUON_K_NORM, 0.0, 4.0 * B.prep_blocks * nm,
+                   [&] { return launch_norm_finalize(pp, nm, stream); });
+        if (st != MUON_OK) return st;
+
+        GemmParams g{};
+        g.rr_stride = rr_stride;
+        g.ldr = (int)B.r_pad;
+        g.a = hp.a;
+        g.b = hp.b;
+        g.c = hp.c;
+        if (f32path) {
+          g.sG = g.sP = g.sQ = g.sH = 1.0f;
+        } else {
+          g.sG = kSG;
+          g.sP = kSP;
+          g.sQ = kSQ;
+          g.sH = kSH;
+        }
+        g.inv_norm = d_inv + ch.first;
+        g.table = d_table + ch.first;
+        g.Gf = Gf;
+        g.Hf = Hf;
+        g.Gh = Gh;
+        g.Ph = Ph;
+        g.Hh = Hh;
+        g.products = 1;
+        auto rr_setup = [&](const void* A, const void* Bop, const void* B2, int products) {
+          g.A = A;
+          g.B = Bop;
+          g.B2 = B2;
+          g.a_stride = g.b_stride = g.b2_stride = h_stride;
+          g.lda = g.ldb = (int)B.r_pad;
+          g.Mdim = g.Ndim = g.Kdim = (int)B.r_pad;
           g.tiles_m = g.tiles_n = T;
           g.triangular = 1;
           g.tiles_per_prod = ntri;
-          g.products = 1;
-          st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (2.0 * rcf + 2.0 * r2) * nm,
-                     [&] { return gemm(g, EPI_SYRK); });
-          if (st != MUON_OK) return st;
-          // P~ = b A + c A^2
-          rr_setup(Gh, Gh, Gh, 1);
-          st = timed(p, stream, MUON_K_POLY, r3 * nm, 4.0 * r2 * nm, [&] { return gemm(g, EPI_POLY); });
-          if (st != MUON_OK) return st;
-          // X' = a X + P~ X, written in both layouts
-          GemmParams xg = g;
-          xg.A = Ph;
-          xg.a_stride = h_stride;
-          xg.lda = (int)B.r_pad;
-          xg.B = xg.B2 = XTk;
-          xg.b_stride = xg.b2_stride = x_stride;
-          xg.ldb = (int)B.r_pad;
-          xg.Mdim = (int)B.r_pad;
-          xg.Ndim = (int)B.c_pad;
-          xg.Kdim = (int)B.r_pad;
-          xg.tiles_m = tm;
-          xg.tiles_n = tn;
-          xg.triangular = 0;
-          xg.tiles_per_prod = tm * tn;
-          xg.products = 1;
-          xg.Yn = B.transposed ? Xt[nx] : Xn[nx];
-          xg.Yt = B.transposed ? Xn[nx] : Xt[nx];
-          xg.ldyn = (int)B.c_pad;
-          xg.ldyt = (int)B.r_pad;
-          xg.y_stride = x_stride;
-          st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + 6.0 * rcf) * nm,
-                     [&] { return gemm(xg, EPI_XUPD); });
-          if (st != MUON_OK) return st;
-        }
-        // W <- (1 - lr wd) W - lr s O^-1(X_N): the natural-layout buffer of
-        // the last pair holds O^-1(X_N) in W's layout
-        WupdParams wp{};
-        wp.table = d_table + ch.first;
-        wp.X = Xn[N & 1];
-        wp.x_stride = x_stride;
-        wp.m = (int)B.m;
-        wp.n = (int)B.n;
-        wp.n_pad = (int)B.n_pad;
-        wp.inv_sx = 1.0f / kSX;
-        wp.decay = (float)(1.0 - (double)lr * wd);
-        wp.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
-        st = timed(p, stream, MUON_K_WUPD, 0.0, 10.0 * (double)B.m * B.n * nm,
-                   [&] { return launch_wupd(wp, nm, vec, stream); });
-        if (st != MUON_OK) return st;
-        continue;
-      }
+          g.products = products;
+        };
 
-      // G0 = X0 X0^T / ||U||^2
-      g.A = g.B = g.B2 = X;
-      g.a_stride = g.b_stride = g.b2_stride = x_stride;
-      g.lda = g.ldb = (int)B.c_pad;
-      g.Mdim = g.Ndim = (int)B.r_pad;
-      g.Kdim = (int)B.c_pad;
-      g.tiles_m = g.tiles_n = T;
-      g.triangular = 1;
-      g.tiles_per_prod = ntri;
-      g.products = 1;
-      st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (xes * rcf + r2 * out_b) * nm,
-                 [&] { return gemm(g, EPI_SYRK); });
-      if (st != MUON_OK) return st;
-
-      for (int k = 0; k < N; ++k) {
-        const int dst = k & 1, src = dst ^ 1;
-        g.first = k == 0;
-        g.last = k == N - 1;
-        g.Qf_src = Qf[src];
-        g.Qf_dst = Qf[dst];
-        g.Qh_dst = Qh[dst];
-        g.Qh_src = Qh[src];
-        // P~ = b G + c G^2 (and Q1 = a I + P~ on the first iteration)
-        rr_setup(Gh, Gh, Gh, 1);
-        st = timed(p, stream, MUON_K_POLY, r3 * nm, r2 * (op_b + in_b + out_b * (k == 0 ? 2 : 1)) * nm,
-                   [&] { return gemm(g, EPI_POLY); });
-        if (st != MUON_OK) return st;
-        const bool need_q = k > 0;
-        const bool need_h = k < N - 1;
-        if (need_q || need_h) {
-          // PQ: Q_k = a Q_{k-1} + P~ Q_{k-1};  PG: H = a G + P~ G
-          if (need_q && need_h) {
-            rr_setup(Ph, Qh[src], Gh, 2);
-            g.prod_base = 0;
-          } else if (need_q) {
-            rr_setup(Ph, Qh[src], Qh[src], 1);
-            g.prod_base = 0;
-          } else {  // first iteration: Q1 came from the POLY epilogue
-            rr_setup(Ph, Gh, Gh, 1);
-            g.prod_base = 1;
+        if (B.direct) {
+          // X0 = U / ||U||, in place, as fp16 scaled by kSX
+          XcastParams xc{};
+          xc.Xn = Xnat;
+          xc.Xt = Xtr;
+          xc.x_stride = x_stride;
+          xc.elems = B.m_pad * B.n_pad;
+          xc.inv_norm = d_inv + ch.first;
+          xc.sx = kSX;
+          st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
+                     [&] { return launch_xcast(xc, nm, stream); });
+          if (st != MUON_OK) return st;
+          void* Xn[2] = {Xnat, Xn2};
+          void* Xt[2] = {Xtr, Xt2};
+          g.xkind = 1;
+          g.syrk_scale = 1.0f / (kSX * kSX);
+          g.sX = kSX;
+          g.first = g.last = 0;
+          const int tm = (int)(B.r_pad / 256), tn = (int)(B.c_pad / 256);
+          for (int k = 0; k < N; ++k) {
+            const int cur = k & 1, nx = cur ^ 1;
+            void* Xk = B.transposed ? Xt[cur] : Xn[cur];    // r_pad x c_pad
+            void* XTk = B.transposed ? Xn[cur] : Xt[cur];   // c_pad x r_pad
+            // A = X X^T (lower tiles, mirrored)
+            g.A = g.B = g.B2 = Xk;
+            g.a_stride = g.b_stride = g.b2_stride = x_stride;
+            g.lda = g.ldb = (int)B.c_pad;
+            g.Mdim = g.Ndim = (int)B.r_pad;
+            g.Kdim = (int)B.c_pad;
+            g.tiles_m = g.tiles_n = T;
+            g.triangular = 1;
+            g.tiles_per_prod = ntri;
+            g.products = 1;
+            st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (2.0 * rcf + 2.0 * r2) * nm,
+                       [&] { return gemm(g, EPI_SYRK); });
+            if (st != MUON_OK) return st;
+            // P~ = b A + c A^2
+            rr_setup(Gh, Gh, Gh, 1);
+            st = timed(p, stream, MUON_K_POLY, r3 * nm, 4.0 * r2 * nm, [&] { return gemm(g, EPI_POLY); });
+            if (st != MUON_OK) return st;
+            // X' = a X + P~ X, written in both layouts
+            GemmParams xg = g;
+            xg.A = Ph;
+            xg.a_stride = h_stride;
+            xg.lda = (int)B.r_pad;
+            xg.B = xg.B2 = XTk;
+            xg.b_stride = xg.b2_stride = x_stride;
+            xg.ldb = (int)B.r_pad;
+            xg.Mdim = (int)B.r_pad;
+            xg.Ndim = (int)B.c_pad;
+            xg.Kdim = (int)B.r_pad;
+            xg.tiles_m = tm;
+            xg.tiles_n = tn;
+            xg.triangular = 0;
+            xg.tiles_per_prod = tm * tn;
+            xg.products = 1;
+            xg.Yn = B.transposed ? Xt[nx] : Xn[nx];
+            xg.Yt = B.transposed ? Xn[nx] : Xt[nx];
+            xg.ldyn = (int)B.c_pad;
+            xg.ldyt = (int)B.r_pad;
+            xg.y_stride = x_stride;
+            st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + 6.0 * rcf) * nm,
+                       [&] { return gemm(xg, EPI_XUPD); });
+            if (st != MUON_OK) return st;
           }
-          const int np = g.products;
-          st = timed(p, stream, MUON_K_PQPG, r3 * np * nm, r2 * (op_b + np * (op_b + in_b + out_b)) * nm,
-                     [&] { return gemm(g, EPI_PQPG); });
-          g.prod_base = 0;
+          // W <- (1 - lr wd) W - lr s O^-1(X_N): the natural-layout buffer of
+          // the last pair holds O^-1(X_N) in W's layout
+          WupdParams wp{};
+          wp.table = d_table + ch.first;
+          wp.X = Xn[N & 1];
+          wp.x_stride = x_stride;
+          wp.m = (int)B.m;
+          wp.n = (int)B.n;
+          wp.n_pad = (int)B.n_pad;
+          wp.inv_sx = 1.0f / kSX;
+          wp.decay = (float)(1.0 - (double)lr * wd);
+          wp.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
+          st = timed(p, stream, MUON_K_WUPD, 0.0, 10.0 * (double)B.m * B.n * nm,
+                     [&] { return launch_wupd(wp, nm, vec, stream); });
           if (st != MUON_OK) return st;
+          continue;
         }
-        if (need_h) {
-          // G_k = a H + P~ H
-          rr_setup(Ph, Hh, Hh, 1);
-          st = timed(p, stream, MUON_K_PH, r3 * nm, r2 * (2 * op_b + in_b + out_b) * nm,
-                     [&] { return gemm(g, EPI_PH); });
-          if (st != MUON_OK) return st;
-        }
-      }
 
-      // O = Q X0 / ||U||;  W <- (1 - lr wd) W - lr s O   (with O^-1 orientation)
-      const void* Qfinal = f32path ? (const void*)Qf[(N - 1) & 1] : (const void*)Qh[(N - 1) & 1];
-      GemmParams fg = g;
-      fg.Kdim = (int)B.r_pad;
-      fg.triangular = 0;
-      fg.products = 1;
-      fg.vec = vec;
-      fg.out_rows = (int)B.m;
-      fg.out_cols = (int)B.n;
-      fg.decay = (float)(1.0 - (double)lr * wd);
-      fg.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
-      if (!B.transposed) {  // O (r x c) = Q (r x r) * (X0^T)^T
-        fg.A = Qfinal;
-        fg.a_stride = h_stride;
-        fg.lda = (int)B.r_pad;
-        fg.B = fg.B2 = XT;
-        fg.b_stride = fg.b2_stride = x_stride;
-        fg.ldb = (int)B.r_pad;
-        fg.Mdim = (int)B.r_pad;
-        fg.Ndim = (int)B.c_pad;
-      } else {  // O^T (c x r) = X0^T (c x r) * Q
-        fg.A = XT;
-        fg.a_stride = x_stride;
-        fg.lda = (int)B.r_pad;
-        fg.B = fg.B2 = Qfinal;
-        fg.b_stride = fg.b2_stride = h_stride;
-        fg.ldb = (int)B.r_pad;
-        fg.Mdim = (int)B.c_pad;
-        fg.Ndim = (int)B.r_pad;
+        // G0 = X0 X0^T / ||U||^2
+        g.A = g.B = g.B2 = X;
+        g.a_stride = g.b_stride = g.b2_stride = x_stride;
+        g.lda = g.ldb = (int)B.c_pad;
+        g.Mdim = g.Ndim = (int)B.r_pad;
+        g.Kdim = (int)B.c_pad;
+        g.tiles_m = g.tiles_n = T;
+        g.triangular = 1;
+        g.tiles_per_prod = ntri;
+        g.products = 1;
+        st = timed(p, stream, MUON_K_SYRK, r2 * cc * nm, (xes * rcf + r2 * out_b) * nm,
+                   [&] { return gemm(g, EPI_SYRK); });
+        if (st != MUON_OK) return st;
+
+        for (int k = 0; k < N; ++k) {
+          const int dst = k & 1, src = dst ^ 1;
+          g.first = k == 0;
+          g.last = k == N - 1;
+          g.Qf_src = Qf[src];
+          g.Qf_dst = Qf[dst];
+          g.Qh_dst = Qh[dst];
+          g.Qh_src = Qh[src];
+          // P~ = b G + c G^2 (and Q1 = a I + P~ on the first iteration)
+          rr_setup(Gh, Gh, Gh, 1);
+          st = timed(p, stream, MUON_K_POLY, r3 * nm, r2 * (op_b + in_b + out_b * (k == 0 ? 2 : 1)) * nm,
+                     [&] { return gemm(g, EPI_POLY); });
+          if (st != MUON_OK) return st;
+          const bool need_q = k > 0;
+          const bool need_h = k < N - 1;
+          if (need_q || need_h) {
+            // PQ: Q_k = a Q_{k-1} + P~ Q_{k-1};  PG: H = a G + P~ G
+            if (need_q && need_h) {
+              rr_setup(Ph, Qh[src], Gh, 2);
+              g.prod_base = 0;
+            } else if (need_q) {
+              rr_setup(Ph, Qh[src], Qh[src], 1);
+              g.prod_base = 0;
+            } else {  // first iteration: Q1 came from the POLY epilogue
+              rr_setup(Ph, Gh, Gh, 1);
+              g.prod_base = 1;
+            }
+            const int np = g.products;
+            st = timed(p, stream, MUON_K_PQPG, r3 * np * nm, r2 * (op_b + np * (op_b + in_b + out_b)) * nm,
+                       [&] { return gemm(g, EPI_PQPG); });
+            g.prod_base = 0;
+            if (st != MUON_OK) return st;
+          }
+          if (need_h) {
+            // G_k = a H + P~ H
+            rr_setup(Ph, Hh, Hh, 1);
+            st = timed(p, stream, MUON_K_PH, r3 * nm, r2 * (2 * op_b + in_b + out_b) * nm,
+                       [&] { return gemm(g, EPI_PH); });
+            if (st != MUON_OK) return st;
+          }
+        }
+
+        // O = Q X0 / ||U||;  W <- (1 - lr wd) W - lr s O   (with O^-1 orientation)
+        const void* Qfinal = f32path ? (const void*)Qf[(N - 1) & 1] : (const void*)Qh[(N - 1) & 1];
+        GemmParams fg = g;
+        fg.Kdim = (int)B.r_pad;
+        fg.triangular = 0;
+        fg.products = 1;
+        fg.vec = vec;
+        fg.out_rows = (int)B.m;
+        fg.out_cols = (int)B.n;
+        fg.decay = (float)(1.0 - (double)lr * wd);
+        fg.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
+        if (!B.transposed) {  // O (r x c) = Q (r x r) * (X0^T)^T
+          fg.A = Qfinal;
+          fg.a_stride = h_stride;
+          fg.lda = (int)B.r_pad;
+          fg.B = fg.B2 = XT;
+          fg.b_stride = fg.b2_stride = x_stride;
+          fg.ldb = (int)B.r_pad;
+          fg.Mdim = (int)B.r_pad;
+          fg.Ndim = (int)B.c_pad;
+        } else {  // O^T (c x r) = X0^T (c x r) * Q
+          fg.A = XT;
+          fg.a_stride = x_stride;
+          fg.lda = (int)B.r_pad;
+          fg.B = fg.B2 = Qfinal;
+          fg.b_stride = fg.b2_stride = h_stride;
+          fg.ldb = (int)B.r_pad;
+          fg.Mdim = (int)B.c_pad;
+          fg.Ndim = (int)B.r_pad;
+        }
+        fg.tiles_m = fg.Mdim / B.bt;
+        fg.tiles_n = fg.Ndim / B.bt;
+        fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
+        st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + op_b * r2 + 8.0 * rcf) * nm,
+                   [&] { return gemm(fg, EPI_FINAL); });
+        if (st != MUON_OK) return st;
       }
-      fg.tiles_m = fg.Mdim / B.bt;
-      fg.tiles_n = fg.Ndim / B.bt;
-      fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
-      st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + op_b * r2 + 8.0 * rcf) * nm,
-                 [&] { return gemm(fg, EPI_FINAL); });
-      if (st != MUON_OK) return st;
     }
-  }
-  return MUON_OK;
+    return MUON_OK;
   };
   st = run_buckets();
   // join: the caller's stream waits for every slot (also after a failed

@@ -237,3 +237,16 @@ def test_bucket_hints_validation():
     assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128}}) == uns   # direct needs 256
     assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128, "formulation": "gram"}}) == 0
     assert plan_status([(300, 700)], hints={(300, 700): {"tile": 64, "formulation": "direct"}}) == uns
+
+
+def test_concurrent_bucket_layout_and_cap_fallback():
+    # small buckets get one scratch region per internal stream; a cap below
+    # their sum (but above each bucket's own need) falls back to one region
+    small = [(640, 640)] * 2 + [(512, 1536)] * 2 + [(1536, 512)] + [(300, 700)] * 3 + [(96, 2000)]
+    each = max(L.Plan([s] * small.count(s)).workspace_bytes for s in dict.fromkeys(small))
+    conc = L.Plan(small).workspace_bytes
+    seq = L.Plan(small, max_workspace_bytes=each).workspace_bytes
+    assert conc > seq and seq <= each + (1 << 20)
+    # a bucket that fills the device keeps every bucket on the caller's stream
+    big = small + [(3584, 3584)] * 8
+    assert L.Plan(big).workspace_bytes <= L.Plan([(3584, 3584)] * 8).workspace_bytes + (1 << 20)

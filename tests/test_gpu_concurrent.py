@@ -48,3 +48,14 @@ def test_concurrent_buckets_parity_and_repeatability():
     (W2, _, O2), _ = run(SHAPES, W, M, G, LR, WD, "f32", "bf16")
     for a, b in zip(O1 + W1, O2 + W2):
         assert np.array_equal(a, b)
+
+
+def test_cap_fallback_matches_concurrent_run():
+    from matrix_aware_optimizer_muon_amd import Plan
+    each = max(Plan([s] * SHAPES.count(s)).workspace_bytes for s in dict.fromkeys(SHAPES))
+    W, M, G = seeded(SHAPES, 93, mscale=1e-3)
+    (Wc, Mc, Oc), pc = run(SHAPES, W, M, G, LR, WD, "f32", "bf16")
+    (Ws, Ms, Os), ps = run(SHAPES, W, M, G, LR, WD, "f32", "bf16", max_ws=each)
+    assert ps.workspace_bytes < pc.workspace_bytes
+    for a, b in zip(Wc + Mc + Oc, Ws + Ms + Os):
+        assert np.array_equal(a, b)
