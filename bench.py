@@ -117,6 +117,8 @@ def main():
                          "are tuned first, on the device)")
     ap.add_argument("--tune-cache", default=None,
                     help="tuning cache file (default: the one shipped with the package)")
+    ap.add_argument("--max-workspace-gib", type=float, default=0.0,
+                    help="Newton-Schulz scratch cap passed to the planner (0: the library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-launch event timing")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
@@ -160,7 +162,8 @@ def main():
                         log=lambda msg: print("tune: " + msg, file=sys.stderr, flush=True))
         hints = TU.hints_for(w.shapes, w.grad_dtype, w.ns_dtype, cache)
         torch.cuda.synchronize()
-    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype, formulation=form, hints=hints)
+    plan = pkg.Plan(w.shapes, w.grad_dtype, w.ns_dtype, formulation=form, hints=hints,
+                    max_workspace_bytes=int(args.max_workspace_gib * (1 << 30)))
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -267,8 +270,9 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "library": os.path.relpath(lib_path, ROOT),
-        "plan": [{"shape": list(b["shape"]), "count": b["count"], "tile": b["tile"],
-                  "formulation": b["formulation"]} for b in plan.buckets()],
+        "plan": [{"shape": list(b["shape"]), "count": b["count"], "chunks": b["chunks"],
+                  "tile": b["tile"], "formulation": b["formulation"]} for b in plan.buckets()],
+        "workspace_bytes": plan.workspace_bytes,
     }
     if refresh_ms and rownorm_ms:
         out["refresh_ms"] = round(sum(refresh_ms) / len(refresh_ms), 4)

@@ -131,7 +131,7 @@ typedef struct {
                                 an fp16-MFMA r x r recursion                 */
   muon_hparams hp;
   int64_t max_workspace_bytes; /* cap for the Newton-Schulz scratch; 0 = the
-                                  library default (16 GiB).  Buckets of
+                                  library default (32 GiB).  Buckets of
                                   same-shape matrices are split into chunks
                                   that fit; a single matrix always fits.     */
   muon_formulation formulation; /* see above; 0 = MUON_FORM_AUTO            */

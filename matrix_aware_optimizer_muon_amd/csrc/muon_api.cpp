@@ -34,7 +34,7 @@ using namespace muon;
 
 namespace {
 
-constexpr int64_t kDefaultCap = 16ll << 30;   // Newton-Schulz scratch cap (bytes)
+constexpr int64_t kDefaultCap = 32ll << 30;   // Newton-Schulz scratch cap (bytes)
 constexpr int kMaxSlots = 4;                   // internal streams for concurrent buckets
 constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
 constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
