@@ -51,11 +51,28 @@ template <> struct Store<F32> {
 // Map a linear workgroup id so that consecutive logical ids land on the same
 // XCD.  The hardware dispatches workgroup w to XCD (w mod 8); tiles that share
 // operand panels should share that XCD's L2.  Bijective for any total.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+__host__ __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
   const uint32_t nx = 8;
   uint32_t x = bid % nx, slot = bid / nx;
   uint32_t q = total / nx, rem = total % nx;
   return x * q + (x < rem ? x : rem) + slot;
+}
+
+// Workgroup -> tile id in runs of C per XCD: XCD x takes tiles
+// [k 8C + x C, k 8C + x C + C) in its k-th run, so at any time the eight XCDs
+// work inside one window of 8C consecutive tiles (operands that the shared
+// last-level cache can hold) while each XCD's own workgroups still take
+// consecutive tiles (operand panels shared in its L2).  Tiles past the last
+// whole window are split as in xcd_remap.  A bijection on [0, total) for any
+// C > 0.
+__host__ __device__ __forceinline__ uint32_t xcd_remap_chunked(uint32_t bid, uint32_t total,
+                                                             uint32_t C) {
+  const uint32_t nx = 8;
+  const uint32_t x = bid % nx, slot = bid / nx;
+  const uint32_t span = nx * C, full = total / span;
+  if (slot / C < full) return (slot / C) * span + x * C + slot % C;
+  const uint32_t base = full * span;
+  return base + xcd_remap(bid - base, total - base);
 }
 
 // Streaming (non-temporal) 16-byte global access for data touched once per

@@ -166,7 +166,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   const int wm = wave / WGN, wn = wave % WGN;
   const int h = lane >> 5, l32 = lane & 31;
 
-  const uint32_t bid = xcd_remap(blockIdx.x, gridDim.x);
+  const uint32_t bid = p.xcd_chunk > 0 ? xcd_remap_chunked(blockIdx.x, gridDim.x, (uint32_t)p.xcd_chunk)
+                                       : xcd_remap(blockIdx.x, gridDim.x);
   const int per_mat = p.tiles_per_prod * p.products;
   const int mat = bid / per_mat;
   int t = bid - mat * per_mat;

@@ -31,6 +31,8 @@ struct GemmParams {
   int triangular;          // lower-triangle tiles only (symmetric result)
   int tiles_per_prod;      // tiles of one product of one matrix
   int products;            // 1 or 2
+  int xcd_chunk;           // 0: each XCD takes one contiguous range of the
+                           // launch's tiles; > 0: runs of this many (xcd_remap_chunked)
   int prod_base;           // epilogue product index of the first product
   // r x r recursion buffers (fp32 master copies and MFMA operand copies)
   float* Gf;
