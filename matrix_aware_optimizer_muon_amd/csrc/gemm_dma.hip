@@ -113,10 +113,15 @@ __device__ __forceinline__ uint2 pack_b4(float4 v) {
 }
 
 // Store elements [lo, hi) of four packed 16-bit values at base + o (one
-// 8-byte store when all four go).
+// 8-byte store when all four go).  The whole-chunk stores are non-temporal:
+// a launch's outputs (over 1 GB for the large buckets) are read only by the
+// next launch and would otherwise push the operand panels that the resident
+// tiles still share out of L2 (measured 0.4-1.6 % faster per product class).
 __device__ __forceinline__ void store16x4(uint16_t* base, size_t o, uint2 v, int lo, int hi) {
   if (lo == 0 && hi == 4) {
-    *(uint2*)(base + o) = v;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 x = {v.x, v.y};
+    __builtin_nontemporal_store(x, (u32x2*)(base + o));
     return;
   }
   const uint16_t e[4] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16)};
