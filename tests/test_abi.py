@@ -86,6 +86,18 @@ def test_plan_buckets_and_chunks():
     assert p2.info() == (2, 2)
 
 
+def test_default_cap_keeps_the_qwen_buckets_whole():
+    # The default 32 GiB scratch cap holds the largest Qwen2.5-7B bucket
+    # (56 x 18944 x 3584, ~401 MB of scratch per matrix) in one chunk; a
+    # 16 GiB cap splits it into two equal chunks of 28.
+    p4 = L.Plan(WL.config(4).shapes, grad_dtype="bf16")
+    assert [b["chunks"] for b in p4.buckets()] == [1, 1, 1, 1]
+    assert p4.workspace_bytes <= 32 << 30
+    p16 = L.Plan(WL.config(4).shapes, grad_dtype="bf16", max_workspace_bytes=16 << 30)
+    assert {tuple(b["shape"]): b["chunks"] for b in p16.buckets()}[(18944, 3584)] == 2
+    assert p16.workspace_bytes < p4.workspace_bytes
+
+
 def test_step_validation_happens_before_device_work():
     # Fake (never dereferenced) device pointers: every call must fail in host
     # validation, so nothing reaches the GPU (none exists here).
