@@ -102,14 +102,24 @@ __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) 
   }
 }
 
+// Four fp32 values to packed 16-bit, round to nearest even: one
+// v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 per pair (gfx950).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_h2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+__device__ __forceinline__ uint32_t cvt_b2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint2 pack_h4(float4 v, float scale) {
-  return make_uint2(
-      (uint32_t)f32_to_f16_bits(v.x * scale) | ((uint32_t)f32_to_f16_bits(v.y * scale) << 16),
-      (uint32_t)f32_to_f16_bits(v.z * scale) | ((uint32_t)f32_to_f16_bits(v.w * scale) << 16));
+  return make_uint2(cvt_h2(v.x * scale, v.y * scale), cvt_h2(v.z * scale, v.w * scale));
 }
 __device__ __forceinline__ uint2 pack_b4(float4 v) {
-  return make_uint2((uint32_t)f32_to_bf16_bits(v.x) | ((uint32_t)f32_to_bf16_bits(v.y) << 16),
-                    (uint32_t)f32_to_bf16_bits(v.z) | ((uint32_t)f32_to_bf16_bits(v.w) << 16));
+  return make_uint2(cvt_b2(v.x, v.y), cvt_b2(v.z, v.w));
 }
 
 // Store elements [lo, hi) of four packed 16-bit values at base + o (one
@@ -461,16 +471,20 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       sc1 = p.sQ;
       bf1 = p.last;
     }
+    // beta and the power-of-two fp16 scale fold into one factor: the product
+    // rounds once to fp32 exactly as beta * acc does, then once to 16 bits
+    const float bsc = bf1 ? beta : beta * sc1;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 v = make_float4(beta * acc[i][j][4 * g], beta * acc[i][j][4 * g + 1],
-                                       beta * acc[i][j][4 * g + 2], beta * acc[i][j][4 * g + 3]);
+          const float4 v = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                                       acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
           *(uint2*)(smem + t_off(wn * WTN + 32 * j + l32, wm * 32 + 8 * i + 2 * g + h)) =
-              bf1 ? pack_b4(v) : pack_h4(v, sc1);
+              bf1 ? pack_b4(make_float4(v.x * bsc, v.y * bsc, v.z * bsc, v.w * bsc))
+                  : pack_h4(v, bsc);
         }
     __syncthreads();
     const bool qout = EPI == EPI_POLY && p.first;
