@@ -189,7 +189,18 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
     __syncthreads();
     const int gr0 = row0A + round * RR;
     constexpr int PER = RR * BT / 256;
-    if constexpr (BT >= 256) {
+    if constexpr (EPI == EPI_FINAL) {
+      // four consecutive columns per thread: one 16-byte W load and store
+      // (W is touched once; the fp32 tile row is read from LDS as scalars)
+      constexpr int TPR = BT / 4;        // threads per tile row
+      constexpr int RPI = 256 / TPR;     // tile rows per iteration
+#pragma unroll 4
+      for (int e = 0; e < RR / RPI; ++e) {
+        const int il = e * RPI + tid / TPR, jl = (tid % TPR) * 4;
+        const float* sr = stile + il * EPI_LD + jl;
+        epilogue_final4(p, mat, gr0 + il, row0B + jl, make_float4(sr[0], sr[1], sr[2], sr[3]));
+      }
+    } else if constexpr (BT >= 256) {
       // row pass: one full tile row per iteration
 #pragma unroll 4
       for (int e = 0; e < PER; ++e) {

@@ -124,10 +124,8 @@ __device__ __forceinline__ void epilogue_final4(const GemmParams& p, int mat, in
   const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   const size_t idx = (size_t)gi * p.out_cols + gj;
   if (p.vec && gj + 4 <= p.out_cols) {
-    float4 w = *(const float4*)(mp.W + idx);
-    w = f4_axpy(p.decay, w, -p.step, o);
-    *(float4*)(mp.W + idx) = w;
-    if (mp.O) *(float4*)(mp.O + idx) = o;
+    nt_store4(mp.W + idx, f4_axpy(p.decay, nt_load4(mp.W + idx), -p.step, o));
+    if (mp.O) nt_store4(mp.O + idx, o);
   } else {
     const float ov[4] = {o.x, o.y, o.z, o.w};
     for (int k = 0; k < 4 && gj + k < p.out_cols; ++k) {
