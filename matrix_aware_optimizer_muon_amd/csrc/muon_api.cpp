@@ -25,6 +25,7 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "kernels.h"
@@ -604,10 +605,14 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
     for (hipStream_t s : p->slot_streams)
       if (hipStreamWaitEvent(s, p->fork_ev, 0) != hipSuccess) return MUON_ERR_HIP;
   }
-  auto run_buckets = [&]() -> muon_status {
+  // Enqueue the launch sequence of every bucket on slot `only_slot` (all
+  // buckets when negative).
+  auto run_buckets = [&](int only_slot) -> muon_status {
+    muon_status st = MUON_OK;
     for (size_t bi = 0; bi < p->buckets.size(); ++bi) {
-      const Bucket& B = p->buckets[bi];
       const size_t slot = bi % (size_t)S;
+      if (only_slot >= 0 && (int)slot != only_slot) continue;
+      const Bucket& B = p->buckets[bi];
       const hipStream_t stream = S > 1 ? p->slot_streams[slot] : caller;
       char* scratch = wsb + p->off_scratch + p->slot_scratch_off[slot];
       float* d_part = (float*)(wsb + p->off_part) + p->slot_part_floats * slot;
@@ -926,7 +931,32 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
     }
     return MUON_OK;
   };
-  st = run_buckets();
+  if (S > 1 && !p->profiling) {
+    // Each slot's launch sequence is enqueued from its own host thread, so
+    // that every slot's first kernels reach the GPU at once instead of after
+    // the whole sequence of the slots before it (~13 us of host time per
+    // launch; one Qwen2.5-7B layer: 8.3 -> 7.9 ms per step).  The threads
+    // only read the plan and launch on distinct streams; all are joined here.
+    std::vector<muon_status> sts((size_t)S, MUON_OK);
+    std::vector<std::thread> th;
+    int next = 1;
+    try {
+      for (; next < S; ++next) th.emplace_back([&, slot = next] { sts[(size_t)slot] = run_buckets(slot); });
+    } catch (...) {
+      // no thread for slots next..S-1: they run on this thread below
+    }
+    sts[0] = run_buckets(0);
+    for (std::thread& t : th) t.join();
+    for (int slot = next; slot < S; ++slot) sts[(size_t)slot] = run_buckets(slot);
+    st = MUON_OK;
+    for (muon_status v : sts)
+      if (v != MUON_OK) {
+        st = v;
+        break;
+      }
+  } else {
+    st = run_buckets(-1);
+  }
   // join: the caller's stream waits for every slot (also after a failed
   // launch, so that no work of this call is left unordered)
   if (S > 1) {
