@@ -188,7 +188,6 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
     }
     __syncthreads();
     const int gr0 = row0A + round * RR;
-    constexpr int PER = RR * BT / 256;
     if constexpr (EPI == EPI_FINAL) {
       // four consecutive columns per thread: one 16-byte W load and store
       // (W is touched once; the fp32 tile row is read from LDS as scalars)
@@ -200,32 +199,38 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
         const float* sr = stile + il * EPI_LD + jl;
         epilogue_final4(p, mat, gr0 + il, row0B + jl, make_float4(sr[0], sr[1], sr[2], sr[3]));
       }
-    } else if constexpr (BT >= 256) {
-      // row pass: one full tile row per iteration
-#pragma unroll 4
-      for (int e = 0; e < PER; ++e) {
-        const int il = e * (256 / BT), jl = tid % BT;
-        const int gi = gr0 + il, gj = row0B + jl;
-        if (EPI == EPI_FINAL || gi >= gj)
-          epilogue<EPI, F32PATH>(p, mat, prod, gi, gj, stile[il * EPI_LD + jl]);
-      }
     } else {
-#pragma unroll 4
-      for (int e = 0; e < PER; ++e) {
-        const int il = e * (256 / BT) + tid / BT, jl = tid % BT;
+      // row pass (lower triangle incl. the diagonal): four consecutive
+      // columns of a tile row per thread
+      constexpr int TPR = BT / 4;     // threads per tile row
+      constexpr int RPI = 256 / TPR;  // tile rows per iteration
+#pragma unroll 2
+      for (int e = 0; e < RR / RPI; ++e) {
+        const int il = e * RPI + tid / TPR, jl = (tid % TPR) * 4;
         const int gi = gr0 + il, gj = row0B + jl;
-        if (EPI == EPI_FINAL || gi >= gj)
-          epilogue<EPI, F32PATH>(p, mat, prod, gi, gj, stile[il * EPI_LD + jl]);
+        const int khi = min(max(gi - gj + 1, 0), 4);
+        if (khi > 0) {
+          const float* sr = stile + il * EPI_LD + jl;
+          epilogue4<EPI, F32PATH>(p, mat, prod, gi, gj, make_float4(sr[0], sr[1], sr[2], sr[3]), 0,
+                                  khi);
+        }
       }
-    }
-    if constexpr (EPI != EPI_FINAL) {
-      // mirror pass: consecutive threads take consecutive tile rows il, so the
-      // stores to (gj, gi) are contiguous in gi
-#pragma unroll 4
-      for (int e = 0; e < PER; ++e) {
-        const int il = tid % RR, jl = e * (256 / RR) + tid / RR;
+      // mirror pass (strictly lower part, stored at (gj, gi)): four
+      // consecutive tile rows of one tile column per thread, so the stores
+      // run along the mirrored row
+      constexpr int TPC = RR / 4;     // threads per tile column
+      constexpr int CPI = 256 / TPC;  // tile columns per iteration
+#pragma unroll 2
+      for (int e = 0; e < BT / CPI; ++e) {
+        const int il = (tid % TPC) * 4, jl = e * CPI + tid / TPC;
         const int gi = gr0 + il, gj = row0B + jl;
-        if (gi > gj) epilogue<EPI, F32PATH>(p, mat, prod, gj, gi, stile[il * EPI_LD + jl]);
+        const int klo = min(max(gj - gi + 1, 0), 4);
+        if (klo < 4) {
+          const float* sc = stile + il * EPI_LD + jl;
+          epilogue4<EPI, F32PATH>(p, mat, prod, gj, gi,
+                                  make_float4(sc[0], sc[EPI_LD], sc[2 * EPI_LD], sc[3 * EPI_LD]), klo,
+                                  4);
+        }
       }
     }
     __syncthreads();

@@ -83,6 +83,91 @@ __device__ __forceinline__ float4 f4_axpy(float a, float4 x, float b, float4 y) 
   return make_float4(a * x.x + b * y.x, a * x.y + b * y.y, a * x.z + b * y.z, a * x.w + b * y.w);
 }
 
+// ---------------------------------------------------------------------------
+// Four-column form of `epilogue` for the r x r products: accumulators of
+// (row, col0 + k), k = 0..3, stored for k in [klo, khi) (the rest lies on the
+// other side of the diagonal).  col0 is a multiple of 4 and the padded r x r
+// buffers have a multiple of 4 columns, so every input is one 16-byte load;
+// whole groups store fp32 as 16 bytes and 16-bit copies as 8 bytes.  Each
+// element gets exactly the value the scalar form computes.
+__device__ __forceinline__ float4 ld4(const float* b, size_t o) { return *(const float4*)(b + o); }
+__device__ __forceinline__ float f4at(const float4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ void st4f(float* b, size_t o, float4 v, int klo, int khi) {
+  if (klo == 0 && khi == 4) {
+    *(float4*)(b + o) = v;
+    return;
+  }
+  for (int k = klo; k < khi; ++k) b[o + k] = f4at(v, k);
+}
+// 16-bit copy of four values (scaled fp16, or bf16 when bf is set)
+__device__ __forceinline__ void st4h(void* base, size_t o, float4 v, float scale, bool bf, int klo,
+                                     int khi) {
+  uint16_t e[4];
+  for (int k = 0; k < 4; ++k)
+    e[k] = bf ? f32_to_bf16_bits(f4at(v, k)) : f32_to_f16_bits(f4at(v, k) * scale);
+  uint16_t* b = (uint16_t*)base;
+  if (klo == 0 && khi == 4) {
+    *(uint2*)(b + o) = make_uint2((uint32_t)e[0] | ((uint32_t)e[1] << 16),
+                                  (uint32_t)e[2] | ((uint32_t)e[3] << 16));
+    return;
+  }
+  for (int k = klo; k < khi; ++k) b[o + k] = e[k];
+}
+
+template <int EPI, bool F32PATH>
+__device__ __forceinline__ void epilogue4(const GemmParams& p, int mat, int prod, int row, int col0,
+                                          float4 acc, int klo, int khi) {
+  static_assert(EPI != EPI_FINAL, "the final product uses epilogue_final4");
+  const size_t o1 = (size_t)mat * p.rr_stride + (size_t)row * p.ldr + col0;
+  auto scale4 = [](float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); };
+  float4 v;
+  if constexpr (EPI == EPI_SYRK) {
+    const float inv = p.inv_norm[mat];
+    v = make_float4(acc.x * inv * inv, acc.y * inv * inv, acc.z * inv * inv, acc.w * inv * inv);
+    st4f(p.Gf, o1, v, klo, khi);
+    if constexpr (!F32PATH) st4h(p.Gh, o1, v, p.sG, false, klo, khi);
+    return;
+  } else if constexpr (EPI == EPI_POLY) {
+    const float4 g = ld4(p.Gf, o1);
+    const float4 s2 = scale4(acc, 1.0f / (p.sG * p.sG));
+    const float4 pt = f4_axpy(p.b, g, p.c, s2);
+    if constexpr (F32PATH) st4f((float*)p.Ph, o1, scale4(pt, p.sP), klo, khi);
+    else st4h(p.Ph, o1, pt, p.sP, false, klo, khi);
+    if (!p.first) return;
+    v = pt;  // Q1 = P1 = a I + P~
+    if (row == col0) v.x += p.a;
+    if (row == col0 + 1) v.y += p.a;
+    if (row == col0 + 2) v.z += p.a;
+    if (row == col0 + 3) v.w += p.a;
+  } else if constexpr (EPI == EPI_PQPG) {
+    if (prod == 1) {
+      const float4 hv = f4_axpy(p.a, ld4(p.Gf, o1), 1.0f, scale4(acc, 1.0f / (p.sP * p.sG)));
+      st4f(p.Hf, o1, hv, klo, khi);
+      if constexpr (!F32PATH) st4h(p.Hh, o1, hv, p.sH, false, klo, khi);
+      return;
+    }
+    v = f4_axpy(p.a, ld4(p.Qf_src, o1), 1.0f, scale4(acc, 1.0f / (p.sP * p.sQ)));
+  } else {  // EPI_PH
+    const float4 g = f4_axpy(p.a, ld4(p.Hf, o1), 1.0f, scale4(acc, 1.0f / (p.sP * p.sH)));
+    st4f(p.Gf, o1, g, klo, khi);
+    if constexpr (!F32PATH) st4h(p.Gh, o1, g, p.sG, false, klo, khi);
+    return;
+  }
+  // Q output (POLY on the first iteration, or the PQ product)
+  if constexpr (F32PATH) {
+    st4f(p.Qf_dst, o1, v, klo, khi);
+  } else {
+    if (p.last) {  // operand of the final bf16 product, unscaled
+      st4h(p.Qh_dst, o1, v, 1.0f, true, klo, khi);
+    } else {
+      st4f(p.Qf_dst, o1, v, klo, khi);
+      st4h(p.Qh_dst, o1, v, p.sQ, false, klo, khi);
+    }
+  }
+}
+
 // The 256-tile kernels fold the identity term of each r x r product into
 // the accumulators while the product runs (acc += gamma * X, X the raw fp16
 // identity-term operand), so the epilogue only scales: v = beta * acc.
