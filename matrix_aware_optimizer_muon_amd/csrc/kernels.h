@@ -70,6 +70,19 @@ hipError_t launch_gemm(const GemmParams& p, int epi, int op, int bt, int nmat, h
 // 256-tile 16-bit products with the direct-to-LDS pipeline (gemm_dma.hip)
 hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s);
 
+// The whole r x r recursion in one launch for r_pad <= 128 (rr_fused.hip):
+// reads G0 (fp32, from the SYRK), writes the last Q as bf16.
+struct RrFusedParams {
+  const float* Gf;         // G0 per matrix, r_pad x r_pad fp32
+  int64_t rr_stride;       // elements between matrices (Gf and Qout)
+  int r_pad;               // 64 or 128
+  void* Qout;              // bf16 Q_N per matrix, r_pad x r_pad
+  float a, b, c;           // quintic coefficients
+  float sG, sP, sQ, sH;    // power-of-two operand scales
+  int N;                   // iterations
+};
+hipError_t launch_rr_fused(const RrFusedParams& p, int nmat, hipStream_t s);
+
 // ---- memory-bound kernels ------------------------------------------------
 struct PrepParams {
   const MatPtrs* table;

@@ -848,7 +848,28 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
                    [&] { return gemm(g, EPI_SYRK); });
         if (st != MUON_OK) return st;
 
-        for (int k = 0; k < N; ++k) {
+        // r_pad <= 128 on the 16-bit path: the whole recursion in one launch
+        // (one workgroup per matrix) instead of up to 17 dependent launches
+        const bool fused_rr = !f32path && !B.dma && B.r_pad <= 128;
+        if (fused_rr) {
+          RrFusedParams fp{};
+          fp.Gf = Gf;
+          fp.rr_stride = rr_stride;
+          fp.r_pad = (int)B.r_pad;
+          fp.Qout = Qh[(N - 1) & 1];
+          fp.a = hp.a;
+          fp.b = hp.b;
+          fp.c = hp.c;
+          fp.sG = g.sG;
+          fp.sP = g.sP;
+          fp.sQ = g.sQ;
+          fp.sH = g.sH;
+          fp.N = N;
+          st = timed(p, stream, MUON_K_POLY, (4.0 * N - 3.0) * r3 * nm, 0.0,
+                     [&] { return launch_rr_fused(fp, nm, stream); });
+          if (st != MUON_OK) return st;
+        }
+        for (int k = 0; k < (fused_rr ? 0 : N); ++k) {
           const int dst = k & 1, src = dst ^ 1;
           g.first = k == 0;
           g.last = k == N - 1;

@@ -1,0 +1,274 @@
+// The whole r x r Newton-Schulz recursion of the Gram form ("DMuon" 2.2,
+// "Infra Optimizers" eq. (2)) in one launch for buckets with r_pad <= 128,
+// one workgroup per matrix.  At that size every product is a few dozen MFMAs
+// per wave and the launch-by-launch sequence (up to 17 dependent launches)
+// is bound by launch latency, not by work.
+//
+// Same arithmetic as the small-tile kernels' epilogues (gemm_epilogue.hpp),
+// same operand formats and power-of-two scales: per iteration k
+//   POLY  S = G G                 P~ = b G + c S, P^ = fp16(P~ sP)
+//                                 (k = 0: Q = a I + P~)
+//   PQ    (k > 0)                 Q  = a Q + P~ Q
+//   PG    (k < N-1)               H  = a G + P~ G
+//   PH    (k < N-1)               G  = a H + P~ H
+// with fp32 masters of G, Q, H and fp16 MFMA operands G^ = fp16(G sG),
+// Q^ = fp16(Q sQ), H^ = fp16(H sH); the last Q is written as bf16, the
+// operand of the final product.
+//
+// Layout: 256 threads = 4 wave64 in 2 x 2, each wave owning an (RP/2)^2
+// quadrant of every product as 32x32 blocks (32x32x16 fp16 MFMAs).  The fp32
+// masters stay in registers in the accumulator layout (lane (h, l32) of block
+// (i, j) holds rows 8(v>>2) + 4h + (v&3), column l32).  The four fp16
+// operands live in LDS, row-major with the 16-byte chunk index XOR-swizzled
+// by the row; a lane writes its four consecutive rows of column l32 as four
+// consecutive elements of LDS row l32, i.e. the LDS copy holds the transpose,
+// which is the same matrix (every matrix of the recursion is symmetric up to
+// rounding).  Exact symmetry is restored after every update: the Gram
+// recursion G <- P G P amplifies an antisymmetric rounding component by about
+// a^2 per iteration (simulated on a 3 x 5 input: 0.74 relative error after
+// N = 5 without, 1.4e-3 with), so each new fp32 master is replaced by the
+// mean of itself and its transpose through an fp32 LDS exchange (the tile
+// kernels get exact symmetry by storing lower tiles and their mirror).
+// LDS: three fp16 operands (G^ and H^ share a buffer: G^ is dead once PQ and
+// PG have read it) and a half-matrix fp32 exchange, RP = 128: 96 + 33 KB.
+#include "common.hpp"
+#include "kernels.h"
+
+namespace muon {
+
+namespace {
+
+template <int RP>
+struct RrLds {
+  static constexpr int NCH = RP / 8;  // 16-byte chunks per row
+  // byte offset of chunk ch of row r
+  __device__ static __forceinline__ int off(int r, int ch) { return r * RP * 2 + ((ch ^ (r & (NCH - 1))) << 4); }
+};
+
+__device__ __forceinline__ uint32_t pk_h2(float a, float b) {
+  return (uint32_t)f32_to_f16_bits(a) | ((uint32_t)f32_to_f16_bits(b) << 16);
+}
+__device__ __forceinline__ uint32_t pk_b2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+}  // namespace
+
+template <int RP>
+__global__ void __launch_bounds__(256, 1) rr_fused_kernel(const RrFusedParams p) {
+  constexpr int WT = RP / 2;          // wave quadrant
+  constexpr int F = WT / 32;          // 32x32 blocks per quadrant dimension
+  constexpr int MB = RP * RP * 2;     // bytes of one fp16 matrix
+  constexpr int XP = RP + 1;           // fp32 exchange pitch (bank spread)
+  __shared__ __attribute__((aligned(16))) char smem[3 * MB + WT * XP * 4];
+  char* bG = smem;                    // G^, or H^ between PG and PH
+  char* bP = smem + MB;
+  char* bQ = smem + 2 * MB;
+  float* xch = (float*)(smem + 3 * MB);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int mat = blockIdx.x;
+
+  // element (row, col) of accumulator value v of block (i, j)
+  auto row_of = [&](int i, int v) { return wm * WT + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3); };
+  auto col_of = [&](int j) { return wn * WT + j * 32 + l32; };
+
+  // exact symmetry: every element becomes the mean of itself and its mirror
+  // (fp32 addition commutes and halving is exact, so (r, c) and (c, r) get
+  // the same value).  The exchange holds WT rows at a time (pitch RP + 1:
+  // a row write and a column read by 32 lanes both touch 32 banks): in half
+  // hf the waves owning rows [hf WT, hf WT + WT) write them, and the waves
+  // whose columns lie in that range read their mirrors.
+  auto symm = [&](f32x16 (*m)[F]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      if (wm == hf) {
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) xch[(row_of(i, v) - hf * WT) * XP + col_of(j)] = m[i][j][v];
+      }
+      __syncthreads();
+      if (wn == hf) {
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+#pragma unroll
+          for (int j = 0; j < F; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              m[i][j][v] = 0.5f * (m[i][j][v] + xch[(col_of(j) - hf * WT) * XP + row_of(i, v)]);
+      }
+      __syncthreads();
+    }
+  };
+
+  // fp16 copy of a (symmetric) master into an LDS matrix: lane's rows
+  // r0..r0+3 of column c become elements r0..r0+3 of LDS row c (one 8-byte
+  // write per group)
+  auto put = [&](char* buf, const f32x16 (*m)[F], float scale) {
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = wm * WT + i * 32 + 8 * g + 4 * h;
+          const int c = col_of(j);
+          const uint2 v = make_uint2(pk_h2(m[i][j][4 * g] * scale, m[i][j][4 * g + 1] * scale),
+                                     pk_h2(m[i][j][4 * g + 2] * scale, m[i][j][4 * g + 3] * scale));
+          *(uint2*)(buf + RrLds<RP>::off(c, r0 >> 3) + ((r0 & 7) << 1)) = v;
+        }
+  };
+
+  // acc = A * B^T over K = RP, both operands in LDS
+  auto mm = [&](const char* A, const char* B, f32x16 (*acc)[F]) {
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < RP / 16; ++ks) {
+      u32x4 af[F], bf[F];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        af[f] = *(const u32x4*)(A + RrLds<RP>::off(wm * WT + f * 32 + l32, 2 * ks + h));
+        bf[f] = *(const u32x4*)(B + RrLds<RP>::off(wn * WT + f * 32 + l32, 2 * ks + h));
+      }
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, af[i]),
+                                                             __builtin_bit_cast(f16x8, bf[j]),
+                                                             acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // bf16 Q (the final product's operand) to global memory
+  auto put_q_out = [&](const f32x16 (*m)[F]) {
+    uint16_t* q = (uint16_t*)p.Qout + (size_t)mat * p.rr_stride;
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int r0 = wm * WT + i * 32 + 8 * g + 4 * h;
+          const int c = col_of(j);
+          *(uint2*)(q + (size_t)c * RP + r0) =
+              make_uint2(pk_b2(m[i][j][4 * g], m[i][j][4 * g + 1]), pk_b2(m[i][j][4 * g + 2], m[i][j][4 * g + 3]));
+        }
+  };
+
+  // fp32 masters: G (H between PG and PH, which replaces it) and Q; P~ is
+  // formed in place in the accumulators
+  f32x16 Gm[F][F], Qm[F][F], acc[F][F];
+  {
+    const float* g0 = p.Gf + (size_t)mat * p.rr_stride;
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) Gm[i][j][v] = g0[(size_t)row_of(i, v) * RP + col_of(j)];
+  }
+  put(bG, Gm, p.sG);  // G0 from the SYRK is stored exactly symmetric
+  __syncthreads();
+
+  const float inv_gg = 1.0f / (p.sG * p.sG);
+  const float inv_pq = 1.0f / (p.sP * p.sQ);
+  const float inv_pg = 1.0f / (p.sP * p.sG);
+  const float inv_ph = 1.0f / (p.sP * p.sH);
+  for (int k = 0; k < p.N; ++k) {
+    const bool first = k == 0, last = k == p.N - 1;
+    // POLY: P~ = b G + c G^2, and Q1 = a I + P~
+    mm(bG, bG, acc);
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+      for (int j = 0; j < F; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float s2 = acc[i][j][v] * inv_gg;
+          acc[i][j][v] = p.b * Gm[i][j][v] + p.c * s2;
+        }
+    symm(acc);
+    put(bP, acc, p.sP);
+    if (first) {
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            Qm[i][j][v] = acc[i][j][v] + (row_of(i, v) == col_of(j) ? p.a : 0.0f);
+      if (last) put_q_out(Qm);
+      else put(bQ, Qm, p.sQ);
+    }
+    __syncthreads();
+    if (!first) {
+      // PQ: Q = a Q + P~ Q
+      mm(bP, bQ, acc);
+      __syncthreads();  // every read of Q^ is done before it is replaced
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) Qm[i][j][v] = p.a * Qm[i][j][v] + acc[i][j][v] * inv_pq;
+      symm(Qm);
+      if (last) put_q_out(Qm);
+      else put(bQ, Qm, p.sQ);
+    }
+    if (!last) {
+      // PG: H = a G + P~ G (in Gm), then PH: G = a H + P~ H
+      mm(bP, bG, acc);
+      __syncthreads();  // every read of G^ is done before H^ replaces it
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) Gm[i][j][v] = p.a * Gm[i][j][v] + acc[i][j][v] * inv_pg;
+      symm(Gm);
+      put(bG, Gm, p.sH);
+      __syncthreads();
+      mm(bP, bG, acc);
+      __syncthreads();  // every read of H^ is done before G^ replaces it
+#pragma unroll
+      for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) Gm[i][j][v] = p.a * Gm[i][j][v] + acc[i][j][v] * inv_ph;
+      symm(Gm);
+      put(bG, Gm, p.sG);
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_rr_fused(const RrFusedParams& p, int nmat, hipStream_t s) {
+  if (nmat <= 0) return hipSuccess;
+  if (p.N < 1) return hipErrorInvalidValue;
+  switch (p.r_pad) {
+    case 64:
+      hipLaunchKernelGGL((rr_fused_kernel<64>), dim3((uint32_t)nmat), dim3(256), 0, s, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((rr_fused_kernel<128>), dim3((uint32_t)nmat), dim3(256), 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace muon
