@@ -73,6 +73,11 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    # torch first: it brings the HIP runtime the process uses (its bundled
+    # copy), which libmuon.so then binds to.  Loaded first, libmuon.so would
+    # pull in the system copy as well, and one of the two runtimes then finds
+    # no device (hipHostMalloc: "no ROCm-capable device is detected").
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     lib.muon_default_hparams.argtypes = [ctypes.POINTER(Hparams)]
