@@ -140,6 +140,18 @@ __device__ __forceinline__ void store16x4(uint16_t* base, size_t o, uint2 v, int
     if (k >= lo && k < hi) base[o + k] = e[k];
 }
 
+// Store elements [lo, 8) of eight packed 16-bit values (v0: 0..3, v1: 4..7)
+// at base + o: one non-temporal 16-byte store when all eight go.
+__device__ __forceinline__ void store16x8(uint16_t* base, size_t o, uint2 v0, uint2 v1, int lo) {
+  if (lo == 0) {
+    const u32x4 x = {v0.x, v0.y, v1.x, v1.y};
+    __builtin_nontemporal_store(x, (u32x4*)(base + o));
+    return;
+  }
+  store16x4(base, o, v0, min(lo, 4), 4);
+  store16x4(base, o + 4, v1, max(lo - 4, 0), 4);
+}
+
 // Q1 = a I + P~ from four staged P~ values (fp16, scaled by 1/inv_sp):
 // element `dk` (if 0..3) lies on the diagonal.  Output in Q's format.
 __device__ __forceinline__ uint2 q_from_p(uint2 pv, float inv_sp, const GemmParams& p, int dk) {
@@ -524,17 +536,26 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
         if (qout) store16x4(out2, o, q_from_p(row, inv_s1, p, diag ? il - jc : -1), 0, n);
       }
     }
+    // mirror pass: two staged columns per iteration, half a wave each; lane
+    // k of a half takes chunks 2k and 2k + 1 (tile rows 8k..8k+7), which sit
+    // in slots s and s ^ 1 (s = 2k ^ f(c)) of one aligned 16-byte pair, and
+    // stores them as eight consecutive elements of mirrored row c
     constexpr int CPW = 256 / NW;  // mirrored rows per wave
 #pragma unroll 4
-    for (int it = 0; it < CPW; ++it) {
-      const int jc = wave * CPW + it;
-      const uint2 v = *(const uint2*)(smem + t_off(jc, lane));
-      const int il0 = 4 * lane;
+    for (int it = 0; it < CPW / 2; ++it) {
+      const int jc = wave * CPW + 2 * it + (lane >> 5);
+      const int k = lane & 31;
+      const int sl = (2 * k) ^ (((jc >> 2) ^ ((jc & 3) << 3)) & 31);
+      const uint4 w = *(const uint4*)(smem + jc * 512 + ((sl & ~1) << 3));
+      const bool sw = sl & 1;
+      const uint2 v0 = sw ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);  // rows 8k..8k+3
+      const uint2 v1 = sw ? make_uint2(w.x, w.y) : make_uint2(w.z, w.w);  // rows 8k+4..8k+7
+      const int il0 = 8 * k;
       const size_t o = mb + (size_t)(row0B + jc) * ldm + (row0A + il0);
       // diagonal tile: rows il0 + e > jc only (strictly lower in the tile)
-      const int s0 = diag ? min(max(jc - il0 + 1, 0), 4) : 0;
-      store16x4(outm, o, v, s0, 4);
-      if (qout) store16x4(out2, o, q_from_p(v, inv_s1, p, -1), s0, 4);
+      const int s0 = diag ? min(max(jc - il0 + 1, 0), 8) : 0;
+      store16x8(outm, o, v0, v1, s0);
+      if (qout) store16x8(out2, o, q_from_p(v0, inv_s1, p, -1), q_from_p(v1, inv_s1, p, -1), s0);
     }
   }
 }
