@@ -100,6 +100,43 @@ def read_traffic(workload: str, root: str):
     return out
 
 
+def mfma_table(path, workload, command, xcds):
+    """Per kernel class: MfmaUtil (rocprofv3's derived metric: MFMA-busy
+    cycles over GPU-busy cycles x SIMDs, duration-weighted), executed MFMA
+    flops per second (SQ_INSTS_VALU_MFMA_MOPS_{F16,BF16} x 512) and the clock
+    implied by GRBM_GUI_ACTIVE over the dispatch duration (the counter is
+    summed over the XCDs)."""
+    per = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        d = per[int(r["Dispatch_Id"])]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_name"] = r["Kernel_Name"]
+        d["_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    agg = collections.OrderedDict()
+    for d in per.values():
+        cls = kernel_class(d["_name"])
+        if cls is None or d["_s"] <= 0:
+            continue
+        a = agg.setdefault(cls, [0, 0.0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += d["_s"]
+        a[2] += d.get("MfmaUtil", 0.0) * d["_s"]
+        a[3] += (d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)) * 512
+        a[4] += d.get("GRBM_GUI_ACTIVE", 0.0)
+    print(f"# MFMA utilisation per launch class: {workload}\n")
+    print("Counter run (GPU box, repo root), one refresh step:\n")
+    print(f"```\n{command}\n```\n")
+    print(f"kernel source hash: `{source_hash()}`\n")
+    print("MfmaUtil is relative to the running clock; the clock column is only "
+          "meaningful for launches much longer than the counter window's overhead "
+          "(not for the ~20 us norm launches).\n")
+    print("| class | launches | avg ms | MfmaUtil % | executed MFMA TFLOP/s | clock GHz |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for cls, (n, sec, u, fl, g) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"| {cls} | {n} | {sec * 1e3 / n:.3f} | {u / sec:.1f} | {fl / sec / 1e12:.1f} | "
+              f"{g / xcds / sec / 1e9:.2f} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -108,6 +145,11 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     sub.add_parser("hash")
+    mf = sub.add_parser("mfma")
+    mf.add_argument("--csv", required=True)
+    mf.add_argument("--workload", required=True)
+    mf.add_argument("--command", required=True)
+    mf.add_argument("--xcds", type=int, default=8)
     k = sub.add_parser("trace")
     k.add_argument("--stats", required=True)
     k.add_argument("--title", required=True)
@@ -115,6 +157,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "hash":
         print(source_hash())
+        return
+    if a.cmd == "mfma":
+        mfma_table(a.csv, a.workload, a.command, a.xcds)
         return
     if a.cmd == "trace":
         rows = list(csv.DictReader(open(a.stats)))
