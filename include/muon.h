@@ -171,6 +171,9 @@ typedef struct {
   int tile;                  /* 64, 128 or 256                               */
   muon_formulation formulation; /* MUON_FORM_GRAM or MUON_FORM_DIRECT        */
   int transposed;            /* 1 iff rows > cols (X0 = U^T)                 */
+  int fused_recursion;       /* 1: the Gram form's whole r x r recursion runs
+                                as one launch, one workgroup per matrix (16-bit
+                                path, tiles below 256, r padded to <= 128)   */
 } muon_bucket_info;
 
 /* Fill *info for one bucket.  MUON_ERR_INVALID_ARGUMENT for a NULL plan or

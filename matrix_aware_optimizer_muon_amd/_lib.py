@@ -52,7 +52,7 @@ class BucketHint(ctypes.Structure):
 class BucketInfo(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("count", ctypes.c_int64),
                 ("chunks", ctypes.c_int64), ("tile", ctypes.c_int), ("formulation", ctypes.c_int),
-                ("transposed", ctypes.c_int)]
+                ("transposed", ctypes.c_int), ("fused_recursion", ctypes.c_int)]
 
 
 class PlanDesc(ctypes.Structure):
@@ -186,7 +186,8 @@ class Plan:
                 raise MuonError(st, "muon_plan_bucket_info")
             out.append({"shape": (int(b.rows), int(b.cols)), "count": int(b.count),
                         "chunks": int(b.chunks), "tile": int(b.tile),
-                        "formulation": names[int(b.formulation)], "transposed": bool(b.transposed)})
+                        "formulation": names[int(b.formulation)], "transposed": bool(b.transposed),
+                        "fused": bool(b.fused_recursion)})
         return out
 
     def _call(self, fn, name, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream, out):

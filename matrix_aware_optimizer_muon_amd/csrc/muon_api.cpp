@@ -75,6 +75,7 @@ struct Bucket {
   bool transposed;
   bool dma;  // 256-tile direct-to-LDS path with fp16-only r x r buffers
   bool direct;  // direct form (eq. (2) on X)
+  bool fused_rr;  // Gram form with the whole r x r recursion in one launch
   int bt;
   int first, count;  // range in plan order
   std::vector<Chunk> chunks;
@@ -462,6 +463,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       const int64_t xes = f32path ? 4 : 2;
       const int64_t rr = B.r_pad * B.r_pad;
       B.dma = !f32path && B.bt == 256;
+      B.fused_rr = !f32path && !B.dma && !B.direct && B.r_pad <= 128;
       // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
       // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
       // the 256-tile path keeps only the fp16 copies
@@ -569,6 +571,7 @@ muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_i
   info->tile = B.bt;
   info->formulation = B.direct ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
   info->transposed = B.transposed ? 1 : 0;
+  info->fused_recursion = B.fused_rr ? 1 : 0;
   return MUON_OK;
 }
 
@@ -850,7 +853,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
 
         // r_pad <= 128 on the 16-bit path: the whole recursion in one launch
         // (one workgroup per matrix) instead of up to 17 dependent launches
-        const bool fused_rr = !f32path && !B.dma && B.r_pad <= 128;
+        const bool fused_rr = B.fused_rr;
         if (fused_rr) {
           RrFusedParams fp{};
           fp.Gf = Gf;

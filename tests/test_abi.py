@@ -86,6 +86,19 @@ def test_plan_buckets_and_chunks():
     assert p2.info() == (2, 2)
 
 
+def test_fused_recursion_rule():
+    # the one-launch r x r recursion: Gram form on the 16-bit path with tiles
+    # below 256 and r padded to <= 128
+    b2 = {tuple(b["shape"]): b for b in L.Plan(WL.config(2).shapes).buckets()}
+    assert b2[(128, 3584)]["fused"] and b2[(128, 3584)]["tile"] == 64
+    assert not b2[(256, 256)]["fused"]  # square: direct form
+    assert not any(b["fused"] for b in L.Plan(WL.config(3).shapes).buckets())
+    assert not L.Plan([(128, 3584)], ns_dtype="f32").buckets()[0]["fused"]  # fp32 path
+    assert L.Plan([(3584, 64)]).buckets()[0]["fused"]  # tall: r = 64
+    assert not L.Plan([(200, 900)]).buckets()[0]["fused"]  # r_pad = 256
+    assert L.Plan([(64, 64)], formulation="gram").buckets()[0]["fused"]
+
+
 def test_default_cap_keeps_the_qwen_buckets_whole():
     # The default 32 GiB scratch cap holds the largest Qwen2.5-7B bucket
     # (56 x 18944 x 3584, ~401 MB of scratch per matrix) in one chunk; a
