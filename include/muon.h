@@ -34,7 +34,10 @@
  *     concurrently on up to 4 internal streams of the plan (default
  *     priority, created on the first such call, destroyed with the plan):
  *     they wait for `stream` on entry and `stream` waits for all of them on
- *     return, so the call behaves as one operation on `stream`.
+ *     return, so the call behaves as one operation on `stream`.  Each
+ *     internal stream's launches are enqueued from its own short-lived host
+ *     thread, joined before the call returns (one thread per call when the
+ *     launch profiler is on).
  *   - Errors: all validation happens on the host before anything is
  *     enqueued.  On any status other than MUON_OK and MUON_ERR_HIP nothing
  *     was enqueued and no memory was touched.  MUON_ERR_HIP means a HIP
