@@ -6,90 +6,26 @@
 
 namespace muon {
 
-template <bool F32PATH>
-__device__ __forceinline__ void store_hat(void* base, size_t o, float v) {
-  if constexpr (F32PATH) {
-    ((float*)base)[o] = v;
-  } else {
-    ((uint16_t*)base)[o] = f32_to_f16_bits(v);
-  }
-}
-
-// Epilogue value for one accumulator element at global (gi, gj) of matrix
-// `mat`; it also performs the stores for the element itself.  The mirrored
-// element (gj, gi) of a symmetric result is stored by a second call with the
-// indices swapped, which recomputes the identical value from the transposed
-// read (all r x r inputs are stored exactly symmetric).
-template <int EPI, bool F32PATH>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int mat, int prod, int gi, int gj,
-                                         float acc) {
-  if constexpr (EPI == EPI_FINAL) {
-    if (gi < p.out_rows && gj < p.out_cols) {
-      const MatPtrs mp = p.table[mat];
-      const float o = acc * p.inv_norm[mat];
-      const size_t idx = (size_t)gi * p.out_cols + gj;
-      mp.W[idx] = p.decay * mp.W[idx] - p.step * o;
-      if (mp.O) mp.O[idx] = o;
-    }
-    return;
-  } else {
-    const size_t o1 = (size_t)mat * p.rr_stride + (size_t)gi * p.ldr + gj;
-    float v;
-    if constexpr (EPI == EPI_SYRK) {
-      const float inv = p.inv_norm[mat];
-      v = acc * inv * inv;
-      p.Gf[o1] = v;
-      if constexpr (!F32PATH) store_hat<false>(p.Gh, o1, v * p.sG);
-      return;
-    } else if constexpr (EPI == EPI_POLY) {
-      const float g = p.Gf[o1];
-      const float s2 = acc * (1.0f / (p.sG * p.sG));
-      const float pt = p.b * g + p.c * s2;
-      store_hat<F32PATH>(p.Ph, o1, pt * p.sP);
-      if (!p.first) return;
-      v = pt + (gi == gj ? p.a : 0.0f);  // Q1 = P1 = a I + P~
-    } else if constexpr (EPI == EPI_PQPG) {
-      if (prod == 1) {
-        const float hv = p.a * p.Gf[o1] + acc * (1.0f / (p.sP * p.sG));
-        p.Hf[o1] = hv;
-        if constexpr (!F32PATH) store_hat<false>(p.Hh, o1, hv * p.sH);
-        return;
-      }
-      v = p.a * p.Qf_src[o1] + acc * (1.0f / (p.sP * p.sQ));
-    } else {  // EPI_PH
-      const float g = p.a * p.Hf[o1] + acc * (1.0f / (p.sP * p.sH));
-      p.Gf[o1] = g;
-      if constexpr (!F32PATH) store_hat<false>(p.Gh, o1, g * p.sG);
-      return;
-    }
-    // Q output (POLY on the first iteration, or the PQ product)
-    if constexpr (F32PATH) {
-      p.Qf_dst[o1] = v;
-    } else {
-      if (p.last) {  // operand of the final bf16 product, unscaled
-        ((uint16_t*)p.Qh_dst)[o1] = f32_to_bf16_bits(v);
-      } else {
-        p.Qf_dst[o1] = v;
-        store_hat<false>(p.Qh_dst, o1, v * p.sQ);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Helpers of the 256-tile path (gemm_dma.hip), which keeps no fp32 master
-// copies of the r x r results.
+// a x + b y, elementwise
 __device__ __forceinline__ float4 f4_axpy(float a, float4 x, float b, float4 y) {
   return make_float4(a * x.x + b * y.x, a * x.y + b * y.y, a * x.z + b * y.z, a * x.w + b * y.w);
 }
 
 // ---------------------------------------------------------------------------
-// Four-column form of `epilogue` for the r x r products: accumulators of
-// (row, col0 + k), k = 0..3, stored for k in [klo, khi) (the rest lies on the
-// other side of the diagonal).  col0 is a multiple of 4 and the padded r x r
-// buffers have a multiple of 4 columns, so every input is one 16-byte load;
-// whole groups store fp32 as 16 bytes and 16-bit copies as 8 bytes.  Each
-// element gets exactly the value the scalar form computes.
+// Epilogues of the small-tile kernel's r x r products, four columns at a
+// time: accumulators of (row, col0 + k), k = 0..3, stored for k in
+// [klo, khi) (the rest lies on the other side of the diagonal).  The mirror
+// pass calls it with row and column swapped and recomputes the identical
+// value from the transposed read (every r x r input is stored exactly
+// symmetric).  col0 is a multiple of 4 and the padded r x r buffers have a
+// multiple of 4 columns, so every input is one 16-byte load; whole groups
+// store fp32 as 16 bytes and 16-bit copies as 8 bytes.
+//   SYRK  G0 = acc / ||U||^2                      fp32 G, fp16 G^ = G sG
+//   POLY  P~ = b G + c acc / sG^2                 fp16 P^ = P~ sP; first: Q = a I + P~
+//   PQPG  H = a G + acc / (sP sG)   (product 1)   fp32 H, fp16 H^ = H sH
+//         Q = a Q + acc / (sP sQ)   (product 0)   fp32 Q, fp16 Q^ = Q sQ (bf16 Q when last)
+//   PH    G = a H + acc / (sP sH)                 fp32 G, fp16 G^
+// (the fp32 path keeps fp32 operand copies: every scale is 1)
 __device__ __forceinline__ float4 ld4(const float* b, size_t o) { return *(const float4*)(b + o); }
 __device__ __forceinline__ float f4at(const float4& v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
@@ -168,6 +104,10 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int mat, int prod
   }
 }
 
+// ---------------------------------------------------------------------------
+// Helpers of the 256-tile path (gemm_dma.hip), which keeps no fp32 master
+// copies of the r x r results.
+//
 // The 256-tile kernels fold the identity term of each r x r product into
 // the accumulators while the product runs (acc += gamma * X, X the raw fp16
 // identity-term operand), so the epilogue only scales: v = beta * acc.
