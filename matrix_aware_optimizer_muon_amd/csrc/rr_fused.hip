@@ -81,7 +81,12 @@ __global__ void __launch_bounds__(256, 1) rr_fused_kernel(const RrFusedParams p)
   // the same value).  The exchange holds WT rows at a time (pitch RP + 1:
   // a row write and a column read by 32 lanes both touch 32 banks): in half
   // hf the waves owning rows [hf WT, hf WT + WT) write them, and the waves
-  // whose columns lie in that range read their mirrors.
+  // whose columns lie in that range read their mirrors.  The lower
+  // off-diagonal quadrant (wm > wn) is averaged in half 0 and written as
+  // averaged in half 1, so its mirror, the upper quadrant (wm < wn), takes
+  // those values as they are instead of averaging a second time.
+  const float keep = wm < wn ? 0.0f : 0.5f;  // m <- keep m + take mirror
+  const float take = wm < wn ? 1.0f : 0.5f;
   auto symm = [&](f32x16 (*m)[F]) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -101,7 +106,7 @@ __global__ void __launch_bounds__(256, 1) rr_fused_kernel(const RrFusedParams p)
           for (int j = 0; j < F; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
-              m[i][j][v] = 0.5f * (m[i][j][v] + xch[(col_of(j) - hf * WT) * XP + row_of(i, v)]);
+              m[i][j][v] = keep * m[i][j][v] + take * xch[(col_of(j) - hf * WT) * XP + row_of(i, v)];
       }
       __syncthreads();
     }
