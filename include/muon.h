@@ -152,7 +152,12 @@ muon_status muon_default_hparams(muon_hparams* hp);
  * no device allocation.  On success *plan owns host memory only and
  * *workspace_bytes (nullable) receives the workspace size needed by both
  * step calls.  MUON_ERR_UNSUPPORTED for MUON_FORM_DIRECT with ns_dtype
- * MUON_F32; MUON_ERR_INVALID_ARGUMENT for an unknown formulation. */
+ * MUON_F32; MUON_ERR_INVALID_ARGUMENT for an unknown formulation.
+ * ns_dtype MUON_BF16 keeps every operand of the recursion in fp16 with a
+ * power-of-two scale derived here from (a, b, c) and ns_steps (bounds of the
+ * iterated polynomials over singular values in [0, 1]); it gives
+ * MUON_ERR_UNSUPPORTED when c == 0, |b / c| > 2^60, or a bound needs a scale
+ * below 2^-14 (coefficients whose iteration grows without limit). */
 muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* workspace_bytes);
 
 /* Release a plan.  NULL is accepted.  The caller must ensure no work using
@@ -177,6 +182,9 @@ typedef struct {
   int fused_recursion;       /* 1: the Gram form's whole r x r recursion runs
                                 as one launch, one workgroup per matrix (16-bit
                                 path, tiles below 256, r padded to <= 128)   */
+  float operand_scales[5];   /* fp16 operand scales of G, P~, H, Q and the
+                                direct form's X (plan-wide; all 1 on the fp32
+                                path); see muon_plan                         */
 } muon_bucket_info;
 
 /* Fill *info for one bucket.  MUON_ERR_INVALID_ARGUMENT for a NULL plan or

@@ -52,7 +52,8 @@ class BucketHint(ctypes.Structure):
 class BucketInfo(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("count", ctypes.c_int64),
                 ("chunks", ctypes.c_int64), ("tile", ctypes.c_int), ("formulation", ctypes.c_int),
-                ("transposed", ctypes.c_int), ("fused_recursion", ctypes.c_int)]
+                ("transposed", ctypes.c_int), ("fused_recursion", ctypes.c_int),
+                ("operand_scales", ctypes.c_float * 5)]
 
 
 class PlanDesc(ctypes.Structure):
@@ -187,7 +188,8 @@ class Plan:
             out.append({"shape": (int(b.rows), int(b.cols)), "count": int(b.count),
                         "chunks": int(b.chunks), "tile": int(b.tile),
                         "formulation": names[int(b.formulation)], "transposed": bool(b.transposed),
-                        "fused": bool(b.fused_recursion)})
+                        "fused": bool(b.fused_recursion),
+                        "scales": tuple(float(x) for x in b.operand_scales)})
         return out
 
     def _call(self, fn, name, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream, out):

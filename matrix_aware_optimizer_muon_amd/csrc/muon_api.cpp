@@ -50,16 +50,70 @@ constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
 constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
 constexpr int kRing = 4;                      // pinned descriptor staging slots
 
-// Operand scales (powers of two, exact) of the fp16 r x r recursion.  They
-// keep every operand inside fp16's normal range: eigenvalues of G lie in
-// [0, 1.45] (f^k maps [0, 1] into [0, 1.2025]), of P~ = b G + c G^2 in
-// [-2.81, 0], of H = P G in [0, 5.0], of Q = P_k...P_1 in [0, a^N]; entries
-// are bounded by the largest eigenvalue in magnitude.
-constexpr float kSG = 16384.0f, kSP = 16384.0f, kSH = 8192.0f, kSQ = 64.0f;
-// Direct form: X kept as fp16 scaled by kSX.  X0 = U / ||U||_F has entries of
-// RMS 1/sqrt(r c); every later X has spectral norm <= 1.2025, which bounds
-// its entries (x kSX <= 308).
-constexpr float kSX = 256.0f;
+// Operand scales (powers of two, exact) of the 16-bit Newton-Schulz path.
+// Every matrix of the recursion is a polynomial in X0 X0^T, and X0 = U /
+// ||U||_F has singular values sigma in [0, 1].  With f(s) = a s + b s^3 +
+// c s^5 and p(g) = a + b g + c g^2, iteration k has G with eigenvalues
+// g_k = f^k(sigma)^2, P~ = b G + c G^2 with b g_k + c g_k^2, H = P G with
+// p(g_k) g_k, Q = P_k...P_1 with the product of p(g_j) (a^k at sigma = 0:
+// padding and rank-deficient directions), and the direct form's X with
+// f^k(sigma).  Entries of a symmetric matrix are bounded by its largest
+// |eigenvalue|, so each scale is the largest power of two that keeps
+// 1.05 x bound inside fp16's range, capped at the value that suits the
+// default coefficients (for them only the Q scale depends on N: 64 up to
+// N = 5, since a^5 = 484).  The bounds are taken over a grid of sigma in
+// [0, 1.01] (bf16 rounding of X0 may lift sigma above 1).
+constexpr float kSG = 16384.0f, kSP = 16384.0f, kSH = 8192.0f, kSQ = 64.0f, kSX = 256.0f;
+constexpr double kF16Max = 65504.0;
+constexpr float kMinScale = 1.0f / 16384.0f;  // below: too few fp16 bits left
+
+struct NsScales {
+  float sG = 1.0f, sP = 1.0f, sH = 1.0f, sQ = 1.0f, sX = 1.0f;
+};
+
+float pow2_fit(double bound, float cap) {
+  if (!(bound > 0.0)) return cap;  // identically zero: any scale fits
+  if (!std::isfinite(bound)) return 0.0f;
+  const double lim = kF16Max / (1.05 * bound);
+  float s = cap;
+  while (s > kMinScale / 2 && (double)s > lim) s *= 0.5f;
+  return s;
+}
+
+// MUON_ERR_UNSUPPORTED when the coefficients leave a bound beyond what a
+// power-of-two fp16 scale can hold, or when c == 0 (the 256-tile quintic
+// product folds b G into c G^2 as (b / c) G).
+muon_status ns_scales(const muon_hparams& hp, NsScales* out) {
+  const double a = hp.a, b = hp.b, c = hp.c;
+  if (c == 0.0 || !std::isfinite(b / c) || std::fabs(b / c) > 0x1p60) return MUON_ERR_UNSUPPORTED;
+  const int N = hp.ns_steps;
+  double bg = 0.0, bp = 0.0, bh = 0.0, bq = 0.0, bx = 0.0;
+  constexpr int kGrid = 8192;
+  for (int i = 0; i <= kGrid; ++i) {
+    double x = 1.01 * i / kGrid, q = 1.0;
+    bx = std::max(bx, std::fabs(x));
+    for (int k = 0; k < N; ++k) {
+      const double g = x * x, pk = a + b * g + c * g * g;
+      bg = std::max(bg, g);
+      bp = std::max(bp, std::fabs(b * g + c * g * g));
+      if (k < N - 1) bh = std::max(bh, std::fabs(pk * g));
+      q *= pk;
+      bq = std::max(bq, std::fabs(q));
+      x *= pk;
+      bx = std::max(bx, std::fabs(x));
+    }
+  }
+  NsScales s;
+  s.sG = pow2_fit(bg, kSG);
+  s.sP = pow2_fit(bp, kSP);
+  s.sH = pow2_fit(bh, kSH);
+  s.sQ = pow2_fit(bq, kSQ);
+  s.sX = pow2_fit(bx, kSX);
+  for (float v : {s.sG, s.sP, s.sH, s.sQ, s.sX})
+    if (!(v >= kMinScale)) return MUON_ERR_UNSUPPORTED;
+  *out = s;
+  return MUON_OK;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -105,6 +159,7 @@ struct muon_plan_s {
   muon_dtype ns_dtype = MUON_BF16;
   int formulation = MUON_FORM_AUTO;  // as requested; resolved per bucket
   muon_hparams hp{};
+  NsScales scales;  // operand scales of the 16-bit path (all 1 on the fp32 path)
   std::vector<int64_t> rows, cols;
   std::vector<int> order;  // plan position -> caller index
   std::vector<Bucket> buckets;
@@ -398,6 +453,11 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
   if (form == MUON_FORM_DIRECT && desc->ns_dtype == MUON_F32) return MUON_ERR_UNSUPPORTED;
   muon_status st = validate_hp(desc->hp);
   if (st != MUON_OK) return st;
+  NsScales scales;
+  if (desc->ns_dtype == MUON_BF16) {
+    st = ns_scales(desc->hp, &scales);
+    if (st != MUON_OK) return st;
+  }
   for (int64_t i = 0; i < desc->num_matrices; ++i) {
     const int64_t m = desc->rows[i], n = desc->cols[i];
     if (m < 1 || n < 1) return MUON_ERR_INVALID_ARGUMENT;
@@ -412,6 +472,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
     p->grad_dtype = desc->grad_dtype;
     p->ns_dtype = desc->ns_dtype;
     p->hp = desc->hp;
+    p->scales = scales;
     p->rows.assign(desc->rows, desc->rows + desc->num_matrices);
     p->cols.assign(desc->cols, desc->cols + desc->num_matrices);
     const bool f32path = desc->ns_dtype == MUON_F32;
@@ -572,6 +633,9 @@ muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_i
   info->formulation = B.direct ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
   info->transposed = B.transposed ? 1 : 0;
   info->fused_recursion = B.fused_rr ? 1 : 0;
+  const NsScales& sc = plan->scales;
+  const float scales[5] = {sc.sG, sc.sP, sc.sH, sc.sQ, sc.sX};
+  std::memcpy(info->operand_scales, scales, sizeof scales);
   return MUON_OK;
 }
 
@@ -724,14 +788,10 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         g.a = hp.a;
         g.b = hp.b;
         g.c = hp.c;
-        if (f32path) {
-          g.sG = g.sP = g.sQ = g.sH = 1.0f;
-        } else {
-          g.sG = kSG;
-          g.sP = kSP;
-          g.sQ = kSQ;
-          g.sH = kSH;
-        }
+        g.sG = p->scales.sG;  // all 1 on the fp32 path
+        g.sP = p->scales.sP;
+        g.sQ = p->scales.sQ;
+        g.sH = p->scales.sH;
         g.inv_norm = d_inv + ch.first;
         g.table = d_table + ch.first;
         g.Gf = Gf;
@@ -754,22 +814,22 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         };
 
         if (B.direct) {
-          // X0 = U / ||U||, in place, as fp16 scaled by kSX
+          // X0 = U / ||U||, in place, as fp16 scaled by sX
           XcastParams xc{};
           xc.Xn = Xnat;
           xc.Xt = Xtr;
           xc.x_stride = x_stride;
           xc.elems = B.m_pad * B.n_pad;
           xc.inv_norm = d_inv + ch.first;
-          xc.sx = kSX;
+          xc.sx = p->scales.sX;
           st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
                      [&] { return launch_xcast(xc, nm, stream); });
           if (st != MUON_OK) return st;
           void* Xn[2] = {Xnat, Xn2};
           void* Xt[2] = {Xtr, Xt2};
           g.xkind = 1;
-          g.syrk_scale = 1.0f / (kSX * kSX);
-          g.sX = kSX;
+          g.syrk_scale = 1.0f / (p->scales.sX * p->scales.sX);
+          g.sX = p->scales.sX;
           g.first = g.last = 0;
           const int tm = (int)(B.r_pad / 256), tn = (int)(B.c_pad / 256);
           for (int k = 0; k < N; ++k) {
@@ -828,7 +888,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
           wp.m = (int)B.m;
           wp.n = (int)B.n;
           wp.n_pad = (int)B.n_pad;
-          wp.inv_sx = 1.0f / kSX;
+          wp.inv_sx = 1.0f / p->scales.sX;
           wp.decay = (float)(1.0 - (double)lr * wd);
           wp.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
           st = timed(p, stream, MUON_K_WUPD, 0.0, 10.0 * (double)B.m * B.n * nm,

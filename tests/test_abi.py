@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from matrix_aware_optimizer_muon_amd import _lib as L
@@ -97,6 +98,53 @@ def test_fused_recursion_rule():
     assert L.Plan([(3584, 64)]).buckets()[0]["fused"]  # tall: r = 64
     assert not L.Plan([(200, 900)]).buckets()[0]["fused"]  # r_pad = 256
     assert L.Plan([(64, 64)], formulation="gram").buckets()[0]["fused"]
+
+
+def _scales(n, ns_dtype="bf16", **coef):
+    hp = L.default_hparams()
+    hp.ns_steps = n
+    for k, v in coef.items():
+        setattr(hp, k, v)
+    return L.Plan([(100, 900)], ns_dtype=ns_dtype, hp=hp).buckets()[0]["scales"]
+
+
+def test_operand_scales_follow_the_iteration_bounds():
+    # Default coefficients: p(g) = a + b g + c g^2 peaks at g = 0 on the
+    # singular-value range, so Q = P_N...P_1 is bounded by a^N (reached in
+    # padding and rank-deficient directions) and its fp16 scale is the
+    # largest power of two with 1.05 a^N s <= 65504, capped at 64; the other
+    # bounds do not depend on N and keep their scales.
+    a = float(np.float32(3.4445))
+    assert _scales(5) == (16384.0, 16384.0, 8192.0, 64.0, 256.0)
+    for n in range(1, 17):
+        expect = 64.0
+        while 1.05 * a ** n * expect > 65504.0:
+            expect /= 2
+        s = _scales(n)
+        assert s[3] == expect, (n, s)
+        assert (s[0], s[1], s[4]) == (16384.0, 16384.0, 256.0)
+    assert _scales(8)[3] == 2.0 and _scales(16)[3] == 2.0 ** -13
+    assert _scales(5, ns_dtype="f32") == (1.0,) * 5
+
+
+def test_coefficients_the_16bit_path_cannot_scale():
+    # c = 0 (a cubic): the 256-tile quintic product folds b G into c G^2 as
+    # (b / c) G; the fp32 path takes it
+    assert plan_status([(4, 4)], hp=_hp(c=0.0)) == L.MUON_ERR_UNSUPPORTED
+    assert plan_status([(4, 4)], ns_dtype="f32", hp=_hp(c=0.0)) == 0
+    # an iteration that grows without limit (f(1) = 4 and beyond): no fp16
+    # scale holds it
+    assert plan_status([(4, 4)], hp=_hp(a=2.0, b=1.0, c=1.0)) == L.MUON_ERR_UNSUPPORTED
+    # the cubic of classic Newton-Schulz written as a quintic with a tiny c
+    s = _scales(5, a=1.5, b=-0.5, c=1e-6)
+    assert all(v >= 2.0 ** -14 for v in s)
+
+
+def _hp(**coef):
+    hp = L.default_hparams()
+    for k, v in coef.items():
+        setattr(hp, k, v)
+    return hp
 
 
 def test_default_cap_keeps_the_qwen_buckets_whole():
