@@ -1,8 +1,10 @@
-"""Iteration counts above the default on the 16-bit path: the fp16 scale of
-Q = P_N...P_1 shrinks with N (Q reaches a^N in padding and rank-deficient
-directions), so ragged shapes on every kernel path (fused recursion,
-small tiles, 256-wide tiles, direct form) stay finite and within the bf16
-bar of the float64 oracle up to N = 16."""
+"""Iteration counts above the default on the 16-bit path, and rank-deficient
+inputs.  The fp16 scale of Q = P_N...P_1 shrinks with N (Q reaches a^N in
+padding and rank-deficient directions), so ragged shapes on every kernel
+path (fused recursion, small tiles, 256-wide tiles, direct form) stay
+finite and within the bf16 bar of the float64 oracle up to N = 16.  On
+rank-deficient inputs every reduced-precision run is far from the oracle;
+there the paths must beat the iteration run with bf16 operands."""
 import numpy as np
 import pytest
 
@@ -48,3 +50,37 @@ def test_many_iterations_on_ragged_shapes(steps):
         Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=OR.Hyper(ns_steps=steps), form="direct")
         assert np.isfinite(Og[i]).all(), (steps, s)
         assert rel(Og[i], Oo) <= TOL[steps], (steps, s, rel(Og[i], Oo))
+
+
+def _bf16_iteration(U, steps=5, a=3.4445, b=-4.7750, c=2.0315):
+    """The direct-form iteration with every operand rounded to bf16 (torch
+    CPU): the precision the method is commonly run in, as a yardstick."""
+    import torch
+    X = torch.from_numpy(np.ascontiguousarray(U, dtype=np.float32))
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T.contiguous()
+    X = (X / X.norm()).bfloat16()
+    for _ in range(steps):
+        A = X @ X.T
+        X = a * X + (b * A + c * (A @ A)) @ X
+    return (X.T if tall else X).float().numpy()
+
+
+@pytest.mark.parametrize("form", ["auto", "direct"])
+def test_rank_deficient_inputs_no_worse_than_a_bf16_iteration(form):
+    # Rounding noise in zero singular directions grows by up to a^N on any
+    # reduced-precision path, so a rank-deficient U is far from the float64
+    # oracle everywhere; the paths here must stay below the bf16 iteration.
+    shapes, ranks = [(100, 900), (1000, 3000), (900, 100)], [4, 16, 8]
+    rng = np.random.default_rng(5)
+    W = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    G = [((rng.standard_normal((s[0], k)) @ rng.standard_normal((k, s[1]))) * 1e-3 / np.sqrt(k))
+         .astype(np.float32) for s, k in zip(shapes, ranks)]
+    M = [np.zeros(s, np.float32) for s in shapes]
+    (Wg, Mg, Og), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", formulation=form)
+    for i, s in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, form="direct")
+        U = 0.95 * G[i] + G[i]  # Nesterov blend from zero momentum
+        e_gpu, e_bf16 = rel(Og[i], Oo), rel(_bf16_iteration(U), Oo)
+        assert np.isfinite(Og[i]).all() and e_gpu < e_bf16, (form, s, e_gpu, e_bf16)
