@@ -84,3 +84,22 @@ def test_rank_deficient_inputs_no_worse_than_a_bf16_iteration(form):
         U = 0.95 * G[i] + G[i]  # Nesterov blend from zero momentum
         e_gpu, e_bf16 = rel(Og[i], Oo), rel(_bf16_iteration(U), Oo)
         assert np.isfinite(Og[i]).all() and e_gpu < e_bf16, (form, s, e_gpu, e_bf16)
+
+
+@pytest.mark.parametrize("coef", [(2.0, -1.5, 0.5), (3.0, -3.2, 1.2)])
+def test_other_coefficients(coef):
+    # The operand scales follow (a, b, c): a quintic that converges to 1
+    # (2, -1.5, 0.5) and one with a steeper start, at N = 5 and 10, on
+    # every kernel path
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    a, b, c = coef
+    for steps in (5, 10):
+        hp = default_hparams()
+        hp.ns_steps, hp.a, hp.b, hp.c = steps, a, b, c
+        W, M, G = seeded(SHAPES, 90 + steps, mscale=1e-3)
+        (Wg, Mg, Og), plan = run(SHAPES, W, M, G, LR, WD, "f32", "bf16", hp=hp, hints=HINTS)
+        ohp = OR.Hyper(ns_steps=steps, a=a, b=b, c=c)
+        for i, s in enumerate(SHAPES):
+            Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=ohp, form="direct")
+            assert np.isfinite(Og[i]).all(), (coef, steps, s)
+            assert rel(Og[i], Oo) <= 2e-2, (coef, steps, s, rel(Og[i], Oo), plan.buckets()[0]["scales"])
