@@ -36,8 +36,11 @@
  *     they wait for `stream` on entry and `stream` waits for all of them on
  *     return, so the call behaves as one operation on `stream`.  Each
  *     internal stream's launches are enqueued from its own short-lived host
- *     thread, joined before the call returns (one thread per call when the
- *     launch profiler is on).
+ *     thread (with the caller's current device made current), joined before
+ *     the call returns (one thread per call when the launch profiler is
+ *     on).  The internal streams belong to the device that is current at
+ *     that first call: later calls on the plan must keep the same device
+ *     current, as the workspace and the matrices live there.
  *   - Errors: all validation happens on the host before anything is
  *     enqueued.  On any status other than MUON_OK and MUON_ERR_HIP nothing
  *     was enqueued and no memory was touched.  MUON_ERR_HIP means a HIP

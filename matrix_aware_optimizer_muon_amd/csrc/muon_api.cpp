@@ -1015,17 +1015,23 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
     }
     return MUON_OK;
   };
-  if (S > 1 && !p->profiling) {
+  int dev = -1;
+  if (S > 1 && !p->profiling && hipGetDevice(&dev) == hipSuccess) {
     // Each slot's launch sequence is enqueued from its own host thread, so
     // that every slot's first kernels reach the GPU at once instead of after
     // the whole sequence of the slots before it (~13 us of host time per
     // launch; one Qwen2.5-7B layer: 8.3 -> 7.9 ms per step).  The threads
     // only read the plan and launch on distinct streams; all are joined here.
+    // A new host thread starts on device 0, so each first makes the
+    // caller's device current.
     std::vector<muon_status> sts((size_t)S, MUON_OK);
     std::vector<std::thread> th;
     int next = 1;
     try {
-      for (; next < S; ++next) th.emplace_back([&, slot = next] { sts[(size_t)slot] = run_buckets(slot); });
+      for (; next < S; ++next)
+        th.emplace_back([&, slot = next] {
+          sts[(size_t)slot] = hipSetDevice(dev) == hipSuccess ? run_buckets(slot) : MUON_ERR_HIP;
+        });
     } catch (...) {
       // no thread for slots next..S-1: they run on this thread below
     }
