@@ -137,6 +137,45 @@ def mfma_table(path, workload, command, xcds):
               f"{g / xcds / sec / 1e9:.2f} |")
 
 
+def lds_table(path, workload, command):
+    """Per kernel class: LdsUtil and LDSBankConflict (rocprofv3's derived
+    metrics: cycles the LDS serves indexed accesses, and cycles it stalls on
+    bank conflicts, over GPU-busy cycles x compute units; duration-weighted)
+    and the LDS bytes read and written by ds instructions per second
+    (SQ_INSTS_LDS_{LOAD,STORE}_BANDWIDTH x 64).  Direct-to-LDS global loads
+    are not ds instructions and count in neither."""
+    per = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        d = per[int(r["Dispatch_Id"])]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_name"] = r["Kernel_Name"]
+        d["_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    agg = collections.OrderedDict()
+    for d in per.values():
+        cls = kernel_class(d["_name"])
+        if cls is None or d["_s"] <= 0:
+            continue
+        a = agg.setdefault(cls, [0, 0.0, 0.0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += d["_s"]
+        a[2] += d.get("LdsUtil", 0.0) * d["_s"]
+        a[3] += d.get("LDSBankConflict", 0.0) * d["_s"]
+        a[4] += d.get("SQ_INSTS_LDS_LOAD_BANDWIDTH", 0.0) * 64
+        a[5] += d.get("SQ_INSTS_LDS_STORE_BANDWIDTH", 0.0) * 64
+    print(f"# LDS use per launch class: {workload}\n")
+    print("Counter run (GPU box, repo root), one refresh step:\n")
+    print(f"```\n{command}\n```\n")
+    print(f"kernel source hash: `{source_hash()}`\n")
+    print("LdsUtil and LDSBankConflict are percentages of GPU-busy cycles x compute units; "
+          "the byte rates count ds_read / ds_write traffic only (the 256-tile kernels fill "
+          "their operand ring with direct-to-LDS global loads, which add 32 KB per stage).\n")
+    print("| class | launches | avg ms | LdsUtil % | LDSBankConflict % | ds read TB/s | ds write TB/s |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for cls, (n, sec, u, bc, rd, wr) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"| {cls} | {n} | {sec * 1e3 / n:.3f} | {u / sec:.1f} | {bc / sec:.2f} | "
+              f"{rd / sec / 1e12:.2f} | {wr / sec / 1e12:.2f} |")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -150,6 +189,10 @@ def main(argv=None):
     mf.add_argument("--workload", required=True)
     mf.add_argument("--command", required=True)
     mf.add_argument("--xcds", type=int, default=8)
+    ld = sub.add_parser("lds")
+    ld.add_argument("--csv", required=True)
+    ld.add_argument("--workload", required=True)
+    ld.add_argument("--command", required=True)
     k = sub.add_parser("trace")
     k.add_argument("--stats", required=True)
     k.add_argument("--title", required=True)
@@ -160,6 +203,9 @@ def main(argv=None):
         return
     if a.cmd == "mfma":
         mfma_table(a.csv, a.workload, a.command, a.xcds)
+        return
+    if a.cmd == "lds":
+        lds_table(a.csv, a.workload, a.command)
         return
     if a.cmd == "trace":
         rows = list(csv.DictReader(open(a.stats)))
