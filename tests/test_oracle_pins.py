@@ -54,6 +54,26 @@ def test_ns5_matches_svd_closed_form(shape):
     assert rel(out, expect) < 1e-12
 
 
+@pytest.mark.parametrize("steps,coef", [(1, (3.4445, -4.7750, 2.0315)), (8, (3.4445, -4.7750, 2.0315)),
+                                        (5, (2.0, -1.5, 0.5)), (10, (3.0, -3.2, 1.2))])
+def test_other_iteration_counts_and_coefficients_follow_the_svd_closed_form(steps, coef):
+    # Any count N and any odd quintic f(s) = a s + b s^3 + c s^5: both the
+    # direct and the Gram routines act on each singular value by f, N times.
+    a, b, c = coef
+    hp = O.Hyper(ns_steps=steps, a=a, b=b, c=c)
+    rng = np.random.default_rng(300 + steps)
+    M = rng.standard_normal((6, 17))
+    U, sv, Vt = np.linalg.svd(M, full_matrices=False)
+    fs = []
+    for v in sv / np.linalg.norm(M):
+        for _ in range(steps):
+            v = a * v + b * v ** 3 + c * v ** 5
+        fs.append(v)
+    expect = U @ np.diag(fs) @ Vt
+    assert rel(O.ns5_direct(M, hp), expect) < 1e-12
+    assert rel(O.ns5_gram(M, hp), expect) < 1e-10
+
+
 def test_ns5_rank_one_gives_f5_of_one():
     rng = np.random.default_rng(1)
     u, v = rng.standard_normal(9), rng.standard_normal(23)
