@@ -69,7 +69,8 @@ typedef struct muon_plan_s* muon_plan_t;
 typedef enum {
   MUON_OK = 0,
   MUON_ERR_INVALID_ARGUMENT = 1,   /* null pointer, bad count/shape/value */
-  MUON_ERR_UNSUPPORTED = 2,        /* valid but not implemented (dtype, steps) */
+  MUON_ERR_UNSUPPORTED = 2,        /* valid but not implemented (dtype, steps,
+                                      coefficients the 16-bit path cannot scale) */
   MUON_ERR_WORKSPACE_TOO_SMALL = 3,
   MUON_ERR_HIP = 4                 /* a HIP runtime call failed */
 } muon_status;
