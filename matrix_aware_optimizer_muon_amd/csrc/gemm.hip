@@ -197,7 +197,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
       for (int e = 0; e < RR / RPI; ++e) {
         const int il = e * RPI + tid / TPR, jl = (tid % TPR) * 4;
         const float* sr = stile + il * EPI_LD + jl;
-        epilogue_final4(p, mat, gr0 + il, row0B + jl, make_float4(sr[0], sr[1], sr[2], sr[3]));
+        epilogue_final4(p, mat, gr0 + il, row0B + jl, make_float4(sr[0], sr[1], sr[2], sr[3]),
+                        p.inv_norm[mat]);
       }
     } else {
       // row pass (lower triangle incl. the diagonal): four consecutive

@@ -273,7 +273,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   // lane reads the 16-byte chunks holding its FN x 4 groups of 4 consecutive
   // m (half h of each chunk) and adds gamma * X to the accumulators, so the
   // epilogue reads no r x r input.
-  constexpr bool HARVEST = EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH || EPI == EPI_XUPD;
+  constexpr bool HARVEST =
+      EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH || EPI == EPI_XUPD || EPI == EPI_XFINAL;
   float gam = 0.0f;
   if constexpr (HARVEST) gam = rr_gamma<EPI>(p);
   const int hk0 = row0A / DBK + wm * 4;
@@ -387,8 +388,9 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
   __syncthreads();
 
-  if constexpr (EPI == EPI_FINAL) {
-    // Final product: the fp32 tile goes through LDS in two rounds of 128
+  if constexpr (EPI == EPI_FINAL || EPI == EPI_XFINAL) {
+    // Final product (and the direct form's last X', whose identity term the
+    // loop has harvested): the fp32 tile goes through LDS in two rounds of 128
     // rows, its 16-byte column chunks XOR-swizzled by (row / 4) (epi_off) so
     // that the staging writes and the row reads are conflict free.  All of a
     // round's W rows are requested before the staging, so their latency
@@ -402,7 +404,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     constexpr int RPI = NT / 64;   // tile rows per row-pass iteration
     constexpr int PER = RR / RPI;  // row-pass iterations per round
     const MatPtrs mp = p.table[mat];
-    const float inv = p.inv_norm[mat];
+    const float inv = EPI == EPI_FINAL ? p.inv_norm[mat] : rr_beta<EPI_XFINAL>(p, mat, 0);
     const bool wvec = p.vec && gj + 4 <= p.out_cols;
 #pragma unroll
     for (int round = 0; round < 2; ++round) {
@@ -440,7 +442,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
             if (mp.O) nt_store4(mp.O + idx, o);
           }
         } else {
-          epilogue_final4(p, mat, gi, gj, av);
+          epilogue_final4(p, mat, gi, gj, av, inv);
         }
       }
       __syncthreads();
@@ -581,6 +583,7 @@ hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s
     case EPI_SYRK:
       return p.xkind ? launch_dma_one<1, EPI_SYRK>(p, nmat, s) : launch_dma_one<0, EPI_SYRK>(p, nmat, s);
     case EPI_XUPD: return launch_dma_one<1, EPI_XUPD>(p, nmat, s);
+    case EPI_XFINAL: return launch_dma_one<1, EPI_XFINAL>(p, nmat, s);
     case EPI_POLY: return launch_dma_one<1, EPI_POLY>(p, nmat, s);
     case EPI_PQPG: return launch_dma_one<1, EPI_PQPG>(p, nmat, s);
     case EPI_PH: return launch_dma_one<1, EPI_PH>(p, nmat, s);

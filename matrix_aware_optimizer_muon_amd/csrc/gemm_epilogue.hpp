@@ -117,14 +117,15 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int mat, int prod
 //         Q' = a Q + P~ Q,   acc = sP sQ P~ Q     beta = 1/(sP sQ),    gamma = a sP
 //   PH    G' = a H + P~ H,   acc = sP sH P~ H     beta = 1/(sP sH),    gamma = a sP
 //   XUPD  X' = a X + P~ X,   acc = sP sX P~ X     beta = 1/(sP sX),    gamma = a sP
-//         (direct form; SYRK there runs on fp16 X: beta = 1/sX^2)
+//         (direct form; SYRK there runs on fp16 X: beta = 1/sX^2; XFINAL is
+//         the last XUPD applied to W by the final product's epilogue)
 template <int EPI>
 __device__ __forceinline__ float rr_beta(const GemmParams& p, int mat, int prod) {
   if constexpr (EPI == EPI_SYRK) {
     if (p.syrk_scale > 0.0f) return p.syrk_scale;
     const float inv = p.inv_norm[mat];
     return inv * inv;
-  } else if constexpr (EPI == EPI_XUPD) {
+  } else if constexpr (EPI == EPI_XUPD || EPI == EPI_XFINAL) {
     return 1.0f / (p.sP * p.sX);
   } else if constexpr (EPI == EPI_POLY) {
     return p.c * (1.0f / (p.sG * p.sG));
@@ -140,12 +141,12 @@ __device__ __forceinline__ float rr_gamma(const GemmParams& p) {
   else return p.a * p.sP;
 }
 
-// Final product: O = acc / ||U||, W <- decay W - step O at (gi, gj..gj+3).
+// Final product: O = inv * acc (inv = 1/||U||, or the direct form's 1/(sP sX)),
+// W <- decay W - step O at (gi, gj..gj+3).
 __device__ __forceinline__ void epilogue_final4(const GemmParams& p, int mat, int gi, int gj,
-                                                float4 acc) {
+                                                float4 acc, float inv) {
   if (gi >= p.out_rows || gj >= p.out_cols) return;
   const MatPtrs mp = p.table[mat];
-  const float inv = p.inv_norm[mat];
   const float4 o = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   const size_t idx = (size_t)gi * p.out_cols + gj;
   if (p.vec && gj + 4 <= p.out_cols) {

@@ -14,7 +14,10 @@ struct MatPtrs {
   float* O;  // nullable direction output
 };
 
-enum Epi : int { EPI_SYRK = 0, EPI_POLY = 1, EPI_PQPG = 2, EPI_PH = 3, EPI_FINAL = 4, EPI_XUPD = 5 };
+// EPI_XFINAL: the direct form's last X' = a X + P~ X, applied to W as the
+// final product does (X' is O; non-transposed buckets).
+enum Epi : int { EPI_SYRK = 0, EPI_POLY = 1, EPI_PQPG = 2, EPI_PH = 3, EPI_FINAL = 4, EPI_XUPD = 5,
+                 EPI_XFINAL = 6 };
 enum OpType : int { OP_BF16 = 0, OP_F32 = 1 };
 
 // Parameters of one batched GEMM launch C = A * B^T over a chunk of

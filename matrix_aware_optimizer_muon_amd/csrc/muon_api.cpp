@@ -744,6 +744,9 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         // stride; r_pad is a multiple of 64, so both are exactly r_pad^2
         if (rr_stride != h_stride || rr_stride != rr) return MUON_ERR_HIP;
         const int vec = chunk_vec(p, B, ch);
+        // W <- decay W - step_c O
+        const float decay = (float)(1.0 - (double)lr * wd);
+        const float step_c = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
         auto gemm = [&](const GemmParams& gp, int epi) {
           return B.dma ? launch_gemm_dma(gp, epi, nm, stream)
                        : launch_gemm(gp, epi, op, B.bt, nm, stream);
@@ -875,10 +878,25 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
             xg.ldyt = (int)B.r_pad;
             xg.y_stride = x_stride;
             xg.xcd_chunk = full_grid_xcd_chunk(xg.tiles_per_prod);
+            if (k == N - 1 && !B.transposed) {
+              // X_N's tiles are W's tiles: update W from the accumulators
+              // (W <- decay W - step X_N, X_N also to O_out) instead of
+              // storing X_N and running the update pass
+              xg.out_rows = (int)B.m;
+              xg.out_cols = (int)B.n;
+              xg.decay = decay;
+              xg.step = step_c;
+              xg.vec = vec;
+              st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + 10.0 * rcf) * nm,
+                         [&] { return gemm(xg, EPI_XFINAL); });
+              if (st != MUON_OK) return st;
+              break;
+            }
             st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + 6.0 * rcf) * nm,
                        [&] { return gemm(xg, EPI_XUPD); });
             if (st != MUON_OK) return st;
           }
+          if (!B.transposed) continue;  // the last product updated W
           // W <- (1 - lr wd) W - lr s O^-1(X_N): the natural-layout buffer of
           // the last pair holds O^-1(X_N) in W's layout
           WupdParams wp{};
@@ -889,8 +907,8 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
           wp.n = (int)B.n;
           wp.n_pad = (int)B.n_pad;
           wp.inv_sx = 1.0f / p->scales.sX;
-          wp.decay = (float)(1.0 - (double)lr * wd);
-          wp.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
+          wp.decay = decay;
+          wp.step = step_c;
           st = timed(p, stream, MUON_K_WUPD, 0.0, 10.0 * (double)B.m * B.n * nm,
                      [&] { return launch_wupd(wp, nm, vec, stream); });
           if (st != MUON_OK) return st;
@@ -983,8 +1001,8 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         fg.vec = vec;
         fg.out_rows = (int)B.m;
         fg.out_cols = (int)B.n;
-        fg.decay = (float)(1.0 - (double)lr * wd);
-        fg.step = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
+        fg.decay = decay;
+        fg.step = step_c;
         if (!B.transposed) {  // O (r x c) = Q (r x r) * (X0^T)^T
           fg.A = Qfinal;
           fg.a_stride = h_stride;

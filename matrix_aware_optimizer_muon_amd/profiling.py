@@ -23,7 +23,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/rr_fused.hip", "csrc/gemm_epilogue.hpp",
                   "csrc/elementwise.hip", "csrc/common.hpp", "csrc/kernels.h",
                   "csrc/muon_api.cpp")
-EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final", 5: "xupd"}
+EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final", 5: "xupd", 6: "xupd"}
 
 
 def source_hash() -> str:

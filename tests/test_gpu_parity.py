@@ -271,14 +271,15 @@ def test_gram_form_on_squares(shape):
     check_ns([shape], W, M, G, "bf16", label=f"gram {shape}", formulation="gram")
 
 
-def test_final_update_without_direction_output_matches():
-    # Without O_out the final product's epilogue takes its W rows 0..127 of
-    # every tile from the ring (fetched during the last K steps); with O_out it
-    # reads W from HBM.  Both must give the same W' (fp32 rounding apart).
+@pytest.mark.parametrize("form", ["gram", "direct"])
+def test_final_update_without_direction_output_matches(form):
+    # The epilogues that update W (the final product; in the direct form the
+    # last X' product, or the update pass for tall matrices) write O_out only
+    # when it is given; W' must not depend on it.
     shapes = [(1024, 3072), (3072, 1024), (1000, 2000), (2000, 1000), (1536, 1536)]
     W, M, G = seeded(shapes, 77, mscale=1e-3)
-    (W_o, M_o, _), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=True, formulation="gram")
-    (W_n, M_n, _), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=False, formulation="gram")
+    (W_o, M_o, _), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=True, formulation=form)
+    (W_n, M_n, _), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=False, formulation=form)
     for i in range(len(shapes)):
         assert rel(W_n[i], W_o[i]) <= 1e-6, (shapes[i], rel(W_n[i], W_o[i]))
         assert np.array_equal(M_n[i], M_o[i])
