@@ -103,3 +103,20 @@ def test_other_coefficients(coef):
             Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=ohp, form="direct")
             assert np.isfinite(Og[i]).all(), (coef, steps, s)
             assert rel(Og[i], Oo) <= 2e-2, (coef, steps, s, rel(Og[i], Oo), plan.buckets()[0]["scales"])
+
+
+@pytest.mark.parametrize("steps", [8, 16])
+def test_many_iterations_fp32_path(steps):
+    # The fp32 path keeps unscaled fp32 operands: Q's a^N in the padding
+    # (a^16 = 3.9e8) stays in range, and the 1e-4 bar holds
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    hp = default_hparams()
+    hp.ns_steps = steps
+    shapes = [(100, 900), (300, 700), (700, 300), (256, 1024)]
+    W, M, G = seeded(shapes, 110 + steps, mscale=1e-3)
+    (Wg, Mg, Og), plan = run(shapes, W, M, G, LR, WD, "f32", "f32", hp=hp)
+    assert all(b["scales"] == (1.0,) * 5 for b in plan.buckets())
+    for i, s in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=OR.Hyper(ns_steps=steps), form="direct")
+        assert rel(Og[i], Oo) <= 1e-4, (steps, s, rel(Og[i], Oo))
+        assert rel(Wg[i], Wo) <= 1e-5, (steps, s, rel(Wg[i], Wo))
