@@ -7,7 +7,8 @@
 //             ("Scaling Muon for DiT" 3.1), the other X0^T.  One read of M
 //             and G, one write of M and of the two copies.
 // finalize:   deterministic (fixed order, fp64) reduction of the partial sums
-//             to 1/||U||_F per matrix (0 when the norm is 0).
+//             to 1/||U||_F per matrix (0 when the norm is 0, NaN when the sum
+//             is NaN or infinite).
 // rownorm:    the same M update and U, then R_eps over the r oriented rows
 //             ("Scaling Muon for DiT" 3.1) and the decayed, scaled update of W
 //             ("Infra Optimizers" eq. (4)).  m <= n: one workgroup per row,
@@ -197,7 +198,11 @@ __global__ void __launch_bounds__(256) norm_finalize_kernel(const PrepParams p) 
   __syncthreads();
   if (threadIdx.x == 0) {
     const double tot = red[0] + red[1] + red[2] + red[3];
-    p.inv_norm[mat] = tot > 0.0 ? (float)(1.0 / sqrt(tot)) : 0.0f;
+    // ||U|| = 0: no direction (pure decay).  A NaN or an infinite sum (a
+    // NaN or Inf in U, or squares past fp32's range) gives NaN, so the
+    // matrix's direction and weights become NaN as the plain formula's
+    // X / ||X|| does, instead of a silently wrong finite step.
+    p.inv_norm[mat] = tot == 0.0 ? 0.0f : (tot < INFINITY ? (float)(1.0 / sqrt(tot)) : NAN);
   }
 }
 
@@ -229,6 +234,10 @@ hipError_t launch_norm_finalize(const PrepParams& p, int nmat, hipStream_t s) {
 // row (M, G and W) is issued before the row reduction, so its latency is not
 // paid twice; U stays in registers (CH float4 chunks per thread).  Rows wider
 // than NT*CH*4 take the generic path that re-reads M' and G (CH == 0).
+// max(||row||, eps) of R_eps that keeps a NaN norm (fmaxf would return eps
+// and scale the rest of a NaN row by 1/eps).
+__device__ __forceinline__ float max_eps(float nrm, float eps) { return nrm < eps ? eps : nrm; }
+
 template <int BS>
 __device__ __forceinline__ float block_sum_n(float v, float* red) {
   v = wave_sum(v);
@@ -276,7 +285,7 @@ __global__ void __launch_bounds__(NT) rownorm_rows_kernel(const RowNormParams p,
         ss += mm[k].x * mm[k].x + mm[k].y * mm[k].y + mm[k].z * mm[k].z + mm[k].w * mm[k].w;
       }
     }
-    const float inv = 1.0f / fmaxf(sqrtf(block_sum_n<NT>(ss, red)), p.eps);
+    const float inv = 1.0f / max_eps(sqrtf(block_sum_n<NT>(ss, red)), p.eps);
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int c = threadIdx.x + NT * k;
@@ -305,7 +314,7 @@ __global__ void __launch_bounds__(NT) rownorm_rows_kernel(const RowNormParams p,
       store_f4(mp.M + base + col, mn, v4, valid);
       ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
     }
-    const float inv = 1.0f / fmaxf(sqrtf(block_sum_n<NT>(ss, red)), p.eps);
+    const float inv = 1.0f / max_eps(sqrtf(block_sum_n<NT>(ss, red)), p.eps);
     // each thread re-reads exactly the chunks it wrote above
     for (int c = threadIdx.x; c < nc; c += NT) {
       const int col = c * 4, valid = p.n - col;
@@ -391,7 +400,7 @@ __global__ void __launch_bounds__(256) rownorm_colfinal_kernel(const RowNormPara
   double s = 0.0;
   for (int rb = 0; rb < p.row_blocks; ++rb) s += (double)part[(size_t)rb * p.n];
   const float nrm = (float)sqrt(s);
-  p.colscale[(size_t)mat * p.n + col] = 1.0f / fmaxf(nrm, p.eps);
+  p.colscale[(size_t)mat * p.n + col] = 1.0f / max_eps(nrm, p.eps);
 }
 
 template <bool GBF16>

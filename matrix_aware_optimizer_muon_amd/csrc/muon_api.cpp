@@ -49,6 +49,13 @@ constexpr int kMaxSlots = 4;                   // internal streams for concurren
 constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
 constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
 constexpr int kRing = 4;                      // pinned descriptor staging slots
+// Newton-Schulz iteration counts the paths accept.  Rounding accumulates
+// with N on the 16-bit path: measured NS error 0.35-0.5e-2 at N = 6,
+// 0.5-0.9e-2 at N = 12 and 0.6-2.8e-2 at N = 16 (Q's fp16 scale falls to
+// 2^-13 there), so that path stops at 12, where the 2e-2 bound still holds
+// with margin.  The fp32 path measured 1e-5 up to N = 16.
+constexpr int kMaxSteps16 = 12;
+constexpr int kMaxStepsF32 = 16;
 
 // Operand scales (powers of two, exact) of the 16-bit Newton-Schulz path.
 // Every matrix of the recursion is a polynomial in X0 X0^T, and X0 = U /
@@ -198,7 +205,7 @@ muon_status validate_hp(const muon_hparams& hp) {
   if (!finite(hp.momentum) || hp.momentum < 0.0f || hp.momentum > 1.0f) return MUON_ERR_INVALID_ARGUMENT;
   if (hp.nesterov != 0 && hp.nesterov != 1) return MUON_ERR_INVALID_ARGUMENT;
   if (hp.ns_steps < 1) return MUON_ERR_INVALID_ARGUMENT;
-  if (hp.ns_steps > 16) return MUON_ERR_UNSUPPORTED;
+  if (hp.ns_steps > kMaxStepsF32) return MUON_ERR_UNSUPPORTED;
   if (!finite(hp.a) || !finite(hp.b) || !finite(hp.c)) return MUON_ERR_INVALID_ARGUMENT;
   if (!finite(hp.scale_coeff) || hp.scale_coeff < 0.0f) return MUON_ERR_INVALID_ARGUMENT;
   if (!finite(hp.rownorm_eps) || !(hp.rownorm_eps > 0.0f)) return MUON_ERR_INVALID_ARGUMENT;
@@ -455,6 +462,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
   if (st != MUON_OK) return st;
   NsScales scales;
   if (desc->ns_dtype == MUON_BF16) {
+    if (desc->hp.ns_steps > kMaxSteps16) return MUON_ERR_UNSUPPORTED;
     st = ns_scales(desc->hp, &scales);
     if (st != MUON_OK) return st;
   }
@@ -500,14 +508,26 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       B.transposed = B.m > B.n;
       B.r = std::min(B.m, B.n);
       B.c = std::max(B.m, B.n);
-      // AUTO: the direct form for square matrices on the 16-bit path (the
-      // same 20 r^3 flops as the Gram form, in fewer and larger products:
-      // measured 2-10 % faster, 3.6x on 64 x 512^2), the Gram form otherwise
-      // (3 r^2 c + 17 r^3 against 15 r^2 c + 5 r^3 flops for c > r)
+      // AUTO: the direct form for near-square matrices (c <= 1.125 r) on the
+      // 16-bit path, the Gram form otherwise (3 r^2 c + 17 r^3 against
+      // 15 r^2 c + 5 r^3 flops for c > r).  Near-square inputs have singular
+      // values close to zero, which the Gram form's squared spectrum resolves
+      // badly in fp16: measured over r = 40..1000 (worst of two seeds, both
+      // orientations) the Gram form's NS error is 1.1e-2..3.2e-2 on squares
+      // and 0.8e-2 at worst from c > 1.125 r on, the direct form's 0.25e-2..
+      // 0.64e-2 everywhere; on squares the two cost the same 20 r^3 flops
+      // and the direct form measured 2-10 % faster (3.6x on 64 x 512^2).
+      const bool near_square = 8 * B.c <= 9 * B.r;
       B.direct = p->formulation == MUON_FORM_DIRECT ||
-                 (p->formulation == MUON_FORM_AUTO && !f32path && B.m == B.n);
+                 (p->formulation == MUON_FORM_AUTO && !f32path && near_square);
       const muon_bucket_hint* hint = find_hint(desc, B.m, B.n);
       if (hint && hint->formulation != MUON_FORM_AUTO) B.direct = hint->formulation == MUON_FORM_DIRECT;
+      if (!f32path && !B.direct && near_square) {
+        // a Gram form forced onto a near-square bucket on the 16-bit path
+        // would miss the accuracy the path promises (see above)
+        delete p;
+        return MUON_ERR_UNSUPPORTED;
+      }
       B.bt = B.direct ? 256 : choose_tile(B.r, (int64_t)members[b].size(), f32path);
       if (hint && hint->tile != 0) {
         if (B.direct && hint->tile != 256) {

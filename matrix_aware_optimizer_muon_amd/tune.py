@@ -6,21 +6,30 @@ initialisation to obtain the per-shape costs that owner assignment balances.
 This module does both for this library's kernels:
 
 * ``candidates`` lists the settings the kernels provide for one shape
-  (``muon_bucket_hint``: tile 64 / 128 / 256, Gram or direct form);
+  (``muon_bucket_hint``: tile 64 / 128 / 256, Gram or direct form), keeping
+  only those the planner accepts for it (it refuses, for instance, the Gram
+  form on near-square buckets of the 16-bit path);
 * ``time_bucket`` times one setting with a single-bucket plan of that shape
   and count on seeded synthetic device inputs (weights N(0, 0.02^2),
   gradients N(0, 1e-3^2) in the planned gradient dtype), median over a few
   steps after two warm-up steps (the first timed shape of a process runs
-  ~15 % slow after a single one);
+  ~15 % slow after a single one), and returns the direction output of the
+  bucket's first matrix from the first call;
+* every candidate's direction is compared with the fp32 path's direction
+  for the same input (a single-matrix plan on ``ns_dtype="f32"``, accurate
+  to ~1e-5): a setting whose relative error exceeds ``ACCURACY_TOL`` is
+  recorded but never chosen, so a fast but inaccurate setting cannot reach
+  the cache's winners;
 * ``tune`` times every candidate of every (shape, count) not yet in the
-  cache, keeps the fastest, and stores all timings (the per-shape cost
-  profile) in a JSON cache keyed by device, dtypes, shape and count;
+  cache, keeps the fastest accurate one, and stores all timings (the
+  per-shape cost profile) in a JSON cache keyed by device, dtypes, shape and
+  count;
 * ``hints_for`` turns cached winners into ``Plan(hints=...)``.
 
-The cache file is plain JSON: ``{"version": 1, "entries": {key: entry}}``
+The cache file is plain JSON: ``{"version": 2, "entries": {key: entry}}``
 with ``entry = {"tile", "formulation", "ms", "default", "candidates":
-[{"tile", "formulation", "ms"}...]}``.  Timing needs a GPU; the cache logic
-does not.
+[{"tile", "formulation", "ms", "err"}...]}``.  Timing needs a GPU; the cache
+logic does not.
 """
 from __future__ import annotations
 
@@ -29,7 +38,11 @@ import os
 from collections import OrderedDict
 from typing import Callable, Iterable, Optional, Sequence
 
-CACHE_VERSION = 1
+CACHE_VERSION = 2
+# Largest relative Frobenius error of a candidate's direction against the
+# fp32 path's that the tuner accepts: half the 16-bit path's 2e-2 bound (the
+# sample is one matrix and one seed), and the fp32 path's own 1e-4 bound.
+ACCURACY_TOL = {"bf16": 1e-2, "f32": 1e-4}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # Winners measured on the device this package targets, shipped with it.
 SHIPPED_CACHE = os.path.join(_HERE, "tuned", "mi355x.json")
@@ -85,17 +98,30 @@ def save_cache(path: str, data: dict) -> None:
 def candidates(m: int, n: int, ns_dtype: str) -> list:
     """The settings the kernels provide for an m x n bucket.  fp32 path:
     Gram form with 64- or 128-wide tiles.  16-bit path: Gram form with 64-
-    (r <= 1024), 128- or 256-wide tiles, and the direct form (256-wide)."""
+    (r <= 1024), 128- or 256-wide tiles, and the direct form (256-wide);
+    settings the planner refuses for this shape are left out."""
     r = min(m, n)
     if ns_dtype == "f32":
-        return [{"tile": 64, "formulation": "gram"}, {"tile": 128, "formulation": "gram"}]
-    out = []
-    if r <= 1024:
-        out.append({"tile": 64, "formulation": "gram"})
-    out.append({"tile": 128, "formulation": "gram"})
-    out.append({"tile": 256, "formulation": "gram"})
-    out.append({"tile": 256, "formulation": "direct"})
-    return out
+        raw = [{"tile": 64, "formulation": "gram"}, {"tile": 128, "formulation": "gram"}]
+    else:
+        raw = []
+        if r <= 1024:
+            raw.append({"tile": 64, "formulation": "gram"})
+        raw.append({"tile": 128, "formulation": "gram"})
+        raw.append({"tile": 256, "formulation": "gram"})
+        raw.append({"tile": 256, "formulation": "direct"})
+    return [h for h in raw if _plannable(m, n, ns_dtype, h)]
+
+
+def _plannable(m: int, n: int, ns_dtype: str, hint: dict) -> bool:
+    from ._lib import MUON_ERR_UNSUPPORTED, MuonError, Plan
+    try:
+        Plan([(m, n)], "f32", ns_dtype, hints={(m, n): hint}).close()
+    except MuonError as e:
+        if e.status == MUON_ERR_UNSUPPORTED:
+            return False
+        raise
+    return True
 
 
 def device_name() -> str:
@@ -105,30 +131,46 @@ def device_name() -> str:
     return f"{p.name} {arch.split(':')[0]}".strip()
 
 
+def _inputs(m: int, n: int, count: int, grad_dtype: str, seed: int):
+    """Seeded device inputs, matrix i drawn from its own generator, so the
+    first matrix is the same for every count."""
+    import torch
+    dev = torch.device("cuda:0")
+    gdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
+    W, M, G = [], [], []
+    for i in range(count):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed * 1000003 + i)
+        W.append(torch.randn(m, n, device=dev, generator=gen) * 0.02)
+        M.append(torch.zeros(m, n, device=dev))
+        G.append((torch.randn(m, n, device=dev, generator=gen) * 1e-3).to(gdt))
+    return W, M, G
+
+
 def time_bucket(m: int, n: int, count: int, grad_dtype: str, ns_dtype: str, hint: Optional[dict],
-                steps: int = 3, warmup: int = 2, seed: int = 0) -> float:
+                steps: int = 3, warmup: int = 2, seed: int = 0):
     """Median ms of one muon_step_batched call over `count` m x n matrices
-    planned with `hint` (None: the planner's own rule)."""
+    planned with `hint` (None: the planner's own rule), and the direction
+    output (fp32 m x n device tensor) of the first matrix from the first
+    call."""
     import torch
     from ._lib import Plan
     dev = torch.device("cuda:0")
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(seed)
     plan = Plan([(m, n)] * count, grad_dtype, ns_dtype,
                 hints={(m, n): hint} if hint else None)
-    gdt = torch.bfloat16 if grad_dtype == "bf16" else torch.float32
-    W = [torch.randn(m, n, device=dev, generator=gen) * 0.02 for _ in range(count)]
-    M = [torch.zeros(m, n, device=dev) for _ in range(count)]
-    G = [(torch.randn(m, n, device=dev, generator=gen) * 1e-3).to(gdt) for _ in range(count)]
+    W, M, G = _inputs(m, n, count, grad_dtype, seed)
+    O0 = torch.empty(m, n, device=dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ptr = lambda L: [x.data_ptr() for x in L]
     Wp, Mp, Gp = ptr(W), ptr(M), ptr(G)
+    Op = [O0.data_ptr()] + [0] * (count - 1)
     times = []
     for i in range(warmup + steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        plan.step_ptrs(Wp, Mp, Gp, 0.02, 0.1, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        plan.step_ptrs(Wp, Mp, Gp, 0.02, 0.1, ws.data_ptr(), ws.numel(), stream.cuda_stream,
+                       Op if i == 0 else None)
         b.record(stream)
         b.synchronize()
         if i >= warmup:
@@ -136,33 +178,75 @@ def time_bucket(m: int, n: int, count: int, grad_dtype: str, ns_dtype: str, hint
     plan.close()
     del W, M, G, ws
     times.sort()
-    return float(times[len(times) // 2])
+    return float(times[len(times) // 2]), O0
+
+
+def reference_direction(m: int, n: int, grad_dtype: str, seed: int = 0):
+    """The fp32 path's direction for the first matrix of time_bucket's
+    inputs (a single-matrix plan)."""
+    import torch
+    from ._lib import Plan
+    plan = Plan([(m, n)], grad_dtype, "f32")
+    W, M, G = _inputs(m, n, 1, grad_dtype, seed)
+    O = torch.empty(m, n, device="cuda:0")
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda:0")
+    plan.step_ptrs([W[0].data_ptr()], [M[0].data_ptr()], [G[0].data_ptr()], 0.02, 0.1,
+                   ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream,
+                   [O.data_ptr()])
+    torch.cuda.synchronize()
+    plan.close()
+    return O
+
+
+def _rel(a, b) -> float:
+    nb = float(b.double().norm())
+    return float((a.double() - b.double()).norm()) / nb if nb > 0 else float(a.double().norm())
 
 
 def tune(shapes: Sequence[Sequence[int]], grad_dtype: str, ns_dtype: str,
          cache: Optional[dict] = None, device: Optional[str] = None, steps: int = 3,
          warmup: int = 2, timer: Optional[Callable] = None, log: Optional[Callable] = None) -> dict:
     """Time every candidate of each (shape, count) of `shapes` that `cache`
-    does not hold yet and add the results.  `timer(m, n, count, hint)`
-    replaces the device timing (tests).  Returns the (updated) cache."""
+    does not hold yet, check its direction against the fp32 path's, and add
+    the results.  `timer(m, n, count, hint)` replaces the device measurement
+    (tests); it returns ms, or (ms, err) with err the candidate's relative
+    error (None: not checked).  Returns the (updated) cache."""
     if cache is None:
         cache = {"version": CACHE_VERSION, "entries": {}}
     if device is None:
         device = device_name()
-    if timer is None:
-        timer = lambda m, n, c, h: time_bucket(m, n, c, grad_dtype, ns_dtype, h, steps, warmup)
+    tol = ACCURACY_TOL[ns_dtype]
     for (m, n), count in shape_counts(shapes).items():
         key = cache_key(device, grad_dtype, ns_dtype, m, n, count)
         if key in cache["entries"]:
             continue
-        default_ms = timer(m, n, count, None)
+        if timer is None:
+            ref = reference_direction(m, n, grad_dtype)
+
+            def measure(hint):
+                ms, O0 = time_bucket(m, n, count, grad_dtype, ns_dtype, hint, steps, warmup)
+                return ms, _rel(O0, ref)
+        else:
+            def measure(hint):
+                out = timer(m, n, count, hint)
+                return out if isinstance(out, tuple) else (out, None)
+        default_ms, _ = measure(None)
         rows = []
         for h in candidates(m, n, ns_dtype):
-            ms = timer(m, n, count, h)
-            rows.append({"tile": h["tile"], "formulation": h["formulation"], "ms": round(ms, 4)})
+            ms, err = measure(h)
+            row = {"tile": h["tile"], "formulation": h["formulation"], "ms": round(ms, 4),
+                   "err": None if err is None else float(f"{err:.3e}")}
+            if err is not None and not err <= tol:
+                row["rejected"] = True
+            rows.append(row)
             if log:
-                log(f"{m}x{n} x{count}: tile {h['tile']:3d} {h['formulation']:6s} {ms:9.3f} ms")
-        best = min(rows, key=lambda e: e["ms"])
+                e = "-" if err is None else f"{err:.2e}"
+                log(f"{m}x{n} x{count}: tile {h['tile']:3d} {h['formulation']:6s} {ms:9.3f} ms "
+                    f"err {e}{' (rejected)' if row.get('rejected') else ''}")
+        ok = [e for e in rows if not e.get("rejected")]
+        if not ok:
+            raise RuntimeError(f"no setting of {m}x{n} x{count} meets the accuracy bound {tol}")
+        best = min(ok, key=lambda e: e["ms"])
         cache["entries"][key] = {"tile": best["tile"], "formulation": best["formulation"],
                                  "ms": best["ms"], "default": round(default_ms, 4),
                                  "candidates": rows}

@@ -158,7 +158,10 @@ def rownorm(X, eps: float) -> np.ndarray:
     out = np.empty_like(X)
     for i in range(X.shape[0]):
         nrm = math.sqrt(float(np.dot(X[i], X[i])))
-        out[i] = X[i] / max(nrm, eps)
+        # max(nrm, eps); a NaN norm (a NaN in the row) is kept, so the row
+        # stays NaN rather than being scaled by 1/eps
+        den = eps if nrm < eps else nrm
+        out[i] = X[i] / den
     return out
 
 
@@ -198,15 +201,3 @@ def rownorm_step(W, M, G, lr: float, wd: float, hp: Hyper = Hyper()):
     R = unorient(rownorm(X, hp.rownorm_eps), tr)
     W_new = apply_update(W, R, lr, wd, update_scale(m, n, hp.scale_coeff))
     return W_new, M_new, R
-
-
-def f_quintic(x, hp: Hyper = Hyper()):
-    """Scalar quintic f(x) = a x + b x^3 + c x^5 ([Infra] Background)."""
-    return hp.a * x + hp.b * x ** 3 + hp.c * x ** 5
-
-
-def direct_flops(r: int, c: int, steps: int = 5) -> float:
-    """Flops of the direct form as the oracle performs it (full products):
-    per iteration A = X X^T (2 r^2 c), A X (2 r^2 c), A A (2 r^3) and
-    (A A) X (2 r^2 c)."""
-    return steps * (6.0 * r * r * c + 2.0 * r ** 3)

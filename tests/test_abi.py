@@ -62,6 +62,15 @@ def test_plan_rejects_bad_descriptions():
     assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_INVALID_ARGUMENT
     hp = L.default_hparams(); hp.ns_steps = 17
     assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_UNSUPPORTED
+    assert plan_status([(4, 4)], ns_dtype="f32", hp=hp) == L.MUON_ERR_UNSUPPORTED
+    # the 16-bit path stops at N = 12 (its accuracy bound), the fp32 path at 16
+    hp = L.default_hparams(); hp.ns_steps = 13
+    assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_UNSUPPORTED
+    assert plan_status([(4, 4)], ns_dtype="f32", hp=hp) == 0
+    hp = L.default_hparams(); hp.ns_steps = 16
+    assert plan_status([(4, 4)], ns_dtype="f32", hp=hp) == 0
+    hp = L.default_hparams(); hp.ns_steps = 12
+    assert plan_status([(4, 4)], hp=hp) == 0
     hp = L.default_hparams(); hp.rownorm_eps = 0.0
     assert plan_status([(4, 4)], hp=hp) == L.MUON_ERR_INVALID_ARGUMENT
     hp = L.default_hparams(); hp.momentum = float("nan")
@@ -97,7 +106,8 @@ def test_fused_recursion_rule():
     assert not L.Plan([(128, 3584)], ns_dtype="f32").buckets()[0]["fused"]  # fp32 path
     assert L.Plan([(3584, 64)]).buckets()[0]["fused"]  # tall: r = 64
     assert not L.Plan([(200, 900)]).buckets()[0]["fused"]  # r_pad = 256
-    assert L.Plan([(64, 64)], formulation="gram").buckets()[0]["fused"]
+    assert L.Plan([(64, 80)]).buckets()[0]["fused"]  # c > 1.125 r: Gram form
+    assert not L.Plan([(64, 72)]).buckets()[0]["fused"]  # near-square: direct form
 
 
 def _scales(n, ns_dtype="bf16", **coef):
@@ -116,14 +126,14 @@ def test_operand_scales_follow_the_iteration_bounds():
     # bounds do not depend on N and keep their scales.
     a = float(np.float32(3.4445))
     assert _scales(5) == (16384.0, 16384.0, 8192.0, 64.0, 256.0)
-    for n in range(1, 17):
+    for n in range(1, 13):
         expect = 64.0
         while 1.05 * a ** n * expect > 65504.0:
             expect /= 2
         s = _scales(n)
         assert s[3] == expect, (n, s)
         assert (s[0], s[1], s[4]) == (16384.0, 16384.0, 256.0)
-    assert _scales(8)[3] == 2.0 and _scales(16)[3] == 2.0 ** -13
+    assert _scales(8)[3] == 2.0 and _scales(12)[3] == 2.0 ** -6
     assert _scales(5, ns_dtype="f32") == (1.0,) * 5
 
 
@@ -195,24 +205,24 @@ def test_workspace_size_query_matches_plan():
 
 
 def test_formulation_choice_and_validation():
-    # AUTO plans the Gram form for non-square buckets and the direct form for
-    # squares; DIRECT keeps X and X^T twice plus two r x r buffers, all on
-    # 256-wide tiles.
+    # AUTO plans the Gram form for buckets with c > 1.125 r and the direct
+    # form for near-square ones on the 16-bit path; DIRECT keeps X and X^T
+    # twice plus two r x r buffers, all on 256-wide tiles.
     rect = [(600, 1000), (1000, 600)]
     assert L.Plan(rect, formulation="auto").workspace_bytes == \
         L.Plan(rect, formulation="gram").workspace_bytes
     sq = [(1024, 1024)] * 2
     assert L.Plan(sq, formulation="auto").workspace_bytes == \
-        L.Plan(sq, formulation="direct").workspace_bytes != L.Plan(sq, formulation="gram").workspace_bytes
+        L.Plan(sq, formulation="direct").workspace_bytes
     # on the fp32 path AUTO stays with the Gram form
     assert L.Plan(sq, "f32", "f32", formulation="auto").workspace_bytes == \
         L.Plan(sq, "f32", "f32", formulation="gram").workspace_bytes
-    shapes = [(1024, 1024), (600, 1000), (1000, 600)]
+    shapes = [(1200, 1024), (600, 1000), (1000, 600)]
     gram = L.Plan(shapes, formulation="gram")
     direct = L.Plan(shapes, formulation="direct")
     assert direct.info() == gram.info() == (3, 3)
-    r_pad = {(1024, 1024): 1024, (600, 1000): 768, (1000, 600): 768}
-    c_pad = {(1024, 1024): 1024, (600, 1000): 1024, (1000, 600): 1024}
+    r_pad = {(1200, 1024): 1024, (600, 1000): 768, (1000, 600): 768}
+    c_pad = {(1200, 1024): 1280, (600, 1000): 1024, (1000, 600): 1024}
     per_mat = [4 * r_pad[s] * c_pad[s] * 2 + 2 * r_pad[s] ** 2 * 2 for s in shapes]
     assert direct.workspace_bytes >= max(per_mat)
     # unknown formulation; direct form on the fp32 path
@@ -222,6 +232,26 @@ def test_formulation_choice_and_validation():
         L.Plan([(64, 64)], "f32", "f32", formulation="direct")
     assert e.value.status == L.MUON_ERR_UNSUPPORTED
     L.Plan([(64, 64)], "f32", "f32", formulation="gram")
+
+
+def test_near_square_buckets_take_the_direct_form():
+    # c <= 1.125 r: the Gram form's fp16 recursion resolves the small
+    # singular values of near-square inputs too coarsely for the 2e-2 bound,
+    # so AUTO takes the direct form and a forced Gram form is refused on the
+    # 16-bit path (the fp32 path keeps it)
+    uns = L.MUON_ERR_UNSUPPORTED
+    for m, n, direct in [(64, 72, True), (64, 73, False), (100, 112, True), (100, 113, False),
+                         (127, 128, True), (128, 129, True), (63, 64, True), (1, 1, True),
+                         (3584, 4032, True), (3584, 4033, False), (512, 768, False)]:
+        for shape in ((m, n), (n, m)):
+            b = L.Plan([shape]).buckets()[0]
+            assert (b["formulation"] == "direct") == direct, (shape, b)
+            g = plan_status([shape], formulation="gram")
+            assert g == (uns if direct else 0), (shape, g)
+            assert plan_status([shape], formulation="gram", hints={shape: {"formulation": "gram"}}) == g
+            assert plan_status([shape], grad_dtype="f32", ns_dtype="f32", formulation="gram") == 0
+    # a plan-wide Gram form with one near-square bucket is refused as a whole
+    assert plan_status([(256, 1024), (300, 300)], formulation="gram") == uns
 
 
 def test_kernel_class_enum_matches_binding():
@@ -256,14 +286,14 @@ def test_bucket_info_reports_the_planner_rule():
 
 
 def test_bucket_hints_override_tile_and_formulation():
-    shapes = [(3584, 18944), (1024, 1024), (384, 1000), (700, 300)]
-    hints = {(3584, 18944): {"tile": 128}, (1024, 1024): {"formulation": "gram"},
+    shapes = [(3584, 18944), (1024, 1280), (384, 1000), (700, 300)]
+    hints = {(3584, 18944): {"tile": 128}, (1024, 1280): {"formulation": "gram"},
              (384, 1000): {"tile": 256, "formulation": "gram"},
              (700, 300): {"formulation": "direct"},
              (5, 5): {"tile": 64}}                     # matches no matrix: ignored
     b = {x["shape"]: x for x in L.Plan(shapes, hints=hints).buckets()}
     assert (b[(3584, 18944)]["tile"], b[(3584, 18944)]["formulation"]) == (128, "gram")
-    assert (b[(1024, 1024)]["tile"], b[(1024, 1024)]["formulation"]) == (256, "gram")
+    assert (b[(1024, 1280)]["tile"], b[(1024, 1280)]["formulation"]) == (256, "gram")
     assert (b[(384, 1000)]["tile"], b[(384, 1000)]["formulation"]) == (256, "gram")
     assert (b[(700, 300)]["tile"], b[(700, 300)]["formulation"]) == (256, "direct")
     # a 128-wide tile on a 3584-row bucket keeps fp32 master copies: more workspace
@@ -283,8 +313,8 @@ def test_bucket_hints_validation():
     # two hints for one shape
     lib = L.load()
     rows = (ctypes.c_int64 * 1)(64)
-    cols = (ctypes.c_int64 * 1)(64)
-    harr = (L.BucketHint * 2)(L.BucketHint(64, 64, 64, 1), L.BucketHint(64, 64, 128, 1))
+    cols = (ctypes.c_int64 * 1)(80)
+    harr = (L.BucketHint * 2)(L.BucketHint(64, 80, 64, 1), L.BucketHint(64, 80, 128, 1))
     desc = L.PlanDesc()
     desc.num_matrices = 1
     desc.rows = ctypes.cast(rows, ctypes.POINTER(ctypes.c_int64))
@@ -308,7 +338,8 @@ def test_bucket_hints_validation():
     assert plan_status([(64, 64)], grad_dtype="f32", ns_dtype="f32",
                        hints={(64, 64): {"formulation": "direct"}}) == uns
     assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128}}) == uns   # direct needs 256
-    assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128, "formulation": "gram"}}) == 0
+    assert plan_status([(512, 640)], hints={(512, 640): {"tile": 128, "formulation": "gram"}}) == 0
+    assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128, "formulation": "gram"}}) == uns
     assert plan_status([(300, 700)], hints={(300, 700): {"tile": 64, "formulation": "direct"}}) == uns
 
 

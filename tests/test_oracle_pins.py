@@ -281,3 +281,48 @@ def test_ns5_is_not_polar():
     s = np.linalg.svd(O.ns5_direct(M), compute_uv=False)
     assert np.max(np.abs(s - 1.0)) > 0.05
     assert np.max(s) <= 1.2025
+
+
+def test_non_finite_inputs_reach_the_whole_direction():
+    # The pages' formulas on a gradient holding a NaN or an Inf: ||U||_F is
+    # NaN or Inf, so X0 = U / ||U||_F holds a NaN (NaN / x, Inf / Inf) and
+    # eq. (2) spreads it through X X^T to every entry: the matrix's direction
+    # and weights are all NaN.  The momentum keeps NaN / Inf only where the
+    # gradient had it.  R_eps works row by row: only the affected oriented row
+    # changes (NaN row for a NaN; for an Inf, NaN at the Inf and 0 elsewhere,
+    # as x / Inf = 0).
+    rng = np.random.default_rng(21)
+    W = rng.standard_normal((6, 9)) * 0.02
+    with np.errstate(invalid="ignore"):
+        _non_finite_cases(rng, W)
+
+
+def _non_finite_cases(rng, W):
+    for bad in (np.nan, np.inf, -np.inf):
+        G = rng.standard_normal((6, 9)) * 1e-3
+        G[2, 3] = bad
+        Wn, Mn, O = O.muon_step(W, np.zeros_like(W), G, 0.02, 0.1)
+        assert np.isnan(O).all() and np.isnan(Wn).all()
+        assert np.isfinite(np.delete(Mn.ravel(), 2 * 9 + 3)).all()
+        assert Mn[2, 3] == bad or (np.isnan(bad) and np.isnan(Mn[2, 3]))
+        Wr, Mr, R = O.rownorm_step(W, np.zeros_like(W), G, 0.02, 0.1)
+        others = [i for i in range(6) if i != 2]
+        assert np.isfinite(R[others]).all() and np.isfinite(Wr[others]).all()
+        if np.isnan(bad):
+            assert np.isnan(R[2]).all()
+        else:
+            assert np.isnan(R[2, 3]) and (np.delete(R[2], 3) == 0).all()
+        # tall: the oriented rows are columns of U
+        Wt, Mt, Rt = O.rownorm_step(W.T, np.zeros_like(W.T), G.T, 0.02, 0.1)
+        assert np.array_equal(np.isnan(Rt), np.isnan(R.T))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("shape", [(3584, 3584), (3584, 18944), (4096, 16384)])
+def test_gram_and_direct_agree_at_full_size(shape):
+    # The Gram-space routine stands in for the direct definition at the
+    # workloads' full sizes (it needs a quarter of the flops on wide
+    # matrices); pin the two together there in float64.
+    rng = np.random.default_rng(shape[1])
+    X = rng.standard_normal(shape)
+    assert rel(O.ns5_gram(X), O.ns5_direct(X)) < 1e-10

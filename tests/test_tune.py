@@ -25,8 +25,27 @@ def test_candidates_are_plannable():
                 b = L.Plan([shape], "f32", ns, hints={shape: c}).buckets()[0]
                 assert (b["tile"], b["formulation"]) == (c["tile"], c["formulation"])
     assert {c["formulation"] for c in TU.candidates(300, 700, "f32")} == {"gram"}
-    assert {c["tile"] for c in TU.candidates(3584, 3584, "bf16")} == {128, 256}
+    # near-square buckets of the 16-bit path: the planner refuses the Gram form
+    assert TU.candidates(3584, 3584, "bf16") == [{"tile": 256, "formulation": "direct"}]
+    assert TU.candidates(64, 70, "bf16") == [{"tile": 256, "formulation": "direct"}]
+    assert {c["tile"] for c in TU.candidates(3584, 3584, "f32")} == {64, 128}
     assert 64 in {c["tile"] for c in TU.candidates(1024, 4096, "bf16")}
+
+
+def test_tune_never_picks_an_inaccurate_setting():
+    # the fastest candidate misses the accuracy bound: recorded, not chosen
+    table = {(None, None): (10.0, 3e-3), (64, "gram"): (1.0, 5e-2), (128, "gram"): (7.5, 4e-3),
+             (256, "gram"): (9.0, 4e-3), (256, "direct"): (8.0, 3e-3)}
+    timer = lambda m, n, c, h: table[(None, None) if h is None else (h["tile"], h["formulation"])]
+    cache = TU.tune([(512, 2048)], "bf16", "bf16", device=DEV, timer=timer)
+    e = cache["entries"][TU.cache_key(DEV, "bf16", "bf16", 512, 2048, 1)]
+    assert (e["tile"], e["formulation"], e["ms"]) == (128, "gram", 7.5)
+    rej = [c for c in e["candidates"] if c.get("rejected")]
+    assert [(c["tile"], c["formulation"], c["err"]) for c in rej] == [(64, "gram", 5e-2)]
+    # no candidate within the bound: an error, not a silent choice
+    bad = lambda m, n, c, h: (1.0, 1.0)
+    with pytest.raises(RuntimeError):
+        TU.tune([(512, 2048)], "bf16", "bf16", device=DEV, timer=bad)
 
 
 def test_tune_picks_the_fastest_and_skips_cached_shapes():
