@@ -301,8 +301,8 @@ def _non_finite_cases(rng, W):
     for bad in (np.nan, np.inf, -np.inf):
         G = rng.standard_normal((6, 9)) * 1e-3
         G[2, 3] = bad
-        Wn, Mn, O = O.muon_step(W, np.zeros_like(W), G, 0.02, 0.1)
-        assert np.isnan(O).all() and np.isnan(Wn).all()
+        Wn, Mn, D = O.muon_step(W, np.zeros_like(W), G, 0.02, 0.1)
+        assert np.isnan(D).all() and np.isnan(Wn).all()
         assert np.isfinite(np.delete(Mn.ravel(), 2 * 9 + 3)).all()
         assert Mn[2, 3] == bad or (np.isnan(bad) and np.isnan(Mn[2, 3]))
         Wr, Mr, R = O.rownorm_step(W, np.zeros_like(W), G, 0.02, 0.1)
