@@ -56,7 +56,8 @@ def test_direct_iteration_counts(steps):
 
 
 def test_direct_is_deterministic_and_close_to_gram():
-    shapes = [(512, 512), (768, 1536)]
+    # (the Gram form is refused on near-square buckets of the 16-bit path)
+    shapes = [(512, 640), (768, 1536)]
     W, M, G = seeded(shapes, 31, mscale=1e-3)
     (W1, _, O1), _ = run(shapes, W, M, G, LR, WD, formulation="direct")
     (W2, _, O2), _ = run(shapes, W, M, G, LR, WD, formulation="direct")

@@ -11,9 +11,9 @@ from tests.test_gpu_parity import LR, WD, seeded
 
 pytestmark = pytest.mark.gpu
 
-# Rectangular only: the planner gives squares the direct form, and the Gram
-# form on a small square misses the 2e-2 bar with or without fusion (64 x 64,
-# N = 5: 2.8e-2 launch by launch, 2.3e-2 fused).
+# Clearly rectangular only: near-square buckets (c <= 1.125 r) take the
+# direct form, and the planner refuses the Gram form there on the 16-bit path
+# (on a small square it misses the 2e-2 bar: 64 x 64, N = 5, 2.5e-2).
 SHAPES = [(100, 900), (900, 100), (128, 3584), (40, 300), (64, 200)]
 
 

@@ -266,9 +266,87 @@ def test_qwen_layer_full_size(idx):
 
 @pytest.mark.parametrize("shape", [(1, 1), (200, 200), (256, 256), (1024, 1024)])
 def test_gram_form_on_squares(shape):
-    # AUTO takes the direct form for squares; the Gram form stays available
+    # The fp32 path evaluates squares in the Gram form; the 16-bit path
+    # refuses it there (the direct form is AUTO's choice and the accurate one)
     W, M, G = seeded([shape], 3 + shape[0], mscale=1e-3)
-    check_ns([shape], W, M, G, "bf16", label=f"gram {shape}", formulation="gram")
+    check_ns([shape], W, M, G, "f32", label=f"gram {shape}", formulation="gram")
+    from matrix_aware_optimizer_muon_amd import MuonError, Plan
+    with pytest.raises(MuonError) as e:
+        Plan([shape], "f32", "bf16", formulation="gram")
+    assert e.value.status == 2  # MUON_ERR_UNSUPPORTED
+
+
+# Near-square shapes (c <= 1.125 r, both orientations) take the direct form
+# under AUTO; just past the rule they take the Gram form (fused recursion for
+# r <= 128, small tiles, 256-wide tiles).  Measured NS error of the Gram form
+# there: <= 8.2e-3 over r = 40..1000.
+@pytest.mark.parametrize("shape", [(63, 64), (64, 72), (100, 110), (120, 128), (127, 128),
+                                   (128, 129), (64, 73), (100, 113), (300, 338), (1000, 1126)])
+def test_near_square_shapes_under_auto(shape):
+    shapes = [shape, shape[::-1], shape]
+    W, M, G = seeded(shapes, 500 + shape[0] + shape[1], mscale=1e-3)
+    r, c = min(shape), max(shape)
+    (_, _, _), plan = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=False)
+    want = "direct" if 8 * c <= 9 * r else "gram"
+    assert all(b["formulation"] == want for b in plan.buckets()), plan.buckets()
+    check_ns(shapes, W, M, G, "bf16", label=f"near-square {shape}")
+
+
+# Hyper-parameters other than the pages' defaults on every evaluation path:
+# no Nesterov blend (U = M'), mu = 0.9, scale coefficient 0.3, with a
+# non-zero prior momentum so that mu and the blend both matter.
+@pytest.mark.parametrize("ns_dtype,form", [("bf16", "gram"), ("bf16", "direct"), ("bf16", "auto"),
+                                           ("f32", "gram")])
+@pytest.mark.parametrize("nesterov,mu,scale", [(0, 0.95, 0.2), (1, 0.9, 0.2), (1, 0.95, 0.3),
+                                               (0, 0.9, 0.3)])
+def test_other_hyper_parameters(ns_dtype, form, nesterov, mu, scale):
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    hp = default_hparams()
+    hp.nesterov, hp.momentum, hp.scale_coeff = nesterov, mu, scale
+    shapes = [(256, 1024), (1024, 256), (300, 700), (700, 300), (1024, 1536)]
+    if form == "auto":
+        shapes += [(300, 300), (1024, 1024)]  # squares: direct form
+    W, M, G = seeded(shapes, 600 + 10 * nesterov + int(100 * mu) + int(10 * scale), mscale=2e-3)
+    (Wg, Mg, Og), _ = run(shapes, W, M, G, LR, WD, "f32", ns_dtype, hp=hp, formulation=form)
+    ohp = OR.Hyper(nesterov=bool(nesterov), momentum=mu, scale_coeff=scale)
+    for i, (m, n) in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=ohp)
+        assert rel(Og[i], Oo) <= TOL_NS[ns_dtype], (shapes[i], rel(Og[i], Oo))
+        assert rel(Mg[i], Mo) <= 1e-6
+        if ns_dtype == "f32":
+            assert rel(Wg[i], Wo) <= 1e-5, (shapes[i], rel(Wg[i], Wo))
+        else:
+            W_epi = OR.apply_update(W[i], Og[i], LR, WD, OR.update_scale(m, n, scale))
+            assert rel(Wg[i], W_epi) <= 1e-5
+
+
+# A NaN or Inf in a gradient: the NS step gives that matrix an all-NaN
+# direction and weights (the plain formula's X / ||X||_F spreads it through
+# X X^T), RowNorm only the affected oriented row (column when tall); other
+# matrices of the call are unaffected.
+@pytest.mark.parametrize("ns_dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_non_finite_gradient(ns_dtype, bad):
+    shapes = [(256, 1024), (1024, 256), (300, 300), (256, 1024)]
+    W, M, G = seeded(shapes, 31, mscale=1e-3)
+    for i in range(3):
+        G[i][5, 7] = bad
+    for rownorm in (False, True):
+        (Wg, Mg, Og), _ = run(shapes, W, M, G, LR, WD, "f32", ns_dtype, rownorm=rownorm)
+        for i in range(3):
+            with np.errstate(invalid="ignore"):
+                step = OR.rownorm_step if rownorm else OR.muon_step
+                Wo, Mo, Oo = step(W[i], M[i], G[i], LR, WD)
+            assert np.array_equal(np.isnan(Og[i]), np.isnan(Oo)), (shapes[i], rownorm)
+            assert np.array_equal(np.isnan(Wg[i]), np.isnan(Wo)), (shapes[i], rownorm)
+            assert np.array_equal(np.isfinite(Mg[i]), np.isfinite(Mo))
+            if rownorm:
+                fin = np.isfinite(Oo)
+                assert rel(Og[i][fin], Oo[fin]) <= 1e-6
+        # the clean matrix of the same call
+        step = OR.rownorm_step if rownorm else OR.muon_step
+        Wo, Mo, Oo = step(W[3], M[3], G[3], LR, WD)
+        assert rel(Og[3], Oo) <= (1e-6 if rownorm else TOL_NS[ns_dtype])
 
 
 @pytest.mark.parametrize("form", ["gram", "direct"])
@@ -276,7 +354,9 @@ def test_final_update_without_direction_output_matches(form):
     # The epilogues that update W (the final product; in the direct form the
     # last X' product, or the update pass for tall matrices) write O_out only
     # when it is given; W' must not depend on it.
-    shapes = [(1024, 3072), (3072, 1024), (1000, 2000), (2000, 1000), (1536, 1536)]
+    shapes = [(1024, 3072), (3072, 1024), (1000, 2000), (2000, 1000)]
+    if form == "direct":
+        shapes.append((1536, 1536))  # (a near-square bucket takes the direct form only)
     W, M, G = seeded(shapes, 77, mscale=1e-3)
     (W_o, M_o, _), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=True, formulation=form)
     (W_n, M_n, _), _ = run(shapes, W, M, G, LR, WD, "f32", "bf16", want_out=False, formulation=form)

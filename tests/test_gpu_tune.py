@@ -1,6 +1,6 @@
 """GPU parity of the settings only per-shape hints reach (muon_bucket_hint:
-small tiles on large 16-bit buckets, 256-wide tiles on small ones, the Gram
-form on squares, the direct form on rectangles), and the tuner end to end.
+small tiles on large 16-bit buckets, 256-wide tiles on small ones, the direct
+form on rectangles), and the tuner end to end.
 Same bars as the other parity tests: NS output <= 2e-2 relative Frobenius on
 the 16-bit path (<= 1e-5 on the weights of the fp32 path), momentum <= 1e-6,
 the update epilogue <= 1e-5 against the oracle applied to the GPU's output."""
@@ -27,8 +27,8 @@ def _gpu():
     ((384, 1000), {"tile": 256, "formulation": "gram"}),    # default: small tiles
     ((1000, 384), {"tile": 256, "formulation": "gram"}),
     ((700, 300), {"formulation": "direct"}),                # default: Gram form
-    ((1000, 1000), {"tile": 128, "formulation": "gram"}),   # default: direct form
-    ((257, 257), {"tile": 256, "formulation": "gram"}),
+    ((1000, 1130), {"tile": 128, "formulation": "gram"}),   # just past the near-square rule
+    ((257, 300), {"tile": 256, "formulation": "gram"}),     # default: small tiles
 ])
 def test_hinted_bucket_parity(shape, hint):
     shapes = [shape] * 3
@@ -46,6 +46,14 @@ def test_hinted_fp32_path_parity(tile):
     W, M, G = seeded(shapes, 60 + tile, mscale=1e-3)
     hints = {s: {"tile": tile} for s in shapes}
     check_ns(shapes, W, M, G, "f32", label=f"fp32 tile {tile}", hints=hints)
+
+
+def test_gram_hint_on_a_near_square_bucket_is_refused():
+    from matrix_aware_optimizer_muon_amd import MuonError, Plan
+    for shape in [(1000, 1000), (64, 64), (257, 257), (1000, 1100)]:
+        with pytest.raises(MuonError) as e:
+            Plan([shape], "f32", "bf16", hints={shape: {"formulation": "gram"}})
+        assert e.value.status == 2  # MUON_ERR_UNSUPPORTED
 
 
 def test_tuner_end_to_end():
