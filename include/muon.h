@@ -87,10 +87,14 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *                     flops.  16-bit path only (ns_dtype MUON_BF16): X is
  *                     kept as scaled fp16 in both layouts; every product
  *                     uses 256-wide tiles.
- *   MUON_FORM_AUTO:   per bucket: the direct form for square matrices on
- *                     the 16-bit path (equal flops, 20 r^3, in fewer and
- *                     larger products), the Gram form otherwise (fewer flops
- *                     whenever c > r). */
+ *   MUON_FORM_AUTO:   per bucket: the direct form for near-square matrices
+ *                     (c <= 1.125 r) on the 16-bit path, the Gram form
+ *                     otherwise (fewer flops whenever c > r).
+ * On the 16-bit path the Gram form is refused (MUON_ERR_UNSUPPORTED, plan-
+ * wide or per hint) for near-square buckets: the recursion on X X^T squares
+ * the spectrum, and fp16 resolves the small singular values of near-square
+ * inputs too coarsely (measured NS error up to 3.2e-2 on squares against
+ * the 2e-2 bound; 0.8e-2 at most from c > 1.125 r on). */
 typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } muon_formulation;
 
 /* Per-shape override of the planner's choices for one bucket (the matrices
@@ -122,7 +126,9 @@ typedef struct {
 typedef struct {
   float momentum;      /* mu in M <- mu*M + G                               */
   int   nesterov;      /* 1: NS / RowNorm input U = mu*M' + G; 0: U = M'      */
-  int   ns_steps;      /* Newton-Schulz iterations, 1..16                   */
+  int   ns_steps;      /* Newton-Schulz iterations: 1..12 on the 16-bit path
+                          (where the 2e-2 accuracy bound holds), 1..16 on
+                          the fp32 path                                     */
   float a, b, c;       /* quintic coefficients                              */
   float scale_coeff;   /* s(W) = scale_coeff * sqrt(max(m, n))              */
   float rownorm_eps;   /* eps of R_eps, > 0                                 */
@@ -195,7 +201,13 @@ typedef struct {
  * info, or an index out of range. */
 muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_info* info);
 
-/* Newton-Schulz (refresh) step for every planned matrix (Gram form shown;
+/* Non-finite inputs: a NaN or an infinity in a matrix's U (its gradient or
+ * momentum), or a squared norm past fp32's range, makes that matrix's
+ * direction and weights NaN in muon_step_batched, as the plain formula
+ * X0 = U / ||U||_F does (no silently finite step); rownorm_step confines it
+ * to the affected oriented rows.  Other matrices of the call are unaffected.
+ *
+ * Newton-Schulz (refresh) step for every planned matrix (Gram form shown;
  * the direct form evaluates the same X_N by iterating eq. (2) on X):
  *   M  <- mu*M + G                                   ("Infra Optimizers" eq. (1))
  *   U   = mu*M + G  (updated M; U = M if nesterov=0)  (Background, Nesterov)
@@ -224,6 +236,34 @@ muon_status rownorm_step(muon_plan_t plan, float* const* W, float* const* M,
                          const void* const* G, float lr, float weight_decay,
                          void* workspace, size_t workspace_bytes, hipStream_t stream,
                          float* const* R_out);
+
+/* Size of the scratch array the library keeps on every GPU it runs on for
+ * muon_step_batched_noalloc (64 MiB; allocated when the library's code is
+ * loaded onto a GPU and held until the process ends). */
+#define MUON_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* muon_step_batched for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, arguments and results, with the
+ * workspace taken from the library's own per-GPU scratch array of
+ * MUON_NOALLOC_WORKSPACE_BYTES instead of a caller buffer.  The call
+ * allocates nothing (no hipMalloc / hipFree, no pinned host staging; the
+ * pointer table is written by a kernel from its arguments).
+ *   - The plan's single-stream workspace (every bucket on `stream`; plan
+ *     with max_workspace_bytes a few MiB below the limit so that the
+ *     Newton-Schulz scratch is chunked to fit) must not exceed
+ *     MUON_NOALLOC_WORKSPACE_BYTES: else MUON_ERR_WORKSPACE_TOO_SMALL and
+ *     nothing is enqueued.  Buckets never run on internal streams here.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     the GPU (other streams, other host threads, other plans) race and give
+ *     undefined results; order them on one stream or synchronise.
+ *   - The array's contents between calls are irrelevant (every call rewrites
+ *     what it reads).  The launch profiler does not record these calls.
+ * Errors as for muon_step_batched; MUON_ERR_HIP also when the current
+ * device's scratch address cannot be obtained. */
+muon_status muon_step_batched_noalloc(muon_plan_t plan, float* const* W, float* const* M,
+                                      const void* const* G, float lr, float weight_decay,
+                                      hipStream_t stream, float* const* O_out);
 
 /* Kernel classes reported by the launch profiler. */
 typedef enum {

@@ -23,8 +23,11 @@ MUON_ERR_HIP = 4
 MUON_F32 = 0
 MUON_BF16 = 1
 
+NOALLOC_WORKSPACE_BYTES = 64 << 20  # MUON_NOALLOC_WORKSPACE_BYTES
+
 EXPORTED = ("muon_default_hparams", "muon_plan", "muon_plan_destroy", "muon_plan_workspace_size",
-            "muon_plan_info", "muon_plan_bucket_info", "muon_step_batched", "rownorm_step", "muon_plan_set_profiling",
+            "muon_plan_info", "muon_plan_bucket_info", "muon_step_batched",
+            "muon_step_batched_noalloc", "rownorm_step", "muon_plan_set_profiling",
             "muon_plan_kernel_times", "muon_status_string")
 KERNEL_CLASSES = ("prep", "norm", "syrk", "poly", "pqpg", "ph", "final", "rownorm", "colsum",
                   "colfinal", "colapply", "xcast", "xupd", "wupd")
@@ -92,6 +95,9 @@ def load() -> ctypes.CDLL:
                  ctypes.c_float, P, ctypes.c_size_t, P, ctypes.POINTER(P)]
     lib.muon_step_batched.argtypes = step_args
     lib.rownorm_step.argtypes = step_args
+    lib.muon_step_batched_noalloc.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P),
+                                              ctypes.POINTER(P), ctypes.c_float, ctypes.c_float,
+                                              P, ctypes.POINTER(P)]
     lib.muon_plan_set_profiling.argtypes = [P, ctypes.c_int]
     D = ctypes.POINTER(ctypes.c_double)
     lib.muon_plan_kernel_times.argtypes = [P, D, ctypes.POINTER(ctypes.c_int64), D, D]
@@ -99,7 +105,7 @@ def load() -> ctypes.CDLL:
     lib.muon_status_string.restype = ctypes.c_char_p
     for name in ("muon_default_hparams", "muon_plan", "muon_plan_destroy",
                  "muon_plan_workspace_size", "muon_plan_info", "muon_plan_bucket_info",
-                 "muon_step_batched",
+                 "muon_step_batched", "muon_step_batched_noalloc",
                  "rownorm_step", "muon_plan_set_profiling", "muon_plan_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -207,6 +213,19 @@ class Plan:
         """muon_step_batched on raw device pointers."""
         self._call(self._lib.muon_step_batched, "muon_step_batched", W, M, G, lr, wd,
                    workspace_ptr, workspace_bytes, stream, O_out)
+
+    def step_noalloc_ptrs(self, W, M, G, lr, wd, stream=0, O_out=None):
+        """muon_step_batched_noalloc on raw device pointers (the library's own
+        per-GPU scratch instead of a workspace)."""
+        n = len(self.shapes)
+        if not (len(W) == len(M) == len(G) == n):
+            raise ValueError(f"expected {n} matrices")
+        o_arr = _ptr_array(O_out) if O_out is not None else None
+        st = self._lib.muon_step_batched_noalloc(
+            self._handle, _ptr_array(W), _ptr_array(M), _ptr_array(G), ctypes.c_float(lr),
+            ctypes.c_float(wd), ctypes.c_void_p(stream or 0), o_arr)
+        if st != MUON_OK:
+            raise MuonError(st, "muon_step_batched_noalloc")
 
     def rownorm_ptrs(self, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream=0, R_out=None):
         """rownorm_step on raw device pointers."""

@@ -495,6 +495,19 @@ hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int v
 }
 
 // ---------------------------------------------------------------------------
+// Pointer-table upload from kernel arguments (one thread per entry).
+__global__ void __launch_bounds__(64) write_table_kernel(const TableChunk t, MatPtrs* dst) {
+  const int i = threadIdx.x;
+  if (i < t.count) dst[i] = t.e[i];
+}
+
+hipError_t launch_write_table(const TableChunk& t, MatPtrs* dst, hipStream_t s) {
+  if (t.count < 1 || t.count > kTableChunk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(write_table_kernel, dim3(1), dim3(64), 0, s, t, dst);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Direct form.  X0 cast: each thread converts 8 consecutive elements (one
 // 16-byte load, one 16-byte store) of one of the two layouts in place.
 __global__ void __launch_bounds__(256) xcast_kernel(const XcastParams p) {

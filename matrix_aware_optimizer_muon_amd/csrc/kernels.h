@@ -86,6 +86,16 @@ struct RrFusedParams {
 };
 hipError_t launch_rr_fused(const RrFusedParams& p, int nmat, hipStream_t s);
 
+// Write up to kTableChunk pointer-table entries, passed by value as kernel
+// arguments, to dst[0 .. count) (the allocation-free step uploads its table
+// this way: no staging buffer and no host-memory copy).
+constexpr int kTableChunk = 32;
+struct TableChunk {
+  MatPtrs e[kTableChunk];
+  int count;
+};
+hipError_t launch_write_table(const TableChunk& t, MatPtrs* dst, hipStream_t s);
+
 // ---- memory-bound kernels ------------------------------------------------
 struct PrepParams {
   const MatPtrs* table;

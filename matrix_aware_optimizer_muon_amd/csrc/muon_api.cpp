@@ -24,6 +24,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <thread>
 #include <vector>
@@ -152,6 +153,18 @@ struct Slot {
   bool used = false;
 };
 
+// Byte offsets of the workspace parts.  Concurrent buckets: bucket b runs on
+// slot b % nslots, each slot with its own stream, scratch region and
+// partial-sum region; nslots == 1: every bucket on the caller's stream.
+// Streams and events are created on the first step call that needs them.
+struct Layout {
+  size_t off_table = 0, off_inv = 0, off_part = 0, off_colscale = 0, off_scratch = 0;
+  int nslots = 1;
+  std::vector<size_t> slot_scratch_off;  // bytes from off_scratch
+  size_t slot_part_floats = 0;           // floats per slot from off_part
+  size_t ws_bytes = 0;
+};
+
 struct TimedLaunch {
   hipEvent_t start = nullptr, stop = nullptr;
   int cls = 0;
@@ -170,17 +183,10 @@ struct muon_plan_s {
   std::vector<int64_t> rows, cols;
   std::vector<int> order;  // plan position -> caller index
   std::vector<Bucket> buckets;
-  // workspace layout
-  size_t off_table = 0, off_inv = 0, off_part = 0, off_colscale = 0, off_scratch = 0;
-  size_t ws_bytes = 0;
-  size_t max_scratch = 0;
-  // Concurrent buckets: bucket b runs on slot b % nslots, each slot with its
-  // own stream, scratch region and partial-sum region.  nslots == 1: every
-  // bucket on the caller's stream.  Streams and events are created on the
-  // first step call that needs them.
-  int nslots = 1;
-  std::vector<size_t> slot_scratch_off;  // bytes from off_scratch
-  size_t slot_part_floats = 0;           // floats per slot from off_part
+  // Workspace layouts: `lay` for the caller's workspace (concurrent buckets
+  // when the planner chose them), `serial` with every bucket on the caller's
+  // stream (the allocation-free step's layout in the library's own scratch).
+  Layout lay, serial;
   std::vector<hipStream_t> slot_streams;
   std::vector<hipEvent_t> slot_done;
   hipEvent_t fork_ev = nullptr;
@@ -189,8 +195,9 @@ struct muon_plan_s {
   int next_slot = 0;
   bool ring_ready = false;
   std::vector<MatPtrs> host_table;
-  // launch profiler
+  // launch profiler (prof_active: profiling and the running call records)
   bool profiling = false;
+  bool prof_active = false;
   std::vector<TimedLaunch> tpool;
   size_t tused = 0;
   double t_ms[MUON_K_COUNT] = {}, t_flops[MUON_K_COUNT] = {}, t_bytes[MUON_K_COUNT] = {};
@@ -271,7 +278,7 @@ muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
   if (s.used && hipEventSynchronize(s.ev) != hipSuccess) return MUON_ERR_HIP;
   const size_t bytes = sizeof(MatPtrs) * (size_t)p->nmat;
   std::memcpy(s.host, p->host_table.data(), bytes);
-  if (hipMemcpyAsync((char*)ws + p->off_table, s.host, bytes, hipMemcpyHostToDevice, stream) !=
+  if (hipMemcpyAsync((char*)ws + p->lay.off_table, s.host, bytes, hipMemcpyHostToDevice, stream) !=
       hipSuccess)
     return MUON_ERR_HIP;
   if (hipEventRecord(s.ev, stream) != hipSuccess) return MUON_ERR_HIP;
@@ -279,20 +286,51 @@ muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
   return MUON_OK;
 }
 
-muon_status validate_call(muon_plan_s* p, float* const* W, float* const* M, const void* const* G,
-                          float lr, float wd, void* ws, size_t ws_bytes) {
-  if (!p || !W || !M || !G || !ws) return MUON_ERR_INVALID_ARGUMENT;
+muon_status validate_args(muon_plan_s* p, float* const* W, float* const* M, const void* const* G,
+                          float lr, float wd) {
+  if (!p || !W || !M || !G) return MUON_ERR_INVALID_ARGUMENT;
   if (!finite(lr) || !finite(wd)) return MUON_ERR_INVALID_ARGUMENT;
-  if (((uintptr_t)ws & 255u) != 0) return MUON_ERR_INVALID_ARGUMENT;
   for (int64_t i = 0; i < p->nmat; ++i)
     if (!W[i] || !M[i] || !G[i]) return MUON_ERR_INVALID_ARGUMENT;
-  if (ws_bytes < p->ws_bytes) return MUON_ERR_WORKSPACE_TOO_SMALL;
   return MUON_OK;
 }
 
+muon_status validate_call(muon_plan_s* p, float* const* W, float* const* M, const void* const* G,
+                          float lr, float wd, void* ws, size_t ws_bytes) {
+  const muon_status st = validate_args(p, W, M, G, lr, wd);
+  if (st != MUON_OK) return st;
+  if (!ws || ((uintptr_t)ws & 255u) != 0) return MUON_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < p->lay.ws_bytes) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  return MUON_OK;
+}
+
+// The allocation-free step's scratch: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel or a copy (on the host it is only a
+// stand-in for the symbol): it takes each device's address once, through
+// hipGetSymbolAddress with that device current, and uses that.
+static __device__ __align__(256) unsigned char scratch[MUON_NOALLOC_WORKSPACE_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+muon_status noalloc_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MUON_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MUON_ERR_HIP;
+    g_scratch_dev[dev] = (char*)ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MUON_OK;
+}
+
+// host_table is sized at plan time, so this allocates nothing.
 void fill_table(muon_plan_s* p, float* const* W, float* const* M, const void* const* G,
                 float* const* O) {
-  p->host_table.resize((size_t)p->nmat);
   for (int64_t k = 0; k < p->nmat; ++k) {
     const int i = p->order[(size_t)k];
     p->host_table[(size_t)k] = MatPtrs{W[i], M[i], G[i], O ? O[i] : nullptr};
@@ -316,7 +354,7 @@ muon_status hip_ok(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_H
 // Run one launch, bracketed by profiler events when profiling is enabled.
 template <class F>
 muon_status timed(muon_plan_s* p, hipStream_t s, int cls, double flops, double bytes, F&& launch) {
-  if (!p->profiling) return hip_ok(launch());
+  if (!p->prof_active) return hip_ok(launch());
   if (p->tused == p->tpool.size()) {
     TimedLaunch t;
     if (hipEventCreate(&t.start) != hipSuccess) return MUON_ERR_HIP;
@@ -364,13 +402,13 @@ void release_slots(muon_plan_s* p) {
 
 // Internal streams (default priority) and their fork / join events.
 muon_status ensure_slots(muon_plan_s* p) {
-  if ((int)p->slot_streams.size() == p->nslots) return MUON_OK;
+  if ((int)p->slot_streams.size() == p->lay.nslots) return MUON_OK;
   release_slots(p);
   if (hipEventCreateWithFlags(&p->fork_ev, hipEventDisableTiming) != hipSuccess) {
     p->fork_ev = nullptr;
     return MUON_ERR_HIP;
   }
-  for (int i = 0; i < p->nslots; ++i) {
+  for (int i = 0; i < p->lay.nslots; ++i) {
     hipStream_t s = nullptr;
     hipEvent_t e = nullptr;
     if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
@@ -418,271 +456,21 @@ const muon_bucket_hint* find_hint(const muon_plan_desc* desc, int64_t m, int64_t
   return nullptr;
 }
 
-}  // namespace
-
-extern "C" {
-
-muon_status muon_default_hparams(muon_hparams* hp) {
-  if (!hp) return MUON_ERR_INVALID_ARGUMENT;
-  hp->momentum = 0.95f;
-  hp->nesterov = 1;
-  hp->ns_steps = 5;
-  hp->a = 3.4445f;
-  hp->b = -4.7750f;
-  hp->c = 2.0315f;
-  hp->scale_coeff = 0.2f;
-  hp->rownorm_eps = 1e-8f;
-  return MUON_OK;
-}
-
-const char* muon_status_string(muon_status s) {
-  switch (s) {
-    case MUON_OK: return "MUON_OK";
-    case MUON_ERR_INVALID_ARGUMENT: return "MUON_ERR_INVALID_ARGUMENT";
-    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
-    case MUON_ERR_WORKSPACE_TOO_SMALL: return "MUON_ERR_WORKSPACE_TOO_SMALL";
-    case MUON_ERR_HIP: return "MUON_ERR_HIP";
-  }
-  return "MUON_UNKNOWN_STATUS";
-}
-
-muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* workspace_bytes) {
-  if (!desc || !plan) return MUON_ERR_INVALID_ARGUMENT;
-  *plan = nullptr;
-  if (desc->num_matrices < 1 || !desc->rows || !desc->cols) return MUON_ERR_INVALID_ARGUMENT;
-  if (desc->num_matrices > (1ll << 24)) return MUON_ERR_UNSUPPORTED;
-  if (desc->grad_dtype != MUON_F32 && desc->grad_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
-  if (desc->ns_dtype != MUON_F32 && desc->ns_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
-  if (desc->max_workspace_bytes < 0) return MUON_ERR_INVALID_ARGUMENT;
-  const int form = (int)desc->formulation;
-  if (form != MUON_FORM_AUTO && form != MUON_FORM_GRAM && form != MUON_FORM_DIRECT)
-    return MUON_ERR_INVALID_ARGUMENT;
-  if (form == MUON_FORM_DIRECT && desc->ns_dtype == MUON_F32) return MUON_ERR_UNSUPPORTED;
-  muon_status st = validate_hp(desc->hp);
-  if (st != MUON_OK) return st;
-  NsScales scales;
-  if (desc->ns_dtype == MUON_BF16) {
-    if (desc->hp.ns_steps > kMaxSteps16) return MUON_ERR_UNSUPPORTED;
-    st = ns_scales(desc->hp, &scales);
-    if (st != MUON_OK) return st;
-  }
-  for (int64_t i = 0; i < desc->num_matrices; ++i) {
-    const int64_t m = desc->rows[i], n = desc->cols[i];
-    if (m < 1 || n < 1) return MUON_ERR_INVALID_ARGUMENT;
-    if (m > kMaxDim || n > kMaxDim || std::min(m, n) > kMaxShort) return MUON_ERR_UNSUPPORTED;
-  }
-  st = validate_hints(desc);
-  if (st != MUON_OK) return st;
-  muon_plan_s* p = nullptr;
-  try {
-    p = new muon_plan_s();
-    p->nmat = desc->num_matrices;
-    p->grad_dtype = desc->grad_dtype;
-    p->ns_dtype = desc->ns_dtype;
-    p->hp = desc->hp;
-    p->scales = scales;
-    p->rows.assign(desc->rows, desc->rows + desc->num_matrices);
-    p->cols.assign(desc->cols, desc->cols + desc->num_matrices);
-    const bool f32path = desc->ns_dtype == MUON_F32;
-    p->formulation = form;
-    const int64_t cap = desc->max_workspace_bytes > 0 ? desc->max_workspace_bytes : kDefaultCap;
-
-    // buckets in order of first appearance
-    std::vector<std::vector<int>> members;
-    for (int64_t i = 0; i < p->nmat; ++i) {
-      size_t b = 0;
-      for (; b < p->buckets.size(); ++b)
-        if (p->buckets[b].m == p->rows[i] && p->buckets[b].n == p->cols[i]) break;
-      if (b == p->buckets.size()) {
-        Bucket nb{};
-        nb.m = p->rows[i];
-        nb.n = p->cols[i];
-        p->buckets.push_back(nb);
-        members.emplace_back();
-      }
-      members[b].push_back((int)i);
-    }
-    size_t part_floats = 0, colscale_floats = 0, max_scratch = 0;
-    for (size_t b = 0; b < p->buckets.size(); ++b) {
-      Bucket& B = p->buckets[b];
-      B.transposed = B.m > B.n;
-      B.r = std::min(B.m, B.n);
-      B.c = std::max(B.m, B.n);
-      // AUTO: the direct form for near-square matrices (c <= 1.125 r) on the
-      // 16-bit path, the Gram form otherwise (3 r^2 c + 17 r^3 against
-      // 15 r^2 c + 5 r^3 flops for c > r).  Near-square inputs have singular
-      // values close to zero, which the Gram form's squared spectrum resolves
-      // badly in fp16: measured over r = 40..1000 (worst of two seeds, both
-      // orientations) the Gram form's NS error is 1.1e-2..3.2e-2 on squares
-      // and 0.8e-2 at worst from c > 1.125 r on, the direct form's 0.25e-2..
-      // 0.64e-2 everywhere; on squares the two cost the same 20 r^3 flops
-      // and the direct form measured 2-10 % faster (3.6x on 64 x 512^2).
-      const bool near_square = 8 * B.c <= 9 * B.r;
-      B.direct = p->formulation == MUON_FORM_DIRECT ||
-                 (p->formulation == MUON_FORM_AUTO && !f32path && near_square);
-      const muon_bucket_hint* hint = find_hint(desc, B.m, B.n);
-      if (hint && hint->formulation != MUON_FORM_AUTO) B.direct = hint->formulation == MUON_FORM_DIRECT;
-      if (!f32path && !B.direct && near_square) {
-        // a Gram form forced onto a near-square bucket on the 16-bit path
-        // would miss the accuracy the path promises (see above)
-        delete p;
-        return MUON_ERR_UNSUPPORTED;
-      }
-      B.bt = B.direct ? 256 : choose_tile(B.r, (int64_t)members[b].size(), f32path);
-      if (hint && hint->tile != 0) {
-        if (B.direct && hint->tile != 256) {
-          delete p;
-          return MUON_ERR_UNSUPPORTED;
-        }
-        B.bt = hint->tile;
-      }
-      B.r_pad = round_up(B.r, B.bt);
-      B.c_pad = round_up(B.c, B.bt);
-      B.first = (int)p->order.size();
-      B.count = (int)members[b].size();
-      for (int i : members[b]) p->order.push_back(i);
-      const int64_t xes = f32path ? 4 : 2;
-      const int64_t rr = B.r_pad * B.r_pad;
-      B.dma = !f32path && B.bt == 256;
-      B.fused_rr = !f32path && !B.dma && !B.direct && B.r_pad <= 128;
-      // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
-      // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
-      // the 256-tile path keeps only the fp16 copies
-      const int64_t rr_bytes =
-          f32path ? 5 * (int64_t)align256((size_t)(rr * 4))
-                  : (B.dma ? 0 : 4 * (int64_t)align256((size_t)(rr * 4))) +
-                        5 * (int64_t)align256((size_t)(rr * 2));
-      const int64_t xb = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes));
-      // direct form: X and X^T twice (double buffered) plus A and P~ in fp16
-      B.scratch_per_mat = B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) : 2 * xb + rr_bytes;
-      int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
-      per_chunk = std::min<int64_t>(per_chunk, B.count);
-      const int64_t nchunks = (B.count + per_chunk - 1) / per_chunk;
-      const int64_t even = (B.count + nchunks - 1) / nchunks;
-      for (int64_t f = 0; f < B.count; f += even)
-        B.chunks.push_back(Chunk{B.first + (int)f, (int)std::min<int64_t>(even, B.count - f)});
-      B.m_pad = B.transposed ? B.c_pad : B.r_pad;
-      B.n_pad = B.transposed ? B.r_pad : B.c_pad;
-      B.prep_blocks = prep_blocks_per_mat((int)B.m_pad, (int)B.n_pad);
-      B.rn_row_blocks = rownorm_row_blocks((int)B.m, (int)B.n);
-      B.chunk_scratch = (size_t)(even * B.scratch_per_mat);
-      max_scratch = std::max(max_scratch, B.chunk_scratch);
-      part_floats = std::max(part_floats, (size_t)even * (size_t)B.prep_blocks);
-      if (B.transposed) {
-        // RowNorm runs on whole buckets (no NS scratch needed)
-        part_floats = std::max(part_floats, (size_t)B.count * B.rn_row_blocks * (size_t)B.n);
-        colscale_floats = std::max(colscale_floats, (size_t)B.count * (size_t)B.n);
-      }
-    }
-    // Buckets too small to fill the device on their own (one launch chunk,
-    // every r x r product under two waves of tiles for the 256 compute
-    // units) run concurrently on up to kMaxSlots streams when their scratch
-    // regions fit the cap together; otherwise all run one after another.
-    const int nb = (int)p->buckets.size();
-    bool small = nb > 1;
-    for (const Bucket& B : p->buckets) {
-      const int64_t T = B.r_pad / B.bt;
-      if (B.chunks.size() != 1 || (int64_t)B.count * (T * (T + 1) / 2) >= 512) small = false;
-    }
-    int S = small ? std::min(nb, kMaxSlots) : 1;
-    std::vector<size_t> slot_bytes((size_t)S, 0);
-    for (int b = 0; b < nb; ++b)
-      slot_bytes[(size_t)(b % S)] = std::max(slot_bytes[(size_t)(b % S)],
-                                             align256(p->buckets[(size_t)b].chunk_scratch));
-    size_t total = 0;
-    for (size_t v : slot_bytes) total += v;
-    if (S > 1 && total > (size_t)cap) {
-      S = 1;
-      slot_bytes.assign(1, max_scratch);
-      total = max_scratch;
-    }
-    p->nslots = S;
-    p->slot_scratch_off.assign((size_t)S, 0);
-    for (size_t i = 1; i < (size_t)S; ++i)
-      p->slot_scratch_off[i] = p->slot_scratch_off[i - 1] + slot_bytes[i - 1];
-    p->slot_part_floats = align256(sizeof(float) * std::max<size_t>(part_floats, 1)) / sizeof(float);
-    p->off_table = 0;
-    p->off_inv = align256(sizeof(MatPtrs) * (size_t)p->nmat);
-    p->off_part = p->off_inv + align256(sizeof(float) * (size_t)p->nmat);
-    p->off_colscale = p->off_part + sizeof(float) * p->slot_part_floats * (size_t)S;
-    p->off_scratch = p->off_colscale + align256(sizeof(float) * std::max<size_t>(colscale_floats, 1));
-    p->max_scratch = total;
-    p->ws_bytes = p->off_scratch + total;
-  } catch (const std::bad_alloc&) {
-    delete p;
-    return MUON_ERR_INVALID_ARGUMENT;
-  }
-  *plan = p;
-  if (workspace_bytes) *workspace_bytes = p->ws_bytes;
-  return MUON_OK;
-}
-
-muon_status muon_plan_destroy(muon_plan_t plan) {
-  if (!plan) return MUON_OK;
-  release_ring(plan);
-  release_profile(plan);
-  release_slots(plan);
-  delete plan;
-  return MUON_OK;
-}
-
-muon_status muon_plan_workspace_size(muon_plan_t plan, size_t* workspace_bytes) {
-  if (!plan || !workspace_bytes) return MUON_ERR_INVALID_ARGUMENT;
-  *workspace_bytes = plan->ws_bytes;
-  return MUON_OK;
-}
-
-muon_status muon_plan_info(muon_plan_t plan, int64_t* num_buckets, int64_t* num_chunks) {
-  if (!plan) return MUON_ERR_INVALID_ARGUMENT;
-  int64_t nc = 0;
-  for (const auto& b : plan->buckets) nc += (int64_t)b.chunks.size();
-  if (num_buckets) *num_buckets = (int64_t)plan->buckets.size();
-  if (num_chunks) *num_chunks = nc;
-  return MUON_OK;
-}
-
-muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_info* info) {
-  if (!plan || !info || index < 0 || index >= (int64_t)plan->buckets.size())
-    return MUON_ERR_INVALID_ARGUMENT;
-  const Bucket& B = plan->buckets[(size_t)index];
-  info->rows = B.m;
-  info->cols = B.n;
-  info->count = B.count;
-  info->chunks = (int64_t)B.chunks.size();
-  info->tile = B.bt;
-  info->formulation = B.direct ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
-  info->transposed = B.transposed ? 1 : 0;
-  info->fused_recursion = B.fused_rr ? 1 : 0;
-  const NsScales& sc = plan->scales;
-  const float scales[5] = {sc.sG, sc.sP, sc.sH, sc.sQ, sc.sX};
-  std::memcpy(info->operand_scales, scales, sizeof scales);
-  return MUON_OK;
-}
-
-muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
-                              float lr, float wd, void* ws, size_t ws_bytes, hipStream_t stream,
-                              float* const* O_out) {
-  muon_status st = validate_call(p, W, M, G, lr, wd, ws, ws_bytes);
-  if (st != MUON_OK) return st;
-  try {
-    fill_table(p, W, M, G, O_out);
-  } catch (const std::bad_alloc&) {
-    return MUON_ERR_INVALID_ARGUMENT;
-  }
-  st = upload_table(p, ws, stream);
-  if (st != MUON_OK) return st;
-
-  char* wsb = (char*)ws;
-  const MatPtrs* d_table = (const MatPtrs*)(wsb + p->off_table);
-  float* d_inv = (float*)(wsb + p->off_inv);
+// Enqueue the refresh step of every bucket with workspace layout L at wsb
+// (the pointer table already at L.off_table), ordered after `caller`'s
+// earlier work; `caller` waits for all of it.
+muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr, float wd,
+                            hipStream_t caller) {
+  const MatPtrs* d_table = (const MatPtrs*)(wsb + L.off_table);
+  float* d_inv = (float*)(wsb + L.off_inv);
   const bool f32path = p->ns_dtype == MUON_F32;
   const int op = f32path ? OP_F32 : OP_BF16;
   const int xes = f32path ? 4 : 2;
   const int gbf16 = p->grad_dtype == MUON_BF16 ? 1 : 0;
   const muon_hparams& hp = p->hp;
   const int N = hp.ns_steps;
-  const int S = p->nslots;
-  const hipStream_t caller = stream;
+  const int S = L.nslots;
+  muon_status st = MUON_OK;
 
   // fork: every slot stream waits for the table upload on the caller's stream
   if (S > 1) {
@@ -701,8 +489,8 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
       if (only_slot >= 0 && (int)slot != only_slot) continue;
       const Bucket& B = p->buckets[bi];
       const hipStream_t stream = S > 1 ? p->slot_streams[slot] : caller;
-      char* scratch = wsb + p->off_scratch + p->slot_scratch_off[slot];
-      float* d_part = (float*)(wsb + p->off_part) + p->slot_part_floats * slot;
+      char* region = wsb + L.off_scratch + L.slot_scratch_off[slot];
+      float* d_part = (float*)(wsb + L.off_part) + L.slot_part_floats * slot;
       const int64_t rr = B.r_pad * B.r_pad;
       const int T = (int)(B.r_pad / B.bt);
       const int ntri = T * (T + 1) / 2;
@@ -711,7 +499,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
         // scratch layout for this chunk
         size_t off = 0;
         auto take = [&](size_t per_mat_bytes) {
-          char* q = scratch + off;
+          char* q = region + off;
           off += align256(per_mat_bytes) * (size_t)nm;
           return q;
         };
@@ -1054,7 +842,7 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
     return MUON_OK;
   };
   int dev = -1;
-  if (S > 1 && !p->profiling && hipGetDevice(&dev) == hipSuccess) {
+  if (S > 1 && !p->prof_active && hipGetDevice(&dev) == hipSuccess) {
     // Each slot's launch sequence is enqueued from its own host thread, so
     // that every slot's first kernels reach the GPU at once instead of after
     // the whole sequence of the slots before it (~13 us of host time per
@@ -1097,6 +885,296 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
   return st;
 }
 
+}  // namespace
+
+extern "C" {
+
+muon_status muon_default_hparams(muon_hparams* hp) {
+  if (!hp) return MUON_ERR_INVALID_ARGUMENT;
+  hp->momentum = 0.95f;
+  hp->nesterov = 1;
+  hp->ns_steps = 5;
+  hp->a = 3.4445f;
+  hp->b = -4.7750f;
+  hp->c = 2.0315f;
+  hp->scale_coeff = 0.2f;
+  hp->rownorm_eps = 1e-8f;
+  return MUON_OK;
+}
+
+const char* muon_status_string(muon_status s) {
+  switch (s) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_ARGUMENT: return "MUON_ERR_INVALID_ARGUMENT";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_WORKSPACE_TOO_SMALL: return "MUON_ERR_WORKSPACE_TOO_SMALL";
+    case MUON_ERR_HIP: return "MUON_ERR_HIP";
+  }
+  return "MUON_UNKNOWN_STATUS";
+}
+
+muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* workspace_bytes) {
+  if (!desc || !plan) return MUON_ERR_INVALID_ARGUMENT;
+  *plan = nullptr;
+  if (desc->num_matrices < 1 || !desc->rows || !desc->cols) return MUON_ERR_INVALID_ARGUMENT;
+  if (desc->num_matrices > (1ll << 24)) return MUON_ERR_UNSUPPORTED;
+  if (desc->grad_dtype != MUON_F32 && desc->grad_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
+  if (desc->ns_dtype != MUON_F32 && desc->ns_dtype != MUON_BF16) return MUON_ERR_INVALID_ARGUMENT;
+  if (desc->max_workspace_bytes < 0) return MUON_ERR_INVALID_ARGUMENT;
+  const int form = (int)desc->formulation;
+  if (form != MUON_FORM_AUTO && form != MUON_FORM_GRAM && form != MUON_FORM_DIRECT)
+    return MUON_ERR_INVALID_ARGUMENT;
+  if (form == MUON_FORM_DIRECT && desc->ns_dtype == MUON_F32) return MUON_ERR_UNSUPPORTED;
+  muon_status st = validate_hp(desc->hp);
+  if (st != MUON_OK) return st;
+  NsScales scales;
+  if (desc->ns_dtype == MUON_BF16) {
+    if (desc->hp.ns_steps > kMaxSteps16) return MUON_ERR_UNSUPPORTED;
+    st = ns_scales(desc->hp, &scales);
+    if (st != MUON_OK) return st;
+  }
+  for (int64_t i = 0; i < desc->num_matrices; ++i) {
+    const int64_t m = desc->rows[i], n = desc->cols[i];
+    if (m < 1 || n < 1) return MUON_ERR_INVALID_ARGUMENT;
+    if (m > kMaxDim || n > kMaxDim || std::min(m, n) > kMaxShort) return MUON_ERR_UNSUPPORTED;
+  }
+  st = validate_hints(desc);
+  if (st != MUON_OK) return st;
+  muon_plan_s* p = nullptr;
+  try {
+    p = new muon_plan_s();
+    p->nmat = desc->num_matrices;
+    p->grad_dtype = desc->grad_dtype;
+    p->ns_dtype = desc->ns_dtype;
+    p->hp = desc->hp;
+    p->scales = scales;
+    p->rows.assign(desc->rows, desc->rows + desc->num_matrices);
+    p->cols.assign(desc->cols, desc->cols + desc->num_matrices);
+    const bool f32path = desc->ns_dtype == MUON_F32;
+    p->formulation = form;
+    const int64_t cap = desc->max_workspace_bytes > 0 ? desc->max_workspace_bytes : kDefaultCap;
+
+    // buckets in order of first appearance
+    std::vector<std::vector<int>> members;
+    for (int64_t i = 0; i < p->nmat; ++i) {
+      size_t b = 0;
+      for (; b < p->buckets.size(); ++b)
+        if (p->buckets[b].m == p->rows[i] && p->buckets[b].n == p->cols[i]) break;
+      if (b == p->buckets.size()) {
+        Bucket nb{};
+        nb.m = p->rows[i];
+        nb.n = p->cols[i];
+        p->buckets.push_back(nb);
+        members.emplace_back();
+      }
+      members[b].push_back((int)i);
+    }
+    size_t part_floats = 0, colscale_floats = 0, max_scratch = 0;
+    for (size_t b = 0; b < p->buckets.size(); ++b) {
+      Bucket& B = p->buckets[b];
+      B.transposed = B.m > B.n;
+      B.r = std::min(B.m, B.n);
+      B.c = std::max(B.m, B.n);
+      // AUTO: the direct form for near-square matrices (c <= 1.125 r) on the
+      // 16-bit path, the Gram form otherwise (3 r^2 c + 17 r^3 against
+      // 15 r^2 c + 5 r^3 flops for c > r).  Near-square inputs have singular
+      // values close to zero, which the Gram form's squared spectrum resolves
+      // badly in fp16: measured over r = 40..1000 (worst of two seeds, both
+      // orientations) the Gram form's NS error is 1.1e-2..3.2e-2 on squares
+      // and 0.8e-2 at worst from c > 1.125 r on, the direct form's 0.25e-2..
+      // 0.64e-2 everywhere; on squares the two cost the same 20 r^3 flops
+      // and the direct form measured 2-10 % faster (3.6x on 64 x 512^2).
+      const bool near_square = 8 * B.c <= 9 * B.r;
+      B.direct = p->formulation == MUON_FORM_DIRECT ||
+                 (p->formulation == MUON_FORM_AUTO && !f32path && near_square);
+      const muon_bucket_hint* hint = find_hint(desc, B.m, B.n);
+      if (hint && hint->formulation != MUON_FORM_AUTO) B.direct = hint->formulation == MUON_FORM_DIRECT;
+      if (!f32path && !B.direct && near_square) {
+        // a Gram form forced onto a near-square bucket on the 16-bit path
+        // would miss the accuracy the path promises (see above)
+        delete p;
+        return MUON_ERR_UNSUPPORTED;
+      }
+      B.bt = B.direct ? 256 : choose_tile(B.r, (int64_t)members[b].size(), f32path);
+      if (hint && hint->tile != 0) {
+        if (B.direct && hint->tile != 256) {
+          delete p;
+          return MUON_ERR_UNSUPPORTED;
+        }
+        B.bt = hint->tile;
+      }
+      B.r_pad = round_up(B.r, B.bt);
+      B.c_pad = round_up(B.c, B.bt);
+      B.first = (int)p->order.size();
+      B.count = (int)members[b].size();
+      for (int i : members[b]) p->order.push_back(i);
+      const int64_t xes = f32path ? 4 : 2;
+      const int64_t rr = B.r_pad * B.r_pad;
+      B.dma = !f32path && B.bt == 256;
+      B.fused_rr = !f32path && !B.dma && !B.direct && B.r_pad <= 128;
+      // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
+      // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
+      // the 256-tile path keeps only the fp16 copies
+      const int64_t rr_bytes =
+          f32path ? 5 * (int64_t)align256((size_t)(rr * 4))
+                  : (B.dma ? 0 : 4 * (int64_t)align256((size_t)(rr * 4))) +
+                        5 * (int64_t)align256((size_t)(rr * 2));
+      const int64_t xb = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes));
+      // direct form: X and X^T twice (double buffered) plus A and P~ in fp16
+      B.scratch_per_mat = B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) : 2 * xb + rr_bytes;
+      int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
+      per_chunk = std::min<int64_t>(per_chunk, B.count);
+      const int64_t nchunks = (B.count + per_chunk - 1) / per_chunk;
+      const int64_t even = (B.count + nchunks - 1) / nchunks;
+      for (int64_t f = 0; f < B.count; f += even)
+        B.chunks.push_back(Chunk{B.first + (int)f, (int)std::min<int64_t>(even, B.count - f)});
+      B.m_pad = B.transposed ? B.c_pad : B.r_pad;
+      B.n_pad = B.transposed ? B.r_pad : B.c_pad;
+      B.prep_blocks = prep_blocks_per_mat((int)B.m_pad, (int)B.n_pad);
+      B.rn_row_blocks = rownorm_row_blocks((int)B.m, (int)B.n);
+      B.chunk_scratch = (size_t)(even * B.scratch_per_mat);
+      max_scratch = std::max(max_scratch, B.chunk_scratch);
+      part_floats = std::max(part_floats, (size_t)even * (size_t)B.prep_blocks);
+      if (B.transposed) {
+        // RowNorm runs on whole buckets (no NS scratch needed)
+        part_floats = std::max(part_floats, (size_t)B.count * B.rn_row_blocks * (size_t)B.n);
+        colscale_floats = std::max(colscale_floats, (size_t)B.count * (size_t)B.n);
+      }
+    }
+    // Buckets too small to fill the device on their own (one launch chunk,
+    // every r x r product under two waves of tiles for the 256 compute
+    // units) run concurrently on up to kMaxSlots streams when their scratch
+    // regions fit the cap together; otherwise all run one after another.
+    const int nb = (int)p->buckets.size();
+    bool small = nb > 1;
+    for (const Bucket& B : p->buckets) {
+      const int64_t T = B.r_pad / B.bt;
+      if (B.chunks.size() != 1 || (int64_t)B.count * (T * (T + 1) / 2) >= 512) small = false;
+    }
+    int S = small ? std::min(nb, kMaxSlots) : 1;
+    std::vector<size_t> slot_bytes((size_t)S, 0);
+    for (int b = 0; b < nb; ++b)
+      slot_bytes[(size_t)(b % S)] = std::max(slot_bytes[(size_t)(b % S)],
+                                             align256(p->buckets[(size_t)b].chunk_scratch));
+    size_t total = 0;
+    for (size_t v : slot_bytes) total += v;
+    if (S > 1 && total > (size_t)cap) {
+      S = 1;
+      slot_bytes.assign(1, max_scratch);
+      total = max_scratch;
+    }
+    auto layout = [&](const std::vector<size_t>& bytes) {
+      Layout L;
+      const int nsl = (int)bytes.size();
+      L.nslots = nsl;
+      L.slot_scratch_off.assign((size_t)nsl, 0);
+      size_t tot = 0;
+      for (size_t i = 0; i < bytes.size(); ++i) {
+        L.slot_scratch_off[i] = tot;
+        tot += bytes[i];
+      }
+      L.slot_part_floats = align256(sizeof(float) * std::max<size_t>(part_floats, 1)) / sizeof(float);
+      L.off_table = 0;
+      L.off_inv = align256(sizeof(MatPtrs) * (size_t)p->nmat);
+      L.off_part = L.off_inv + align256(sizeof(float) * (size_t)p->nmat);
+      L.off_colscale = L.off_part + sizeof(float) * L.slot_part_floats * (size_t)nsl;
+      L.off_scratch = L.off_colscale + align256(sizeof(float) * std::max<size_t>(colscale_floats, 1));
+      L.ws_bytes = L.off_scratch + tot;
+      return L;
+    };
+    p->lay = layout(slot_bytes);
+    p->serial = layout(std::vector<size_t>(1, max_scratch));
+    p->host_table.resize((size_t)p->nmat);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  *plan = p;
+  if (workspace_bytes) *workspace_bytes = p->lay.ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_destroy(muon_plan_t plan) {
+  if (!plan) return MUON_OK;
+  release_ring(plan);
+  release_profile(plan);
+  release_slots(plan);
+  delete plan;
+  return MUON_OK;
+}
+
+muon_status muon_plan_workspace_size(muon_plan_t plan, size_t* workspace_bytes) {
+  if (!plan || !workspace_bytes) return MUON_ERR_INVALID_ARGUMENT;
+  *workspace_bytes = plan->lay.ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_info(muon_plan_t plan, int64_t* num_buckets, int64_t* num_chunks) {
+  if (!plan) return MUON_ERR_INVALID_ARGUMENT;
+  int64_t nc = 0;
+  for (const auto& b : plan->buckets) nc += (int64_t)b.chunks.size();
+  if (num_buckets) *num_buckets = (int64_t)plan->buckets.size();
+  if (num_chunks) *num_chunks = nc;
+  return MUON_OK;
+}
+
+muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_info* info) {
+  if (!plan || !info || index < 0 || index >= (int64_t)plan->buckets.size())
+    return MUON_ERR_INVALID_ARGUMENT;
+  const Bucket& B = plan->buckets[(size_t)index];
+  info->rows = B.m;
+  info->cols = B.n;
+  info->count = B.count;
+  info->chunks = (int64_t)B.chunks.size();
+  info->tile = B.bt;
+  info->formulation = B.direct ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
+  info->transposed = B.transposed ? 1 : 0;
+  info->fused_recursion = B.fused_rr ? 1 : 0;
+  const NsScales& sc = plan->scales;
+  const float scales[5] = {sc.sG, sc.sP, sc.sH, sc.sQ, sc.sX};
+  std::memcpy(info->operand_scales, scales, sizeof scales);
+  return MUON_OK;
+}
+
+muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
+                              float lr, float wd, void* ws, size_t ws_bytes, hipStream_t stream,
+                              float* const* O_out) {
+  muon_status st = validate_call(p, W, M, G, lr, wd, ws, ws_bytes);
+  if (st != MUON_OK) return st;
+  try {
+    fill_table(p, W, M, G, O_out);
+  } catch (const std::bad_alloc&) {
+    return MUON_ERR_INVALID_ARGUMENT;
+  }
+  st = upload_table(p, ws, stream);
+  if (st != MUON_OK) return st;
+  p->prof_active = p->profiling;
+  return enqueue_refresh(p, p->lay, (char*)ws, lr, wd, stream);
+}
+
+muon_status muon_step_batched_noalloc(muon_plan_t p, float* const* W, float* const* M,
+                                      const void* const* G, float lr, float wd, hipStream_t stream,
+                                      float* const* O_out) {
+  muon_status st = validate_args(p, W, M, G, lr, wd);
+  if (st != MUON_OK) return st;
+  if (p->serial.ws_bytes > (size_t)MUON_NOALLOC_WORKSPACE_BYTES) return MUON_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != MUON_OK) return st;
+  fill_table(p, W, M, G, O_out);
+  // the pointer table reaches the scratch as kernel arguments: no staging
+  // buffer, and ordered on the stream like the rest of the step
+  MatPtrs* d_table = (MatPtrs*)(ws + p->serial.off_table);
+  for (int64_t k = 0; k < p->nmat; k += kTableChunk) {
+    TableChunk tc{};
+    tc.count = (int)std::min<int64_t>(kTableChunk, p->nmat - k);
+    for (int e = 0; e < tc.count; ++e) tc.e[e] = p->host_table[(size_t)(k + e)];
+    if (launch_write_table(tc, d_table + k, stream) != hipSuccess) return MUON_ERR_HIP;
+  }
+  p->prof_active = false;
+  return enqueue_refresh(p, p->serial, ws, lr, wd, stream);
+}
+
 muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
                          float lr, float wd, void* ws, size_t ws_bytes, hipStream_t stream,
                          float* const* R_out) {
@@ -1109,8 +1187,9 @@ muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const 
   }
   st = upload_table(p, ws, stream);
   if (st != MUON_OK) return st;
+  p->prof_active = p->profiling;
   char* wsb = (char*)ws;
-  const MatPtrs* d_table = (const MatPtrs*)(wsb + p->off_table);
+  const MatPtrs* d_table = (const MatPtrs*)(wsb + p->lay.off_table);
   const int gbf16 = p->grad_dtype == MUON_BF16 ? 1 : 0;
   for (const Bucket& B : p->buckets) {
     RowNormParams rp{};
@@ -1122,8 +1201,8 @@ muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const 
     rp.eps = p->hp.rownorm_eps;
     rp.decay = (float)(1.0 - (double)lr * wd);
     rp.step = (float)((double)lr * p->hp.scale_coeff * std::sqrt((double)B.c));
-    rp.partials = (float*)(wsb + p->off_part);
-    rp.colscale = (float*)(wsb + p->off_colscale);
+    rp.partials = (float*)(wsb + p->lay.off_part);
+    rp.colscale = (float*)(wsb + p->lay.off_colscale);
     rp.row_blocks = B.rn_row_blocks;
     const int vec = chunk_vec(p, B, Chunk{B.first, B.count});
     const double elems = (double)B.m * B.n * B.count;

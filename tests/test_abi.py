@@ -194,6 +194,21 @@ def test_step_validation_happens_before_device_work():
         assert call(fn, fake, fake, fake, wsb=p.workspace_bytes - 1) == L.MUON_ERR_WORKSPACE_TOO_SMALL
     assert lib.muon_step_batched(None, None, None, None, 0.0, 0.0, None, 0, None, None) == \
         L.MUON_ERR_INVALID_ARGUMENT
+    # the allocation-free step: argument checks, then the size of the plan's
+    # single-stream workspace against the library's scratch, before any HIP call
+    for kw in ({"lr": float("nan")}, {"G": [0x3000, 0]}):
+        args = dict(W=fake, M=fake, G=fake, lr=0.02)
+        args.update(kw)
+        with pytest.raises(L.MuonError) as e:
+            p.step_noalloc_ptrs(args["W"], args["M"], args["G"], args["lr"], 0.1)
+        assert e.value.status == L.MUON_ERR_INVALID_ARGUMENT
+    big = L.Plan([(4096, 4096)])
+    assert big.workspace_bytes > L.NOALLOC_WORKSPACE_BYTES
+    with pytest.raises(L.MuonError) as e:
+        big.step_noalloc_ptrs([0x1000], [0x2000], [0x3000], 0.02, 0.1)
+    assert e.value.status == L.MUON_ERR_WORKSPACE_TOO_SMALL
+    capped = L.Plan([(128, 3584)] * 200, max_workspace_bytes=L.NOALLOC_WORKSPACE_BYTES - (8 << 20))
+    assert capped.workspace_bytes <= L.NOALLOC_WORKSPACE_BYTES
     assert lib.muon_plan_destroy(None) == L.MUON_OK
 
 
