@@ -35,10 +35,13 @@
  *     priority, created on the first such call, destroyed with the plan):
  *     they wait for `stream` on entry and `stream` waits for all of them on
  *     return, so the call behaves as one operation on `stream`.  Each
- *     internal stream's launches are enqueued from its own short-lived host
- *     thread (with the caller's current device made current), joined before
- *     the call returns (one thread per call when the launch profiler is
- *     on).  The internal streams belong to the device that is current at
+ *     internal stream's launches are enqueued from its own host thread (the
+ *     calling thread for the first; the others are worker threads the plan
+ *     starts on its first such call and stops in muon_plan_destroy; each
+ *     makes the caller's current device current), and the call returns when
+ *     all have enqueued their launches (the calling thread enqueues every
+ *     stream when the launch profiler is on).  The internal streams belong
+ *     to the device that is current at
  *     that first call: later calls on the plan must keep the same device
  *     current, as the workspace and the matrices live there.
  *   - Errors: all validation happens on the host before anything is
@@ -85,8 +88,9 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
  *   MUON_FORM_DIRECT: eq. (2) on X itself, N times A = X X^T (SYRK),
  *                     P~ = b A + c A^2, X <- a X + P~ X.  15 r^2 c + 5 r^3
  *                     flops.  16-bit path only (ns_dtype MUON_BF16): X is
- *                     kept as scaled fp16 in both layouts; every product
- *                     uses 256-wide tiles.
+ *                     kept as scaled fp16 in both layouts; the products
+ *                     use the tile width of the planner's rule (64 or 128
+ *                     for small r, 256 above).
  *   MUON_FORM_AUTO:   per bucket: the direct form for near-square matrices
  *                     (c <= 1.125 r) on the 16-bit path, the Gram form
  *                     otherwise (fewer flops whenever c > r).
@@ -107,7 +111,7 @@ typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } mu
  *                256 = the 256-wide tile kernels (ns_dtype MUON_BF16 only).
  *   formulation: MUON_FORM_AUTO = the plan-wide setting decides; GRAM or
  *                DIRECT force the form for this bucket (DIRECT needs
- *                ns_dtype MUON_BF16 and a tile of 0 or 256).
+ *                ns_dtype MUON_BF16).
  * Hints whose shape matches no planned matrix are ignored.  Two hints for
  * the same shape, or a tile / formulation outside these values, give
  * MUON_ERR_INVALID_ARGUMENT; combinations the kernels do not provide give

@@ -8,6 +8,9 @@
 //   EPI_PH    G' = a H + P~ H   (so G' = P G P)
 //   EPI_FINAL O = Q X0 / ||U||, then W <- (1 - lr wd) W - lr s O
 //             ("Infra Optimizers" eq. (4); "Scaling Muon for DiT" 2.1)
+//   direct form (eq. (2) iterated on X, scaled fp16 X): EPI_SYRK on X,
+//   EPI_POLY, EPI_XUPD X' = a X + P~ X written in both layouts, EPI_XFINAL
+//   the last X' applied to W as EPI_FINAL does
 // Every r x r matrix of the recursion is a polynomial in G0, hence symmetric
 // and commuting, so each product needs only its lower-triangle tiles and
 // B^T == B for the K-contiguous operand layout.
@@ -188,17 +191,52 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
     }
     __syncthreads();
     const int gr0 = row0A + round * RR;
-    if constexpr (EPI == EPI_FINAL) {
+    if constexpr (EPI == EPI_FINAL || EPI == EPI_XFINAL) {
       // four consecutive columns per thread: one 16-byte W load and store
-      // (W is touched once; the fp32 tile row is read from LDS as scalars)
+      // (W is touched once; the fp32 tile row is read from LDS as scalars).
+      // XFINAL (the direct form's last X' = a X + P~ X, X and P~ scaled
+      // fp16): acc + a sP X^ is sP sX X', so O = (acc + a sP X^) / (sP sX)
       constexpr int TPR = BT / 4;        // threads per tile row
       constexpr int RPI = 256 / TPR;     // tile rows per iteration
+      const float inv = EPI == EPI_FINAL ? p.inv_norm[mat] : 1.0f / (p.sP * p.sX);
 #pragma unroll 4
       for (int e = 0; e < RR / RPI; ++e) {
         const int il = e * RPI + tid / TPR, jl = (tid % TPR) * 4;
         const float* sr = stile + il * EPI_LD + jl;
-        epilogue_final4(p, mat, gr0 + il, row0B + jl, make_float4(sr[0], sr[1], sr[2], sr[3]),
-                        p.inv_norm[mat]);
+        float4 acc4 = make_float4(sr[0], sr[1], sr[2], sr[3]);
+        if constexpr (EPI == EPI_XFINAL) {
+          const float4 x = ld4h(p.Xid, (size_t)mat * p.y_stride + (size_t)(gr0 + il) * p.ldyn + row0B + jl);
+          acc4 = f4_axpy(1.0f, acc4, p.a * p.sP, x);
+        }
+        epilogue_final4(p, mat, gr0 + il, row0B + jl, acc4, inv);
+      }
+    } else if constexpr (EPI == EPI_XUPD) {
+      // X'^ = a X^ + acc / sP in the scaled fp16 units of X^ (acc = sP sX P~ X):
+      // the row pass writes the natural layout Yn (X^ from Xid), the column
+      // pass the transposed Yt (X^ from the B operand, X^T), four
+      // consecutive elements per thread in both
+      const size_t yb = (size_t)mat * p.y_stride;
+      const float inv_sp = 1.0f / p.sP;
+      constexpr int TPR = BT / 4;     // threads per tile row
+      constexpr int RPI = 256 / TPR;  // tile rows per iteration
+#pragma unroll 2
+      for (int e = 0; e < RR / RPI; ++e) {
+        const int il = e * RPI + tid / TPR, jl = (tid % TPR) * 4;
+        const float* sr = stile + il * EPI_LD + jl;
+        const size_t o = yb + (size_t)(gr0 + il) * p.ldyn + row0B + jl;
+        const float4 v = f4_axpy(p.a, ld4h(p.Xid, o), inv_sp, make_float4(sr[0], sr[1], sr[2], sr[3]));
+        st4h(p.Yn, o, v, 1.0f, false, 0, 4);
+      }
+      constexpr int TPC = RR / 4;     // threads per tile column
+      constexpr int CPI = 256 / TPC;  // tile columns per iteration
+#pragma unroll 2
+      for (int e = 0; e < BT / CPI; ++e) {
+        const int il = (tid % TPC) * 4, jl = e * CPI + tid / TPC;
+        const float* sc = stile + il * EPI_LD + jl;
+        const size_t o = yb + (size_t)(row0B + jl) * p.ldyt + gr0 + il;
+        const float4 xt = ld4h(p.B, (size_t)mat * p.b_stride + (size_t)(row0B + jl) * p.ldb + gr0 + il);
+        const float4 v = f4_axpy(p.a, xt, inv_sp, make_float4(sc[0], sc[EPI_LD], sc[2 * EPI_LD], sc[3 * EPI_LD]));
+        st4h(p.Yt, o, v, 1.0f, false, 0, 4);
       }
     } else {
       // row pass (lower triangle incl. the diagonal): four consecutive
@@ -252,6 +290,17 @@ template <int BT, bool F32PATH>
 static hipError_t launch_bt(const GemmParams& p, int epi, int nmat, hipStream_t s) {
   constexpr int KX = F32PATH ? K_F32 : K_BF16;  // X0 / final operands
   constexpr int KR = F32PATH ? K_F32 : K_F16;   // r x r recursion operands
+  if constexpr (!F32PATH) {
+    // direct form: scaled fp16 X in every product
+    switch (epi) {
+      case EPI_SYRK:
+        if (p.xkind) return launch_one<K_F16, BT, EPI_SYRK, false>(p, nmat, s);
+        break;
+      case EPI_XUPD: return launch_one<K_F16, BT, EPI_XUPD, false>(p, nmat, s);
+      case EPI_XFINAL: return launch_one<K_F16, BT, EPI_XFINAL, false>(p, nmat, s);
+      default: break;
+    }
+  }
   switch (epi) {
     case EPI_SYRK: return launch_one<KX, BT, EPI_SYRK, F32PATH>(p, nmat, s);
     case EPI_POLY: return launch_one<KR, BT, EPI_POLY, F32PATH>(p, nmat, s);

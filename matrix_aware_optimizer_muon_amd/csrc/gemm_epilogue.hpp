@@ -55,13 +55,17 @@ __device__ __forceinline__ void st4h(void* base, size_t o, float4 v, float scale
 template <int EPI, bool F32PATH>
 __device__ __forceinline__ void epilogue4(const GemmParams& p, int mat, int prod, int row, int col0,
                                           float4 acc, int klo, int khi) {
-  static_assert(EPI != EPI_FINAL, "the final product uses epilogue_final4");
+  static_assert(EPI != EPI_FINAL && EPI != EPI_XUPD && EPI != EPI_XFINAL,
+                "the final and X' products have their own epilogues");
   const size_t o1 = (size_t)mat * p.rr_stride + (size_t)row * p.ldr + col0;
   auto scale4 = [](float4 a, float s) { return make_float4(a.x * s, a.y * s, a.z * s, a.w * s); };
   float4 v;
   if constexpr (EPI == EPI_SYRK) {
+    // Gram form: G0 = acc / ||U||^2; direct form (fp16 X scaled by sX):
+    // A = acc * syrk_scale
     const float inv = p.inv_norm[mat];
-    v = make_float4(acc.x * inv * inv, acc.y * inv * inv, acc.z * inv * inv, acc.w * inv * inv);
+    const float sc = p.syrk_scale > 0.0f ? p.syrk_scale : inv * inv;
+    v = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
     st4f(p.Gf, o1, v, klo, khi);
     if constexpr (!F32PATH) st4h(p.Gh, o1, v, p.sG, false, klo, khi);
     return;
@@ -139,6 +143,13 @@ template <int EPI>
 __device__ __forceinline__ float rr_gamma(const GemmParams& p) {
   if constexpr (EPI == EPI_POLY) return p.b * p.sG / p.c;
   else return p.a * p.sP;
+}
+
+// Four fp16 values (scaled X of the direct form) as floats.
+__device__ __forceinline__ float4 ld4h(const void* base, size_t o) {
+  const uint2 u = *(const uint2*)((const uint16_t*)base + o);
+  const _Float16* h = (const _Float16*)&u;
+  return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
 }
 
 // Final product: O = inv * acc (inv = 1/||U||, or the direct form's 1/(sP sX)),

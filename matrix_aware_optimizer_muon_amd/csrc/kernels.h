@@ -67,6 +67,8 @@ struct GemmParams {
   void* Yt;                // EPI_XUPD: X' transposed (c_pad x r_pad, ld ldyt)
   int ldyn, ldyt;
   int64_t y_stride;        // elements between matrices (both)
+  const void* Xid;         // small-tile EPI_XUPD / EPI_XFINAL: X in the layout
+                           // of Yn (ld ldyn, stride y_stride), for the a X term
 };
 
 hipError_t launch_gemm(const GemmParams& p, int epi, int op, int bt, int nmat, hipStream_t s);

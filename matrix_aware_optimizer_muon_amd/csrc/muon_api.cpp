@@ -24,6 +24,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <condition_variable>
+#include <functional>
 #include <mutex>
 #include <new>
 #include <thread>
@@ -153,6 +155,22 @@ struct Slot {
   bool used = false;
 };
 
+// Host threads that enqueue the launch sequences of concurrent buckets:
+// worker w runs slot w + 1 of each job (the calling thread runs slot 0).
+// Created on the first concurrent call and kept until the plan is destroyed,
+// so a call costs a hand-off instead of a thread start and join per slot.
+struct WorkerPool {
+  std::vector<std::thread> threads;
+  std::mutex mu;
+  std::condition_variable go, done;
+  uint64_t gen = 0;  // job number; workers run each new one once
+  int pending = 0;   // workers still running the current job
+  bool stop = false;
+  int device = 0;
+  std::function<muon_status(int)> job;
+  std::vector<muon_status> status;  // per slot
+};
+
 // Byte offsets of the workspace parts.  Concurrent buckets: bucket b runs on
 // slot b % nslots, each slot with its own stream, scratch region and
 // partial-sum region; nslots == 1: every bucket on the caller's stream.
@@ -189,6 +207,7 @@ struct muon_plan_s {
   Layout lay, serial;
   std::vector<hipStream_t> slot_streams;
   std::vector<hipEvent_t> slot_done;
+  WorkerPool pool;
   hipEvent_t fork_ev = nullptr;
   // descriptor staging
   Slot ring[kRing];
@@ -400,6 +419,84 @@ void release_slots(muon_plan_s* p) {
   p->fork_ev = nullptr;
 }
 
+void stop_pool(WorkerPool& w) {
+  {
+    std::lock_guard<std::mutex> lock(w.mu);
+    w.stop = true;
+  }
+  w.go.notify_all();
+  for (std::thread& t : w.threads) t.join();
+  w.threads.clear();
+  w.stop = false;
+}
+
+void worker_main(WorkerPool* w, int slot) {
+  uint64_t seen = 0;
+  int cur_dev = -1;
+  for (;;) {
+    std::function<muon_status(int)> job;
+    int dev;
+    {
+      std::unique_lock<std::mutex> lock(w->mu);
+      w->go.wait(lock, [&] { return w->stop || w->gen != seen; });
+      if (w->stop) return;
+      seen = w->gen;
+      job = w->job;
+      dev = w->device;
+    }
+    // a new host thread starts on device 0: make the caller's device current
+    muon_status st = MUON_OK;
+    if (dev != cur_dev) {
+      if (hipSetDevice(dev) == hipSuccess) cur_dev = dev;
+      else st = MUON_ERR_HIP;
+    }
+    if (st == MUON_OK) st = job(slot);
+    {
+      std::lock_guard<std::mutex> lock(w->mu);
+      w->status[(size_t)slot] = st;
+      if (--w->pending == 0) w->done.notify_all();
+    }
+  }
+}
+
+// Run job(slot) for slots 0..S-1: slots 1.. on the pool's workers (started
+// here on first use), slot 0 on the calling thread.  Falls back to the
+// calling thread for every slot if the workers cannot be started.
+muon_status run_slots(WorkerPool& w, int S, int device, const std::function<muon_status(int)>& job) {
+  if ((int)w.threads.size() != S - 1) {
+    stop_pool(w);
+    try {
+      w.status.assign((size_t)S, MUON_OK);
+      for (int i = 1; i < S; ++i) w.threads.emplace_back(worker_main, &w, i);
+    } catch (...) {
+      stop_pool(w);
+    }
+  }
+  if ((int)w.threads.size() != S - 1) {
+    muon_status st = MUON_OK;
+    for (int i = 0; i < S; ++i) {
+      const muon_status v = job(i);
+      if (st == MUON_OK) st = v;
+    }
+    return st;
+  }
+  {
+    std::lock_guard<std::mutex> lock(w.mu);
+    w.job = job;
+    w.device = device;
+    w.pending = S - 1;
+    ++w.gen;
+  }
+  w.go.notify_all();
+  muon_status st = job(0);
+  std::unique_lock<std::mutex> lock(w.mu);
+  w.done.wait(lock, [&] { return w.pending == 0; });
+  for (int i = 1; i < S; ++i)
+    if (st == MUON_OK) st = w.status[(size_t)i];
+  w.job = nullptr;
+  return st;
+}
+
 // Internal streams (default priority) and their fork / join events.
 muon_status ensure_slots(muon_plan_s* p) {
   if ((int)p->slot_streams.size() == p->lay.nslots) return MUON_OK;
@@ -515,7 +612,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
         float* Gf = nullptr;
         float* Qf[2] = {nullptr, nullptr};
         float* Hf = nullptr;
-        if (!B.dma) {
+        if (!B.dma && !B.direct) {
           Gf = (float*)take(f32b);
           Qf[0] = (float*)take(f32b);
           Qf[1] = (float*)take(f32b);
@@ -532,6 +629,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
           Xt2 = take(xbytes);
           Gh = take(h16b);
           Ph = take(h16b);
+          if (!B.dma) Gf = (float*)take(f32b);
         } else if (f32path) {
           Gh = Gf;
           Ph = take(f32b);
@@ -642,7 +740,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
           g.syrk_scale = 1.0f / (p->scales.sX * p->scales.sX);
           g.sX = p->scales.sX;
           g.first = g.last = 0;
-          const int tm = (int)(B.r_pad / 256), tn = (int)(B.c_pad / 256);
+          const int tm = (int)(B.r_pad / B.bt), tn = (int)(B.c_pad / B.bt);
           for (int k = 0; k < N; ++k) {
             const int cur = k & 1, nx = cur ^ 1;
             void* Xk = B.transposed ? Xt[cur] : Xn[cur];    // r_pad x c_pad
@@ -685,6 +783,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
             xg.ldyn = (int)B.c_pad;
             xg.ldyt = (int)B.r_pad;
             xg.y_stride = x_stride;
+            xg.Xid = Xk;  // the small-tile epilogue's a X term
             xg.xcd_chunk = full_grid_xcd_chunk(xg.tiles_per_prod);
             if (k == N - 1 && !B.transposed) {
               // X_N's tiles are W's tiles: update W from the accumulators
@@ -847,29 +946,8 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
     // that every slot's first kernels reach the GPU at once instead of after
     // the whole sequence of the slots before it (~13 us of host time per
     // launch; one Qwen2.5-7B layer: 8.3 -> 7.9 ms per step).  The threads
-    // only read the plan and launch on distinct streams; all are joined here.
-    // A new host thread starts on device 0, so each first makes the
-    // caller's device current.
-    std::vector<muon_status> sts((size_t)S, MUON_OK);
-    std::vector<std::thread> th;
-    int next = 1;
-    try {
-      for (; next < S; ++next)
-        th.emplace_back([&, slot = next] {
-          sts[(size_t)slot] = hipSetDevice(dev) == hipSuccess ? run_buckets(slot) : MUON_ERR_HIP;
-        });
-    } catch (...) {
-      // no thread for slots next..S-1: they run on this thread below
-    }
-    sts[0] = run_buckets(0);
-    for (std::thread& t : th) t.join();
-    for (int slot = next; slot < S; ++slot) sts[(size_t)slot] = run_buckets(slot);
-    st = MUON_OK;
-    for (muon_status v : sts)
-      if (v != MUON_OK) {
-        st = v;
-        break;
-      }
+    // only read the plan and launch on distinct streams.
+    st = run_slots(p->pool, S, dev, run_buckets);
   } else {
     st = run_buckets(-1);
   }
@@ -995,14 +1073,10 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
         delete p;
         return MUON_ERR_UNSUPPORTED;
       }
-      B.bt = B.direct ? 256 : choose_tile(B.r, (int64_t)members[b].size(), f32path);
-      if (hint && hint->tile != 0) {
-        if (B.direct && hint->tile != 256) {
-          delete p;
-          return MUON_ERR_UNSUPPORTED;
-        }
-        B.bt = hint->tile;
-      }
+      // the direct form takes the same tile rule: 64- or 128-wide tiles (the
+      // small-tile kernel) for small r, 256-wide ones above
+      B.bt = choose_tile(B.r, (int64_t)members[b].size(), f32path);
+      if (hint && hint->tile != 0) B.bt = hint->tile;
       B.r_pad = round_up(B.r, B.bt);
       B.c_pad = round_up(B.c, B.bt);
       B.first = (int)p->order.size();
@@ -1021,7 +1095,10 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
                         5 * (int64_t)align256((size_t)(rr * 2));
       const int64_t xb = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes));
       // direct form: X and X^T twice (double buffered) plus A and P~ in fp16
-      B.scratch_per_mat = B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) : 2 * xb + rr_bytes;
+      // (and A in fp32 for the small-tile kernel's quintic epilogue)
+      B.scratch_per_mat = B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) +
+                                         (B.dma ? 0 : (int64_t)align256((size_t)(rr * 4)))
+                                   : 2 * xb + rr_bytes;
       int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
       per_chunk = std::min<int64_t>(per_chunk, B.count);
       const int64_t nchunks = (B.count + per_chunk - 1) / per_chunk;
@@ -1096,6 +1173,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
 
 muon_status muon_plan_destroy(muon_plan_t plan) {
   if (!plan) return MUON_OK;
+  stop_pool(plan->pool);
   release_ring(plan);
   release_profile(plan);
   release_slots(plan);

@@ -310,7 +310,7 @@ def test_bucket_hints_override_tile_and_formulation():
     assert (b[(3584, 18944)]["tile"], b[(3584, 18944)]["formulation"]) == (128, "gram")
     assert (b[(1024, 1280)]["tile"], b[(1024, 1280)]["formulation"]) == (256, "gram")
     assert (b[(384, 1000)]["tile"], b[(384, 1000)]["formulation"]) == (256, "gram")
-    assert (b[(700, 300)]["tile"], b[(700, 300)]["formulation"]) == (256, "direct")
+    assert (b[(700, 300)]["tile"], b[(700, 300)]["formulation"]) == (64, "direct")
     # a 128-wide tile on a 3584-row bucket keeps fp32 master copies: more workspace
     assert L.Plan([(3584, 18944)], hints={(3584, 18944): {"tile": 128}}).workspace_bytes > \
         L.Plan([(3584, 18944)]).workspace_bytes
@@ -352,10 +352,10 @@ def test_bucket_hints_validation():
     assert plan_status([(64, 64)], grad_dtype="f32", ns_dtype="f32", hints={(64, 64): {"tile": 256}}) == uns
     assert plan_status([(64, 64)], grad_dtype="f32", ns_dtype="f32",
                        hints={(64, 64): {"formulation": "direct"}}) == uns
-    assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128}}) == uns   # direct needs 256
+    assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128}}) == 0   # small-tile direct form
     assert plan_status([(512, 640)], hints={(512, 640): {"tile": 128, "formulation": "gram"}}) == 0
     assert plan_status([(512, 512)], hints={(512, 512): {"tile": 128, "formulation": "gram"}}) == uns
-    assert plan_status([(300, 700)], hints={(300, 700): {"tile": 64, "formulation": "direct"}}) == uns
+    assert plan_status([(300, 700)], hints={(300, 700): {"tile": 64, "formulation": "direct"}}) == 0
 
 
 def test_concurrent_bucket_layout_and_cap_fallback():

