@@ -112,14 +112,30 @@ typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } mu
  *   formulation: MUON_FORM_AUTO = the plan-wide setting decides; GRAM or
  *                DIRECT force the form for this bucket (DIRECT needs
  *                ns_dtype MUON_BF16).
+ * The remaining fields set how the 256-wide kernels walk and run their
+ * tiles (they need a 256-wide tile; 0 keeps the rule):
+ *   group:       tile rows per tile-order group, 1..64 (rule: 8 for full
+ *                grids, 4 for the lower-triangular grids of symmetric
+ *                products); consecutive tiles of a group share operand panels
+ *                in an XCD's L2.
+ *   xcd_chunk:   consecutive tiles per XCD run, applied to every launch of
+ *                the bucket: -1 = one contiguous range of the launch per XCD,
+ *                1..65536 = runs of that many (rule: max(64, tiles per matrix
+ *                / 8) for full grids, contiguous for triangular ones).
+ *   waves:       wave64s per workgroup of the SYRK and final-product
+ *                launches: 8 (rule; two per SIMD, 128 x 64 each) or 4 (one
+ *                per SIMD, 128 x 128 each).  The other products always use 8.
  * Hints whose shape matches no planned matrix are ignored.  Two hints for
- * the same shape, or a tile / formulation outside these values, give
+ * the same shape, or a value outside these ranges, give
  * MUON_ERR_INVALID_ARGUMENT; combinations the kernels do not provide give
  * MUON_ERR_UNSUPPORTED. */
 typedef struct {
   int64_t rows, cols;
   int tile;
   muon_formulation formulation;
+  int group;
+  int xcd_chunk;
+  int waves;
 } muon_bucket_hint;
 
 /* Hyper-parameters fixed at plan time.  muon_default_hparams fills the
@@ -199,6 +215,7 @@ typedef struct {
   float operand_scales[5];   /* fp16 operand scales of G, P~, H, Q and the
                                 direct form's X (plan-wide; all 1 on the fp32
                                 path); see muon_plan                         */
+  int group, xcd_chunk, waves; /* the bucket's hint values (0: the rule)     */
 } muon_bucket_info;
 
 /* Fill *info for one bucket.  MUON_ERR_INVALID_ARGUMENT for a NULL plan or

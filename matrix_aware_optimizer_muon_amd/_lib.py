@@ -49,14 +49,16 @@ class Hparams(ctypes.Structure):
 
 class BucketHint(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("tile", ctypes.c_int),
-                ("formulation", ctypes.c_int)]
+                ("formulation", ctypes.c_int), ("group", ctypes.c_int), ("xcd_chunk", ctypes.c_int),
+                ("waves", ctypes.c_int)]
 
 
 class BucketInfo(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("count", ctypes.c_int64),
                 ("chunks", ctypes.c_int64), ("tile", ctypes.c_int), ("formulation", ctypes.c_int),
                 ("transposed", ctypes.c_int), ("fused_recursion", ctypes.c_int),
-                ("operand_scales", ctypes.c_float * 5)]
+                ("operand_scales", ctypes.c_float * 5), ("group", ctypes.c_int),
+                ("xcd_chunk", ctypes.c_int), ("waves", ctypes.c_int)]
 
 
 class PlanDesc(ctypes.Structure):
@@ -136,8 +138,9 @@ class Plan:
 
     grad_dtype / ns_dtype are "f32" or "bf16"; formulation is "auto", "gram"
     or "direct" (or the muon_formulation value).  `hints` maps a shape (m, n)
-    to {"tile": 0|64|128|256, "formulation": "auto"|"gram"|"direct"}
-    (muon_bucket_hint)."""
+    to {"tile": 0|64|128|256, "formulation": "auto"|"gram"|"direct",
+    "group": 0..64, "xcd_chunk": -1..65536, "waves": 0|4|8} (muon_bucket_hint;
+    missing keys are 0, the planner's rule)."""
 
     def __init__(self, shapes: Sequence[tuple], grad_dtype: str = "f32", ns_dtype: str = "bf16",
                  hp: Optional[Hparams] = None, max_workspace_bytes: int = 0,
@@ -162,7 +165,9 @@ class Plan:
         for i, ((m, n), h) in enumerate(items):
             f = h.get("formulation", "auto")
             harr[i] = BucketHint(int(m), int(n), int(h.get("tile", 0)),
-                                 FORMULATIONS[f] if isinstance(f, str) else int(f))
+                                 FORMULATIONS[f] if isinstance(f, str) else int(f),
+                                 int(h.get("group", 0)), int(h.get("xcd_chunk", 0)),
+                                 int(h.get("waves", 0)))
         desc.hints = ctypes.cast(harr, ctypes.POINTER(BucketHint)) if items else None
         desc.num_hints = len(items)
         self.hp = desc.hp
@@ -195,7 +200,9 @@ class Plan:
                         "chunks": int(b.chunks), "tile": int(b.tile),
                         "formulation": names[int(b.formulation)], "transposed": bool(b.transposed),
                         "fused": bool(b.fused_recursion),
-                        "scales": tuple(float(x) for x in b.operand_scales)})
+                        "scales": tuple(float(x) for x in b.operand_scales),
+                        "group": int(b.group), "xcd_chunk": int(b.xcd_chunk),
+                        "waves": int(b.waves)})
         return out
 
     def _call(self, fn, name, W, M, G, lr, wd, workspace_ptr, workspace_bytes, stream, out):

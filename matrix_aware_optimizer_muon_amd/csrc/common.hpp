@@ -75,6 +75,48 @@ __host__ __device__ __forceinline__ uint32_t xcd_remap_chunked(uint32_t bid, uin
   return base + xcd_remap(bid - base, total - base);
 }
 
+// Tile traversal orders.  Consecutive tile ids run concurrently on one XCD
+// (after xcd_remap), so the order decides how many operand panels the ~32
+// tiles in flight there share through its L2.
+//
+// Full grid: groups of GH tile rows (8 by default), column by column inside a
+// group, so 32 consecutive tiles cover 8 rows x 4 columns (12 operand panels)
+// instead of one row x 32 columns (33 panels) as in row-major order.
+__host__ __device__ __forceinline__ void full_tile_grouped(int t, int tiles_m, int tiles_n, int GH, int* ti,
+                                                  int* tj) {
+  const int g = t / (GH * tiles_n);
+  const int u = t - g * GH * tiles_n;
+  const int h = GH < tiles_m - g * GH ? GH : tiles_m - g * GH;
+  *ti = g * GH + u % h;
+  *tj = u / h;
+}
+
+// Lower-triangular grid (T x T tiles, I >= J): super-rows of SH tile rows (4
+// by default), walked column by column; the diagonal block of a super-row
+// comes last.
+__host__ __device__ __forceinline__ void tri_tile_grouped(int t, int T, int SH, int* ti, int* tj) {
+  // tiles before super-row s: (SH s)(SH s + 1)/2
+  int s = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f) / SH;
+  while (s > 0 && (SH * s) * (SH * s + 1) / 2 > t) --s;
+  while ((SH * (s + 1)) * (SH * (s + 1) + 1) / 2 <= t && SH * (s + 1) < T) ++s;
+  int u = t - (SH * s) * (SH * s + 1) / 2;
+  const int h = SH < T - SH * s ? SH : T - SH * s;
+  const int r0 = SH * s;
+  if (u < h * r0) {
+    *tj = u / h;
+    *ti = r0 + u % h;
+    return;
+  }
+  u -= h * r0;
+  int d = 0;
+  while (u >= h - d) {
+    u -= h - d;
+    ++d;
+  }
+  *tj = r0 + d;
+  *ti = r0 + d + u;
+}
+
 // Streaming (non-temporal) 16-byte global access for data touched once per
 // step (M, G, W, the X0 copies): keeps it from displacing reusable lines.
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -6,8 +6,9 @@
 // Both operands are K-contiguous (the prep kernel writes X0 and X0^T).
 // 8 wave64 (two per SIMD) in 2 x 4, each owning 128 x 64 = 4 x 2 blocks of
 // 32x32x16 MFMAs (128 fp32 accumulators), so one wave's barrier, DMA-issue
-// and LDS waits overlap the other's MFMAs (a 4-wave 128 x 128 variant is
-// kept as a template option).  A stage holds 32 K elements of both 256-row
+// and LDS waits overlap the other's MFMAs (a 4-wave 128 x 128 variant serves
+// SYRK and the final product when a tuning hint asks for it).  A stage holds
+// 32 K elements of both 256-row
 // operand tiles (2 x 16 KB); every 1-KB DMA instruction lands lane L at LDS
 // offset 16*L of its block, so the 16-byte chunk swizzle is applied on the
 // global side.  Up to four stages
@@ -48,48 +49,6 @@ typedef const __attribute__((address_space(1))) void gbl_ptr_t;
 __device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 3)) & 3; }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Tile traversal orders.  Consecutive tile ids run concurrently on one XCD
-// (after xcd_remap), so the order decides how many operand panels the ~32
-// tiles in flight there share through its L2.
-//
-// Full grid: groups of GH tile rows, column by column inside a group, so 32
-// consecutive tiles cover 8 rows x 4 columns (12 operand panels) instead of
-// one row x 32 columns (33 panels) as in row-major order.
-__device__ __forceinline__ void full_tile_grouped(int t, int tiles_m, int tiles_n, int* ti, int* tj) {
-  constexpr int GH = 8;
-  const int g = t / (GH * tiles_n);
-  const int u = t - g * GH * tiles_n;
-  const int h = min(GH, tiles_m - g * GH);
-  *ti = g * GH + u % h;
-  *tj = u / h;
-}
-
-// Lower-triangular grid (T x T tiles, I >= J): super-rows of SH tile rows,
-// walked column by column; the diagonal block of a super-row comes last.
-__device__ __forceinline__ void tri_tile_grouped(int t, int T, int* ti, int* tj) {
-  constexpr int SH = 4;
-  // tiles before super-row s: (SH s)(SH s + 1)/2
-  int s = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f) / SH;
-  while (s > 0 && (SH * s) * (SH * s + 1) / 2 > t) --s;
-  while ((SH * (s + 1)) * (SH * (s + 1) + 1) / 2 <= t && SH * (s + 1) < T) ++s;
-  int u = t - (SH * s) * (SH * s + 1) / 2;
-  const int h = min(SH, T - SH * s);
-  const int r0 = SH * s;
-  if (u < h * r0) {
-    *tj = u / h;
-    *ti = r0 + u % h;
-    return;
-  }
-  u -= h * r0;
-  int d = 0;
-  while (u >= h - d) {
-    u -= h - d;
-    ++d;
-  }
-  *tj = r0 + d;
-  *ti = r0 + d + u;
-}
 
 template <int KIND>
 __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) {
@@ -202,8 +161,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   t -= pi * p.tiles_per_prod;
   const int prod = pi + p.prod_base;
   int ti, tj;
-  if (p.triangular) tri_tile_grouped(t, p.tiles_m, &ti, &tj);
-  else full_tile_grouped(t, p.tiles_m, p.tiles_n, &ti, &tj);
+  if (p.triangular) tri_tile_grouped(t, p.tiles_m, p.group > 0 ? p.group : 4, &ti, &tj);
+  else full_tile_grouped(t, p.tiles_m, p.tiles_n, p.group > 0 ? p.group : 8, &ti, &tj);
   const int row0A = ti * DT, row0B = tj * DT;
   const char* Ab = (const char*)p.A + (size_t)mat * p.a_stride * 2;
   const char* Bb = pi ? (const char*)p.B2 + (size_t)mat * p.b2_stride * 2
@@ -562,32 +521,35 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   }
 }
 
-#ifndef MUON_DMA_WAVES
-#define MUON_DMA_WAVES 8
-#endif
-
-template <int KIND, int EPI>
+template <int KIND, int EPI, int NW>
 static hipError_t launch_dma_one(const GemmParams& p, int nmat, hipStream_t s) {
   const uint64_t blocks = (uint64_t)nmat * p.tiles_per_prod * p.products;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   if (p.Kdim % DBK != 0 || p.Mdim % DT != 0 || p.Ndim % DT != 0) return hipErrorInvalidValue;
-  constexpr int NW = MUON_DMA_WAVES;
   hipLaunchKernelGGL((gemm_dma_kernel<KIND, EPI, NW>), dim3((uint32_t)blocks), dim3(64 * NW), 0, s,
                      p);
   return hipGetLastError();
 }
 
+// Eight waves (two per SIMD) everywhere; four (one per SIMD, 128 x 128 each,
+// 256 accumulators per lane) for the products without an identity term to
+// harvest (SYRK and the final product), where they fit the register file.
 hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s) {
+  const bool w4 = p.waves == 4;
+  if (p.waves != 0 && p.waves != 4 && p.waves != 8) return hipErrorInvalidValue;
+  if (w4 && epi != EPI_SYRK && epi != EPI_FINAL) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_SYRK:
-      return p.xkind ? launch_dma_one<1, EPI_SYRK>(p, nmat, s) : launch_dma_one<0, EPI_SYRK>(p, nmat, s);
-    case EPI_XUPD: return launch_dma_one<1, EPI_XUPD>(p, nmat, s);
-    case EPI_XFINAL: return launch_dma_one<1, EPI_XFINAL>(p, nmat, s);
-    case EPI_POLY: return launch_dma_one<1, EPI_POLY>(p, nmat, s);
-    case EPI_PQPG: return launch_dma_one<1, EPI_PQPG>(p, nmat, s);
-    case EPI_PH: return launch_dma_one<1, EPI_PH>(p, nmat, s);
-    case EPI_FINAL: return launch_dma_one<0, EPI_FINAL>(p, nmat, s);
+      if (p.xkind) return w4 ? launch_dma_one<1, EPI_SYRK, 4>(p, nmat, s) : launch_dma_one<1, EPI_SYRK, 8>(p, nmat, s);
+      return w4 ? launch_dma_one<0, EPI_SYRK, 4>(p, nmat, s) : launch_dma_one<0, EPI_SYRK, 8>(p, nmat, s);
+    case EPI_XUPD: return launch_dma_one<1, EPI_XUPD, 8>(p, nmat, s);
+    case EPI_XFINAL: return launch_dma_one<1, EPI_XFINAL, 8>(p, nmat, s);
+    case EPI_POLY: return launch_dma_one<1, EPI_POLY, 8>(p, nmat, s);
+    case EPI_PQPG: return launch_dma_one<1, EPI_PQPG, 8>(p, nmat, s);
+    case EPI_PH: return launch_dma_one<1, EPI_PH, 8>(p, nmat, s);
+    case EPI_FINAL:
+      return w4 ? launch_dma_one<0, EPI_FINAL, 4>(p, nmat, s) : launch_dma_one<0, EPI_FINAL, 8>(p, nmat, s);
   }
   return hipErrorInvalidValue;
 }

@@ -36,6 +36,9 @@ struct GemmParams {
   int products;            // 1 or 2
   int xcd_chunk;           // 0: each XCD takes one contiguous range of the
                            // launch's tiles; > 0: runs of this many (xcd_remap_chunked)
+  int group;               // 256-wide kernels: tile rows per tile-order group
+                           // (0: 8 for full grids, 4 for triangular ones)
+  int waves;               // 256-wide kernels: 8, or 4 (SYRK and the final product)
   int prod_base;           // epilogue product index of the first product
   // r x r recursion buffers (fp32 master copies and MFMA operand copies)
   float* Gf;

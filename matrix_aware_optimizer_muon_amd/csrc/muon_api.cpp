@@ -141,6 +141,7 @@ struct Bucket {
   bool direct;  // direct form (eq. (2) on X)
   bool fused_rr;  // Gram form with the whole r x r recursion in one launch
   int bt;
+  int group = 0, xcd = 0, waves = 0;  // 256-wide kernels' hint values (0: rule)
   int first, count;  // range in plan order
   std::vector<Chunk> chunks;
   int64_t scratch_per_mat;
@@ -536,6 +537,9 @@ muon_status validate_hints(const muon_plan_desc* desc) {
     const int f = (int)h.formulation;
     if (f != MUON_FORM_AUTO && f != MUON_FORM_GRAM && f != MUON_FORM_DIRECT)
       return MUON_ERR_INVALID_ARGUMENT;
+    if (h.group < 0 || h.group > 64) return MUON_ERR_INVALID_ARGUMENT;
+    if (h.xcd_chunk < -1 || h.xcd_chunk > 65536) return MUON_ERR_INVALID_ARGUMENT;
+    if (h.waves != 0 && h.waves != 4 && h.waves != 8) return MUON_ERR_INVALID_ARGUMENT;
     seen.emplace_back(h.rows, h.cols);
   }
   std::sort(seen.begin(), seen.end());
@@ -654,8 +658,12 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
         const float decay = (float)(1.0 - (double)lr * wd);
         const float step_c = (float)((double)lr * hp.scale_coeff * std::sqrt((double)B.c));
         auto gemm = [&](const GemmParams& gp, int epi) {
-          return B.dma ? launch_gemm_dma(gp, epi, nm, stream)
-                       : launch_gemm(gp, epi, op, B.bt, nm, stream);
+          if (!B.dma) return launch_gemm(gp, epi, op, B.bt, nm, stream);
+          GemmParams q = gp;
+          q.group = B.group;
+          if (B.xcd) q.xcd_chunk = B.xcd < 0 ? 0 : B.xcd;
+          q.waves = (epi == EPI_SYRK || epi == EPI_FINAL) ? B.waves : 0;
+          return launch_gemm_dma(q, epi, nm, stream);
         };
         // algorithmic work per matrix (true sizes; symmetric products on the
         // lower triangle): SYRK r^2 c, each r x r product r^3, final 2 r^2 c
@@ -1077,6 +1085,16 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       // small-tile kernel) for small r, 256-wide ones above
       B.bt = choose_tile(B.r, (int64_t)members[b].size(), f32path);
       if (hint && hint->tile != 0) B.bt = hint->tile;
+      if (hint) {
+        B.group = hint->group;
+        B.xcd = hint->xcd_chunk;
+        B.waves = hint->waves;
+        // the knobs of the 256-wide kernels need those kernels
+        if ((B.group || B.xcd || B.waves) && (f32path || B.bt != 256)) {
+          delete p;
+          return MUON_ERR_UNSUPPORTED;
+        }
+      }
       B.r_pad = round_up(B.r, B.bt);
       B.c_pad = round_up(B.c, B.bt);
       B.first = (int)p->order.size();
@@ -1211,6 +1229,9 @@ muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_i
   const NsScales& sc = plan->scales;
   const float scales[5] = {sc.sG, sc.sP, sc.sH, sc.sQ, sc.sX};
   std::memcpy(info->operand_scales, scales, sizeof scales);
+  info->group = B.group;
+  info->xcd_chunk = B.xcd;
+  info->waves = B.waves;
   return MUON_OK;
 }
 

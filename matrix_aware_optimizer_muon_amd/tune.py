@@ -21,15 +21,19 @@ This module does both for this library's kernels:
   recorded but never chosen, so a fast but inaccurate setting cannot reach
   the cache's winners;
 * ``tune`` times every candidate of every (shape, count) not yet in the
-  cache, keeps the fastest accurate one, and stores all timings (the
-  per-shape cost profile) in a JSON cache keyed by device, dtypes, shape and
-  count;
+  cache, keeps the fastest accurate one, then, when that one runs on the
+  256-wide kernels, searches their knobs one at a time from it (tile-order
+  group height, XCD run length, four waves per workgroup for SYRK and the
+  final product: ``KNOBS``), keeping a change only when it is faster by more
+  than ``KNOB_GAIN``, and stores all timings (the per-shape cost profile) in
+  a JSON cache keyed by device, dtypes, shape and count;
 * ``hints_for`` turns cached winners into ``Plan(hints=...)``.
 
 The cache file is plain JSON: ``{"version": 2, "entries": {key: entry}}``
-with ``entry = {"tile", "formulation", "ms", "default", "candidates":
-[{"tile", "formulation", "ms", "err"}...]}``.  Timing needs a GPU; the cache
-logic does not.
+with ``entry = {"tile", "formulation", "group", "xcd_chunk", "waves", "ms",
+"default", "candidates": [{"tile", "formulation", ..., "ms", "err"}...]}``
+(knob fields absent or 0: the planner's rule).  Timing needs a GPU; the
+cache logic does not.
 """
 from __future__ import annotations
 
@@ -43,6 +47,14 @@ CACHE_VERSION = 2
 # fp32 path's that the tuner accepts: half the 16-bit path's 2e-2 bound (the
 # sample is one matrix and one seed), and the fp32 path's own 1e-4 bound.
 ACCURACY_TOL = {"bf16": 1e-2, "f32": 1e-4}
+# Knobs of the 256-wide kernels (muon_bucket_hint) and the values tried for
+# each, one knob at a time from the best tile / form: tile-order group height
+# (rule: 8 rows for full grids, 4 for triangular ones), XCD run length (-1:
+# one contiguous range per XCD), wave64s per workgroup of SYRK and the final
+# product.
+KNOBS = (("group", (2, 4, 16)), ("xcd_chunk", (-1, 32, 256)), ("waves", (4,)))
+KNOB_GAIN = 0.01   # a knob value must beat the current best by more than 1 %
+HINT_FIELDS = ("tile", "formulation", "group", "xcd_chunk", "waves")
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # Winners measured on the device this package targets, shipped with it.
 SHIPPED_CACHE = os.path.join(_HERE, "tuned", "mi355x.json")
@@ -232,24 +244,41 @@ def tune(shapes: Sequence[Sequence[int]], grad_dtype: str, ns_dtype: str,
                 return out if isinstance(out, tuple) else (out, None)
         default_ms, _ = measure(None)
         rows = []
-        for h in candidates(m, n, ns_dtype):
+
+        def trial(h):
             ms, err = measure(h)
-            row = {"tile": h["tile"], "formulation": h["formulation"], "ms": round(ms, 4),
-                   "err": None if err is None else float(f"{err:.3e}")}
+            row = dict(h)
+            row["ms"] = round(ms, 4)
+            row["err"] = None if err is None else float(f"{err:.3e}")
             if err is not None and not err <= tol:
                 row["rejected"] = True
             rows.append(row)
             if log:
                 e = "-" if err is None else f"{err:.2e}"
-                log(f"{m}x{n} x{count}: tile {h['tile']:3d} {h['formulation']:6s} {ms:9.3f} ms "
-                    f"err {e}{' (rejected)' if row.get('rejected') else ''}")
+                knobs = " ".join(f"{k}={h[k]}" for k, _ in KNOBS if h.get(k))
+                log(f"{m}x{n} x{count}: tile {h['tile']:3d} {h['formulation']:6s} {knobs} "
+                    f"{ms:9.3f} ms err {e}{' (rejected)' if row.get('rejected') else ''}")
+            return row
+
+        for h in candidates(m, n, ns_dtype):
+            trial(h)
         ok = [e for e in rows if not e.get("rejected")]
         if not ok:
             raise RuntimeError(f"no setting of {m}x{n} x{count} meets the accuracy bound {tol}")
         best = min(ok, key=lambda e: e["ms"])
-        cache["entries"][key] = {"tile": best["tile"], "formulation": best["formulation"],
-                                 "ms": best["ms"], "default": round(default_ms, 4),
-                                 "candidates": rows}
+        if best["tile"] == 256:
+            for knob, values in KNOBS:
+                for v in values:
+                    h = {k: best[k] for k in HINT_FIELDS if k in best}
+                    h[knob] = v
+                    if not _plannable(m, n, ns_dtype, h):
+                        continue
+                    row = trial(h)
+                    if not row.get("rejected") and row["ms"] < best["ms"] * (1.0 - KNOB_GAIN):
+                        best = row
+        entry = {k: best[k] for k in HINT_FIELDS if k in best}
+        entry.update({"ms": best["ms"], "default": round(default_ms, 4), "candidates": rows})
+        cache["entries"][key] = entry
     return cache
 
 
@@ -263,7 +292,8 @@ def hints_for(shapes: Sequence[Sequence[int]], grad_dtype: str, ns_dtype: str, c
     for (m, n), count in shape_counts(shapes).items():
         e = cache.get("entries", {}).get(cache_key(device, grad_dtype, ns_dtype, m, n, count))
         if e:
-            hints[(m, n)] = {"tile": int(e["tile"]), "formulation": e["formulation"]}
+            hints[(m, n)] = {k: (e[k] if k == "formulation" else int(e[k]))
+                             for k in HINT_FIELDS if k in e}
     return hints
 
 
@@ -289,7 +319,8 @@ def main(argv=None):
     save_cache(path, cache)
     for (m, n), count in shape_counts(w.shapes).items():
         e = cache["entries"][cache_key(dev, w.grad_dtype, w.ns_dtype, m, n, count)]
-        print(f"{m}x{n} x{count}: best tile {e['tile']} {e['formulation']} {e['ms']:.3f} ms "
+        knobs = " ".join(f"{k}={e[k]}" for k, _ in KNOBS if e.get(k))
+        print(f"{m}x{n} x{count}: best tile {e['tile']} {e['formulation']} {knobs} {e['ms']:.3f} ms "
               f"(planner rule {e['default']:.3f} ms)")
 
 

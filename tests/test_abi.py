@@ -369,3 +369,22 @@ def test_concurrent_bucket_layout_and_cap_fallback():
     # a bucket that fills the device keeps every bucket on the caller's stream
     big = small + [(3584, 3584)] * 8
     assert L.Plan(big).workspace_bytes <= L.Plan([(3584, 3584)] * 8).workspace_bytes + (1 << 20)
+
+
+def test_kernel_knob_hints():
+    # tile-order group, XCD run length and wave count of the 256-wide kernels
+    shape = (3584, 18944)
+    b = L.Plan([shape], grad_dtype="bf16",
+               hints={shape: {"group": 16, "xcd_chunk": -1, "waves": 4}}).buckets()[0]
+    assert (b["tile"], b["group"], b["xcd_chunk"], b["waves"]) == (256, 16, -1, 4)
+    b = L.Plan([shape]).buckets()[0]
+    assert (b["group"], b["xcd_chunk"], b["waves"]) == (0, 0, 0)
+    bad, uns = L.MUON_ERR_INVALID_ARGUMENT, L.MUON_ERR_UNSUPPORTED
+    for h in ({"group": -1}, {"group": 65}, {"xcd_chunk": -2}, {"xcd_chunk": 65537}, {"waves": 6},
+              {"waves": 2}):
+        assert plan_status([shape], hints={shape: h}) == bad, h
+    # the knobs need the 256-wide kernels
+    assert plan_status([shape], hints={shape: {"tile": 128, "group": 4}}) == uns
+    assert plan_status([(300, 900)], hints={(300, 900): {"waves": 4}}) == uns  # small tiles by rule
+    assert plan_status([shape], grad_dtype="f32", ns_dtype="f32", hints={shape: {"xcd_chunk": 64}}) == uns
+    assert plan_status([(4096, 4096)], hints={(4096, 4096): {"group": 2, "waves": 8}}) == 0

@@ -1,6 +1,8 @@
 """Host-side check of the workgroup -> tile maps of the GEMM kernels
 (csrc/common.hpp): every tile of a launch is taken by exactly one workgroup,
-and the chunked map keeps the promised locality.  The header is compiled
+the chunked map keeps the promised locality, and the grouped tile orders of
+the 256-wide kernels visit every tile of a full grid or lower triangle once
+for every group height a tuning hint may set.  The header is compiled
 into a small host program with hipcc (no GPU needed)."""
 import os
 import shutil
@@ -12,6 +14,7 @@ CSRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "matrix_aware_op
                     "csrc")
 
 PROGRAM = r"""
+#include <cmath>
 #include <cstdio>
 #include <vector>
 #include "common.hpp"
@@ -41,6 +44,34 @@ int main() {
         }
       }
     }
+  // tile-order maps of the 256-wide kernels, every group height a hint may
+  // set: each (row, column) tile of a full grid / lower triangle once
+  for (int G = 1; G <= 64; ++G) {
+    for (int tm : {1, 2, 3, 7, 14, 16, 74}) {
+      for (int tn : {1, 3, 14, 74}) {
+        std::vector<int> seen(tm * tn, 0);
+        for (int t = 0; t < tm * tn; ++t) {
+          int i, j;
+          full_tile_grouped(t, tm, tn, G, &i, &j);
+          if (i < 0 || i >= tm || j < 0 || j >= tn) { printf("full out of range G=%d\n", G); return 1; }
+          ++seen[i * tn + j];
+        }
+        for (int v : seen) if (v != 1) { printf("full not a bijection G=%d %dx%d\n", G, tm, tn); return 1; }
+      }
+    }
+    for (int T : {1, 2, 3, 4, 5, 14, 16, 17, 64}) {
+      std::vector<int> seen(T * T, 0);
+      for (int t = 0; t < T * (T + 1) / 2; ++t) {
+        int i, j;
+        tri_tile_grouped(t, T, G, &i, &j);
+        if (j < 0 || i < j || i >= T) { printf("tri out of range G=%d T=%d t=%d\n", G, T, t); return 1; }
+        ++seen[i * T + j];
+      }
+      for (int i = 0; i < T; ++i)
+        for (int j = 0; j <= i; ++j)
+          if (seen[i * T + j] != 1) { printf("tri not a bijection G=%d T=%d\n", G, T); return 1; }
+    }
+  }
   printf("ok\n");
   return 0;
 }

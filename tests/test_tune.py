@@ -108,4 +108,36 @@ def test_shipped_cache_entries_are_plannable():
         b = L.Plan([(m, n)] * count, g[2:], ns[3:],
                    hints={(m, n): {"tile": e["tile"], "formulation": e["formulation"]}}).buckets()[0]
         assert (b["tile"], b["formulation"]) == (e["tile"], e["formulation"]), key
-        assert e["ms"] == min(c["ms"] for c in e["candidates"]), key
+        assert e["ms"] == min(c["ms"] for c in e["candidates"] if not c.get("rejected")) or \
+            any(c.get(k) for c in e["candidates"] for k, _ in TU.KNOBS), key
+
+
+def test_knob_search_on_the_256_wide_kernels():
+    # the fastest tile / form runs on the 256-wide kernels: each knob value is
+    # tried from it, one knob at a time, and kept only when >1 % faster
+    base = {(128, "gram"): 10.0, (256, "gram"): 8.0, (256, "direct"): 20.0}
+    knob = {("group", 2): 8.5, ("group", 4): 7.0, ("group", 16): 7.95, ("xcd_chunk", -1): 6.0,
+            ("xcd_chunk", 32): 6.99, ("xcd_chunk", 256): 7.5, ("waves", 4): 5.96}
+    seen = []
+
+    def timer(m, n, count, h):
+        if h is None:
+            return 9.0, 1e-3
+        seen.append(dict(h))
+        k = [(f, h[f]) for f, _ in TU.KNOBS if h.get(f)]
+        if not k:
+            return base[(h["tile"], h["formulation"])], 1e-3
+        return knob[k[-1]], 1e-3
+
+    cache = TU.tune([(3584, 18944)], "bf16", "bf16", device=DEV, timer=timer)
+    e = cache["entries"][TU.cache_key(DEV, "bf16", "bf16", 3584, 18944, 1)]
+    # group 4 (7.0) beats 8.0; xcd_chunk -1 (6.0) beats 7.0; waves 4 (5.96) is
+    # within 1 % of 6.0 and is not taken
+    assert (e["tile"], e["group"], e["xcd_chunk"], e.get("waves", 0), e["ms"]) == (256, 4, -1, 0, 6.0)
+    hints = TU.hints_for([(3584, 18944)], "bf16", "bf16", cache, device=DEV)
+    assert hints == {(3584, 18944): {"tile": 256, "formulation": "gram", "group": 4, "xcd_chunk": -1}}
+    L.Plan([(3584, 18944)], "bf16", "bf16", hints=hints)
+    # no knob is tried on a small-tile winner
+    seen.clear()
+    TU.tune([(128, 3584)], "bf16", "bf16", device=DEV,
+            timer=lambda m, n, c, h: (1.0 if h and h["tile"] == 64 else 2.0, 1e-3))
