@@ -120,8 +120,7 @@ typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } mu
  *                in an XCD's L2.
  *   xcd_chunk:   consecutive tiles per XCD run, applied to every launch of
  *                the bucket: -1 = one contiguous range of the launch per XCD,
- *                1..65536 = runs of that many (rule: max(64, tiles per matrix
- *                / 8) for full grids, contiguous for triangular ones).
+ *                1..65536 = runs of that many (rule: 32).
  *   waves:       wave64s per workgroup of the SYRK and final-product
  *                launches: 8 (rule; two per SIMD, 128 x 64 each) or 4 (one
  *                per SIMD, 128 x 128 each).  The other products always use 8.

@@ -40,14 +40,16 @@ namespace {
 
 constexpr int64_t kDefaultCap = 32ll << 30;   // Newton-Schulz scratch cap (bytes)
 
-// Tile runs per XCD for the full-grid 256-tile products (final product,
-// XUPD): at least 64 tiles per run (an XCD's 32 resident workgroups then
-// take consecutive tiles) and about one matrix per window of 8 runs, so the
-// eight XCDs read the operands of one or two matrices at a time.
-// Measured (same-box A/B against one contiguous range per XCD): final
-// product +2 % and XUPD +4 % on the Qwen2.5-7B set, XUPD +3.5 % and the
-// final product -1 % at DiT shapes; 1.3-1.4 % per refresh step on both.
-int full_grid_xcd_chunk(int tiles_per_mat) { return std::max(64, (tiles_per_mat + 7) / 8); }
+// Tile runs per XCD for every launch of the 256-wide kernels (the hardware
+// sends workgroup w to XCD w mod 8; xcd_remap_chunked gives XCD x the tiles
+// [8Ck + xC, +C) of its k-th run): with runs of 32, all eight XCDs work in
+// one window of 256 consecutive tiles (two to three matrices of the r x r
+// products, a quarter of a final product) whose operands the shared
+// last-level cache holds, while each XCD's 32 resident workgroups take
+// consecutive tiles.  Found by the tuner and confirmed in same-box runs
+// against the earlier rule (one contiguous range per XCD for triangular
+// grids, runs of max(64, tiles per matrix / 8) for full grids).
+constexpr int kXcdRun = 32;
 constexpr int kMaxSlots = 4;                   // internal streams for concurrent buckets
 constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
 constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
@@ -661,7 +663,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
           if (!B.dma) return launch_gemm(gp, epi, op, B.bt, nm, stream);
           GemmParams q = gp;
           q.group = B.group;
-          if (B.xcd) q.xcd_chunk = B.xcd < 0 ? 0 : B.xcd;
+          q.xcd_chunk = B.xcd == 0 ? kXcdRun : (B.xcd < 0 ? 0 : B.xcd);
           q.waves = (epi == EPI_SYRK || epi == EPI_FINAL) ? B.waves : 0;
           return launch_gemm_dma(q, epi, nm, stream);
         };
@@ -792,7 +794,6 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
             xg.ldyt = (int)B.r_pad;
             xg.y_stride = x_stride;
             xg.Xid = Xk;  // the small-tile epilogue's a X term
-            xg.xcd_chunk = full_grid_xcd_chunk(xg.tiles_per_prod);
             if (k == N - 1 && !B.transposed) {
               // X_N's tiles are W's tiles: update W from the accumulators
               // (W <- decay W - step X_N, X_N also to O_out) instead of
@@ -940,7 +941,6 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
         fg.tiles_m = fg.Mdim / B.bt;
         fg.tiles_n = fg.Ndim / B.bt;
         fg.tiles_per_prod = fg.tiles_m * fg.tiles_n;
-        if (B.dma) fg.xcd_chunk = full_grid_xcd_chunk(fg.tiles_per_prod);
         st = timed(p, stream, MUON_K_FINAL, 2.0 * r2 * cc * nm, (xes * rcf + op_b * r2 + 8.0 * rcf) * nm,
                    [&] { return gemm(fg, EPI_FINAL); });
         if (st != MUON_OK) return st;

@@ -49,10 +49,10 @@ CACHE_VERSION = 2
 ACCURACY_TOL = {"bf16": 1e-2, "f32": 1e-4}
 # Knobs of the 256-wide kernels (muon_bucket_hint) and the values tried for
 # each, one knob at a time from the best tile / form: tile-order group height
-# (rule: 8 rows for full grids, 4 for triangular ones), XCD run length (-1:
-# one contiguous range per XCD), wave64s per workgroup of SYRK and the final
-# product.
-KNOBS = (("group", (2, 4, 16)), ("xcd_chunk", (-1, 32, 256)), ("waves", (4,)))
+# (rule: 8 rows for full grids, 4 for triangular ones), XCD run length (rule:
+# 32; -1: one contiguous range per XCD), wave64s per workgroup of SYRK and
+# the final product (rule: 8).
+KNOBS = (("group", (2, 4, 16)), ("xcd_chunk", (-1, 16, 64, 256)), ("waves", (4,)))
 KNOB_GAIN = 0.01   # a knob value must beat the current best by more than 1 %
 HINT_FIELDS = ("tile", "formulation", "group", "xcd_chunk", "waves")
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -109,9 +109,9 @@ def save_cache(path: str, data: dict) -> None:
 
 def candidates(m: int, n: int, ns_dtype: str) -> list:
     """The settings the kernels provide for an m x n bucket.  fp32 path:
-    Gram form with 64- or 128-wide tiles.  16-bit path: Gram form with 64-
-    (r <= 1024), 128- or 256-wide tiles, and the direct form (256-wide);
-    settings the planner refuses for this shape are left out."""
+    Gram form with 64- or 128-wide tiles.  16-bit path: Gram and direct form
+    with 64- and 128-wide (r <= 1024) and 256-wide tiles; settings the
+    planner refuses for this shape are left out."""
     r = min(m, n)
     if ns_dtype == "f32":
         raw = [{"tile": 64, "formulation": "gram"}, {"tile": 128, "formulation": "gram"}]
@@ -121,6 +121,9 @@ def candidates(m: int, n: int, ns_dtype: str) -> list:
             raw.append({"tile": 64, "formulation": "gram"})
         raw.append({"tile": 128, "formulation": "gram"})
         raw.append({"tile": 256, "formulation": "gram"})
+        if r <= 1024:
+            raw.append({"tile": 64, "formulation": "direct"})
+            raw.append({"tile": 128, "formulation": "direct"})
         raw.append({"tile": 256, "formulation": "direct"})
     return [h for h in raw if _plannable(m, n, ns_dtype, h)]
 

@@ -27,7 +27,7 @@ def test_candidates_are_plannable():
     assert {c["formulation"] for c in TU.candidates(300, 700, "f32")} == {"gram"}
     # near-square buckets of the 16-bit path: the planner refuses the Gram form
     assert TU.candidates(3584, 3584, "bf16") == [{"tile": 256, "formulation": "direct"}]
-    assert TU.candidates(64, 70, "bf16") == [{"tile": 256, "formulation": "direct"}]
+    assert TU.candidates(64, 70, "bf16") == [{"tile": t, "formulation": "direct"} for t in (64, 128, 256)]
     assert {c["tile"] for c in TU.candidates(3584, 3584, "f32")} == {64, 128}
     assert 64 in {c["tile"] for c in TU.candidates(1024, 4096, "bf16")}
 
@@ -35,7 +35,8 @@ def test_candidates_are_plannable():
 def test_tune_never_picks_an_inaccurate_setting():
     # the fastest candidate misses the accuracy bound: recorded, not chosen
     table = {(None, None): (10.0, 3e-3), (64, "gram"): (1.0, 5e-2), (128, "gram"): (7.5, 4e-3),
-             (256, "gram"): (9.0, 4e-3), (256, "direct"): (8.0, 3e-3)}
+             (256, "gram"): (9.0, 4e-3), (256, "direct"): (8.0, 3e-3), (64, "direct"): (9.5, 3e-3),
+             (128, "direct"): (9.9, 3e-3)}
     timer = lambda m, n, c, h: table[(None, None) if h is None else (h["tile"], h["formulation"])]
     cache = TU.tune([(512, 2048)], "bf16", "bf16", device=DEV, timer=timer)
     e = cache["entries"][TU.cache_key(DEV, "bf16", "bf16", 512, 2048, 1)]
@@ -50,7 +51,7 @@ def test_tune_never_picks_an_inaccurate_setting():
 
 def test_tune_picks_the_fastest_and_skips_cached_shapes():
     table = {(None, None): 10.0, (64, "gram"): 12.0, (128, "gram"): 7.5,
-             (256, "gram"): 9.0, (256, "direct"): 8.0}
+             (256, "gram"): 9.0, (256, "direct"): 8.0, (64, "direct"): 11.0, (128, "direct"): 11.5}
     calls = []
 
     def timer(m, n, count, hint):
@@ -117,7 +118,8 @@ def test_knob_search_on_the_256_wide_kernels():
     # tried from it, one knob at a time, and kept only when >1 % faster
     base = {(128, "gram"): 10.0, (256, "gram"): 8.0, (256, "direct"): 20.0}
     knob = {("group", 2): 8.5, ("group", 4): 7.0, ("group", 16): 7.95, ("xcd_chunk", -1): 6.0,
-            ("xcd_chunk", 32): 6.99, ("xcd_chunk", 256): 7.5, ("waves", 4): 5.96}
+            ("xcd_chunk", 16): 6.99, ("xcd_chunk", 64): 6.5, ("xcd_chunk", 256): 7.5,
+            ("waves", 4): 5.96}
     seen = []
 
     def timer(m, n, count, h):
