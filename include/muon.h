@@ -31,12 +31,12 @@
  *     Results are valid once the stream has reached that point.  When every
  *     bucket of a plan is too small to fill the GPU on its own and their
  *     scratch fits the cap together, muon_step_batched runs the buckets
- *     concurrently on up to 4 internal streams of the plan (default
- *     priority, created on the first such call, destroyed with the plan):
- *     they wait for `stream` on entry and `stream` waits for all of them on
- *     return, so the call behaves as one operation on `stream`.  Each
- *     internal stream's launches are enqueued from its own host thread (the
- *     calling thread for the first; the others are worker threads the plan
+ *     concurrently on `stream` and up to 3 internal streams of the plan
+ *     (default priority, created on the first such call, destroyed with the
+ *     plan): they wait for `stream` on entry and `stream` waits for all of
+ *     them on return, so the call behaves as one operation on `stream`.  Each
+ *     stream's launches are enqueued from its own host thread (the calling
+ *     thread for `stream`; the others are worker threads the plan
  *     starts on its first such call and stops in muon_plan_destroy; each
  *     makes the caller's current device current), and the call returns when
  *     all have enqueued their launches (the calling thread enqueues every

@@ -50,7 +50,13 @@ constexpr int64_t kDefaultCap = 32ll << 30;   // Newton-Schulz scratch cap (byte
 // against the earlier rule (one contiguous range per XCD for triangular
 // grids, runs of max(64, tiles per matrix / 8) for full grids).
 constexpr int kXcdRun = 32;
-constexpr int kMaxSlots = 4;                   // internal streams for concurrent buckets
+// Concurrent buckets run on up to 4 streams: the caller's (slot 0) and up
+// to 3 internal ones, so that with the default 4 hardware queues per process
+// (GPU_MAX_HW_QUEUES) every stream gets a queue of its own; a fifth stream
+// shares a queue with another, and its launches then wait behind that
+// stream's (a kernel trace of one Qwen2.5-7B layer showed two buckets
+// running one after the other that way).
+constexpr int kMaxSlots = 4;
 constexpr int64_t kMaxDim = 1ll << 24;        // per-dimension limit
 constexpr int64_t kMaxShort = 1ll << 16;      // r = min(m, n) limit
 constexpr int kRing = 4;                      // pinned descriptor staging slots
@@ -414,8 +420,10 @@ void release_profile(muon_plan_s* p) {
 }
 
 void release_slots(muon_plan_s* p) {
-  for (hipStream_t s : p->slot_streams) (void)hipStreamDestroy(s);
-  for (hipEvent_t e : p->slot_done) (void)hipEventDestroy(e);
+  for (hipStream_t s : p->slot_streams)
+    if (s) (void)hipStreamDestroy(s);
+  for (hipEvent_t e : p->slot_done)
+    if (e) (void)hipEventDestroy(e);
   if (p->fork_ev) (void)hipEventDestroy(p->fork_ev);
   p->slot_streams.clear();
   p->slot_done.clear();
@@ -500,7 +508,8 @@ muon_status run_slots(WorkerPool& w, int S, int device, const std::function<muon
   return st;
 }
 
-// Internal streams (default priority) and their fork / join events.
+// Internal streams (default priority) of slots 1.. and their fork / join
+// events (slot 0 runs on the caller's stream; its entries stay null).
 muon_status ensure_slots(muon_plan_s* p) {
   if ((int)p->slot_streams.size() == p->lay.nslots) return MUON_OK;
   release_slots(p);
@@ -508,7 +517,9 @@ muon_status ensure_slots(muon_plan_s* p) {
     p->fork_ev = nullptr;
     return MUON_ERR_HIP;
   }
-  for (int i = 0; i < p->lay.nslots; ++i) {
+  p->slot_streams.push_back(nullptr);
+  p->slot_done.push_back(nullptr);
+  for (int i = 1; i < p->lay.nslots; ++i) {
     hipStream_t s = nullptr;
     hipEvent_t e = nullptr;
     if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
@@ -581,7 +592,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
     if (st != MUON_OK) return st;
     if (hipEventRecord(p->fork_ev, caller) != hipSuccess) return MUON_ERR_HIP;
     for (hipStream_t s : p->slot_streams)
-      if (hipStreamWaitEvent(s, p->fork_ev, 0) != hipSuccess) return MUON_ERR_HIP;
+      if (s && hipStreamWaitEvent(s, p->fork_ev, 0) != hipSuccess) return MUON_ERR_HIP;
   }
   // Enqueue the launch sequence of every bucket on slot `only_slot` (all
   // buckets when negative).
@@ -591,7 +602,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
       const size_t slot = bi % (size_t)S;
       if (only_slot >= 0 && (int)slot != only_slot) continue;
       const Bucket& B = p->buckets[bi];
-      const hipStream_t stream = S > 1 ? p->slot_streams[slot] : caller;
+      const hipStream_t stream = slot > 0 ? p->slot_streams[slot] : caller;
       char* region = wsb + L.off_scratch + L.slot_scratch_off[slot];
       float* d_part = (float*)(wsb + L.off_part) + L.slot_part_floats * slot;
       const int64_t rr = B.r_pad * B.r_pad;
@@ -962,7 +973,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
   // join: the caller's stream waits for every slot (also after a failed
   // launch, so that no work of this call is left unordered)
   if (S > 1) {
-    for (int i = 0; i < S; ++i) {
+    for (int i = 1; i < S; ++i) {
       if (hipEventRecord(p->slot_done[(size_t)i], p->slot_streams[(size_t)i]) != hipSuccess ||
           hipStreamWaitEvent(caller, p->slot_done[(size_t)i], 0) != hipSuccess)
         st = MUON_ERR_HIP;
