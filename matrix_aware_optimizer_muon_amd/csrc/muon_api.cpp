@@ -1148,14 +1148,17 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       }
     }
     // Buckets too small to fill the device on their own (one launch chunk,
-    // every r x r product under two waves of tiles for the 256 compute
-    // units) run concurrently on up to kMaxSlots streams when their scratch
-    // regions fit the cap together; otherwise all run one after another.
+    // every r x r product under two waves of workgroups for the 256 compute
+    // units: a compute unit holds one 256-wide tile's workgroup, two of the
+    // 128-wide kernel and four of the 64-wide one) run concurrently on up to
+    // kMaxSlots streams when their scratch regions fit the cap together;
+    // otherwise all run one after another.
     const int nb = (int)p->buckets.size();
     bool small = nb > 1;
     for (const Bucket& B : p->buckets) {
       const int64_t T = B.r_pad / B.bt;
-      if (B.chunks.size() != 1 || (int64_t)B.count * (T * (T + 1) / 2) >= 512) small = false;
+      const int64_t per_cu = B.bt == 256 ? 1 : (B.bt == 128 ? 2 : 4);
+      if (B.chunks.size() != 1 || (int64_t)B.count * (T * (T + 1) / 2) >= 512 * per_cu) small = false;
     }
     int S = small ? std::min(nb, kMaxSlots) : 1;
     std::vector<size_t> slot_bytes((size_t)S, 0);
