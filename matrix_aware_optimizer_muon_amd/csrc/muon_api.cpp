@@ -298,7 +298,26 @@ muon_status ensure_ring(muon_plan_s* p) {
 
 // Upload the per-matrix pointer table into the workspace (one H->D copy per
 // call, from a pinned slot that is reused only after its previous copy ran).
+// Write the pointer table from kernel arguments (kTableChunk entries per
+// launch) at dst: no staging buffer, and the stream stays on its compute
+// queue (a host-to-device copy between kernels costs a copy-engine hand-off
+// each way, ~15 us per call in a kernel trace of a one-matrix step).
+muon_status write_table(const muon_plan_s* p, MatPtrs* dst, hipStream_t stream) {
+  for (int64_t k = 0; k < p->nmat; k += kTableChunk) {
+    TableChunk tc{};
+    tc.count = (int)std::min<int64_t>(kTableChunk, p->nmat - k);
+    for (int e = 0; e < tc.count; ++e) tc.e[e] = p->host_table[(size_t)(k + e)];
+    if (launch_write_table(tc, dst + k, stream) != hipSuccess) return MUON_ERR_HIP;
+  }
+  return MUON_OK;
+}
+
+// Small tables (up to kKernelTable entries) go through write_table; larger
+// ones through one copy from a pinned ring slot.
+constexpr int64_t kKernelTable = 4 * kTableChunk;
+
 muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
+  if (p->nmat <= kKernelTable) return write_table(p, (MatPtrs*)((char*)ws + p->lay.off_table), stream);
   muon_status st = ensure_ring(p);
   if (st != MUON_OK) return st;
   Slot& s = p->ring[p->next_slot];
@@ -1277,13 +1296,8 @@ muon_status muon_step_batched_noalloc(muon_plan_t p, float* const* W, float* con
   fill_table(p, W, M, G, O_out);
   // the pointer table reaches the scratch as kernel arguments: no staging
   // buffer, and ordered on the stream like the rest of the step
-  MatPtrs* d_table = (MatPtrs*)(ws + p->serial.off_table);
-  for (int64_t k = 0; k < p->nmat; k += kTableChunk) {
-    TableChunk tc{};
-    tc.count = (int)std::min<int64_t>(kTableChunk, p->nmat - k);
-    for (int e = 0; e < tc.count; ++e) tc.e[e] = p->host_table[(size_t)(k + e)];
-    if (launch_write_table(tc, d_table + k, stream) != hipSuccess) return MUON_ERR_HIP;
-  }
+  st = write_table(p, (MatPtrs*)(ws + p->serial.off_table), stream);
+  if (st != MUON_OK) return st;
   p->prof_active = false;
   return enqueue_refresh(p, p->serial, ws, lr, wd, stream);
 }
