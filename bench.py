@@ -373,6 +373,23 @@ def main():
             r.pop("kernels", None)
             extra[f"config{k}"] = r
             print(f"extra config {k}: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
+        if args.config == 4:
+            # the same workload planned with the shipped tuning cache's
+            # per-shape winners (no tuning at run time: shapes it lacks keep
+            # the planner's rule)
+            from matrix_aware_optimizer_muon_amd import tune as TU
+            try:
+                cache = TU.load_cache(TU.SHIPPED_CACHE)
+                th = TU.hints_for(w.shapes, w.grad_dtype, w.ns_dtype, cache)
+            except Exception as e:  # pragma: no cover
+                th = None
+                print(f"tuned extra skipped: {e}", file=sys.stderr)
+            if th is not None:
+                r, _, _ = run_workload(4, args.steps, args.warmup, hints=th, profile=False)
+                r.pop("plan", None)
+                r["hints"] = {f"{m}x{n}": h for (m, n), h in th.items()}
+                extra["config4_tuned"] = r
+                print(f"extra config 4 tuned: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
         out["extra"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, per_shape)
