@@ -4,18 +4,23 @@
 // product of the Gram form, and the direct form's X' = a X + P~ X (XUPD).
 //
 // Both operands are K-contiguous (the prep kernel writes X0 and X0^T).
-// 8 wave64 (two per SIMD) in 2 x 4, each owning 128 x 64 = 4 x 2 blocks of
-// 32x32x16 MFMAs (128 fp32 accumulators), so one wave's barrier, DMA-issue
+// 8 wave64 (two per SIMD) in 2 x 4, each owning 128 x 64 = 8 x 4 blocks of
+// 16x16x32 MFMAs (128 fp32 accumulators), so one wave's barrier, DMA-issue
 // and LDS waits overlap the other's MFMAs (a 4-wave 128 x 128 variant serves
 // SYRK and the final product when a tuning hint asks for it).  A stage holds
-// 32 K elements of both 256-row
-// operand tiles (2 x 16 KB); every 1-KB DMA instruction lands lane L at LDS
-// offset 16*L of its block, so the 16-byte chunk swizzle is applied on the
-// global side.  Up to four stages
+// 32 K elements of both 256-row operand tiles (2 x 16 KB), one MFMA K step;
+// every 1-KB DMA instruction lands lane L at LDS offset 16*L of its block, so
+// the 16-byte chunk swizzle is applied on the global side.  Up to four stages
 // are in flight; each K step has one barrier, placed so that it both
 // publishes the next stage and retires the reads of the current one.  The
-// two K=16 halves of a stage are software pipelined: the fragments of one
-// half are read from LDS while the MFMAs of the other run.
+// stage's MFMAs run in two halves by block row: the fragments of the second
+// half are read from LDS while the first half's MFMAs run, and the next
+// stage's first-half fragments while the second half's run.
+//
+// 16x16x32 rather than 32x32x16 MFMAs: the same issue rate per flop with half
+// the accumulator traffic per instruction; measured on the final product
+// (same box, sustained): 1046 -> 1084 TFLOP/s over eight 3584 x 18944
+// products, 970 -> 1028 over one.
 #include "common.hpp"
 #include "gemm_epilogue.hpp"
 #include "kernels.h"
@@ -41,22 +46,32 @@ typedef __attribute__((address_space(3))) void lds_ptr_t;
 typedef const __attribute__((address_space(1))) void gbl_ptr_t;
 
 // 16-byte chunk swizzle of a 64-byte row for the MFMA fragment reads (lane
-// l32 reads row base + l32, chunk 2s + h).  Chosen by measurement on gfx950
-// with eight waves reading concurrently: (r ^ (r >> 3)) & 3 sustains ~200
-// B/clk/CU of ds_read_b128 and shows no bank-conflict cycles, where
-// ((r >> 1) ^ (r >> 3)) & 3 reached ~120 B/clk/CU with ~3.5 conflict cycles
-// per read.
-__device__ __forceinline__ int swz4(int row) { return (row ^ (row >> 3)) & 3; }
+// l reads row base + (l & 15), chunk l >> 4).  Chosen by measurement on
+// gfx950 (bank-conflict counter of a one-wave ds_read_b128 probe over all
+// 1024 GF(2)-linear 2-bit functions of the row's low five bits): flipping
+// chunk bit 1 with row bit 2 is conflict free, while (r ^ (r >> 3)) & 3,
+// (r >> 2) & 3 and (r ^ (r >> 2)) & 3 cost four conflict cycles per read.
+__device__ __forceinline__ int swz4(int row) { return ((row >> 2) & 1) << 1; }
+
+// Slot of 8-byte chunk q (tile rows 4q..4q+3) in staged column c of the
+// 16-bit epilogue (64 slots per 512-byte column): a bijection per column,
+// conflict free for the staging writes (16 columns x 4 chunks per
+// instruction), the row reads (columns 4L + k of one chunk) and the mirror
+// reads (one whole column per half wave, as aligned 16-byte pairs).
+__device__ __forceinline__ int slot16(int c, int q) {
+  const int h = ((((c >> 2) & 3) << 2) | ((c & 3) << 4)) ^ ((c >> 4) & 3) ^ (((c >> 6) & 3) << 4);
+  return q ^ h;
+}
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int KIND>
-__device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x16& c) {
+__device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x4& c) {
   if constexpr (KIND == 0) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   } else {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
 }
@@ -126,19 +141,20 @@ __device__ __forceinline__ uint2 q_from_p(uint2 pv, float inv_sp, const GemmPara
 
 }  // namespace
 
-// NW = 4: waves in 2 x 2, each 128 x 128 (4 x 4 MFMA blocks, one wave per SIMD)
-// NW = 8: waves in 2 x 4, each 128 x 64 (4 x 2 MFMA blocks, two waves per SIMD)
+// NW = 4: waves in 2 x 2, each 128 x 128 (8 x 8 MFMA blocks, one wave per SIMD)
+// NW = 8: waves in 2 x 4, each 128 x 64 (8 x 4 MFMA blocks, two waves per SIMD)
 template <int KIND, int EPI, int NW>
 __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p) {
   constexpr int NT = 64 * NW;                    // threads
   constexpr int WGN = NW / 2;                    // waves along N
   constexpr int WTN = DT / WGN;                  // wave tile N (128 or 64)
-  constexpr int FM = 4, FN = WTN / 32;           // MFMA blocks per wave
+  constexpr int FM = 8, FN = WTN / 16;           // 16 x 16 MFMA blocks per wave
   constexpr int DMA_PER_OP = OPB / 1024 / NW;    // 1-KB DMA instructions per wave per operand
   constexpr int DPS = 2 * DMA_PER_OP;            // per wave per stage (vmcnt units)
-  constexpr int NMF = FM * FN;                   // MFMAs per half stage
-  static_assert(NMF == 2 * DPS, "two MFMAs per DMA instruction");
-  static_assert((FM - 1) * FN >= DPS, "first-half MFMAs carry DPS / 2 DMA instructions");
+  // MFMAs between the refill DMAs: the first half-stage carries DPS / 2 of
+  // them after its first block row, the second half-stage the other DPS / 2
+  constexpr int I1 = 3 * FN / (DPS / 2), I2 = 4 * FN / (DPS / 2);
+  static_assert(I1 * (DPS / 2) == 3 * FN && I2 * (DPS / 2) == 4 * FN, "even DMA spacing");
   constexpr int RR = 128;
   constexpr int SMEM_OPS = DSTAGES * STAGEB;
   constexpr int SMEM_EPI = RR * DT * 4;
@@ -150,7 +166,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / WGN, wn = wave % WGN;
-  const int h = lane >> 5, l32 = lane & 31;
+  const int q4 = lane >> 4, c16 = lane & 15;  // MFMA lane: K chunk / output row group, row / column
 
   const uint32_t bid = p.xcd_chunk > 0 ? xcd_remap_chunked(blockIdx.x, gridDim.x, (uint32_t)p.xcd_chunk)
                                        : xcd_remap(blockIdx.x, gridDim.x);
@@ -187,9 +203,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   const int nk = p.Kdim / DBK;
   // Wave priority: raised while a wave issues an MFMA run and lowered for
   // its fragment reads and the stage barrier, so that the SIMD's arbiter
-  // favours the wave that feeds the matrix core.  Measured in same-box A/B
-  // runs: PQPG and PH 1.7-1.8 % and SYRK 0.6 % faster, POLY 0.9 % slower,
-  // the final product and XUPD unchanged, so only the first three use it.
+  // favours the wave that feeds the matrix core (measured with 32x32x16
+  // MFMAs in same-box A/B runs: PQPG and PH 1.7-1.8 % and SYRK 0.6 %
+  // faster, POLY 0.9 % slower, the final product and XUPD unchanged, so
+  // only the first three use it).
   constexpr bool SP = EPI == EPI_SYRK || EPI == EPI_PQPG || EPI == EPI_PH;
   auto dma = [&](int q, int buf, int ks) {
     const int koff = (ks < nk ? ks : nk - 1) * ROWB;
@@ -199,39 +216,30 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)sb, 16, 0, 0);
   };
 
-  // fragment addresses (byte offsets within a stage) for half s
-  int offA[2][FM], offB[2][FN];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-      const int ra = wm * 128 + f * 32 + l32;
-      offA[s][f] = ra * ROWB + (((2 * s + h) ^ swz4(ra)) << 4);
-    }
-#pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int rb = wn * WTN + f * 32 + l32;
-      offB[s][f] = OPB + rb * ROWB + (((2 * s + h) ^ swz4(rb)) << 4);
-    }
-  }
+  // fragment addresses (byte offsets within a stage): block f of A / B
+  // starts 16 rows (1 KB) after block f - 1, and the swizzle depends only on
+  // the row's low bits, so one base per operand serves every block
+  const int ra0 = wm * 128 + c16, rb0 = wn * WTN + c16;
+  const int offA = ra0 * ROWB + ((q4 ^ swz4(ra0)) << 4);
+  const int offB = OPB + rb0 * ROWB + ((q4 ^ swz4(rb0)) << 4);
+  auto frag = [&](const char* sb, int off, int f) { return *(const u32x4*)(sb + off + f * 16 * ROWB); };
 
-  f32x16 acc[FM][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  u32x4 fa[FM], fb0[FN], fb1[FN];
 
-  // Identity-term harvest (POLY, PQPG, PH).  The term X(m, n) that the
-  // epilogue adds is symmetric, and X(n, m) is this tile's own B operand at
-  // K = m: stages hk0 .. hk0+3 hold the wave's 128 rows m, stage hk0 + i
-  // the 32 rows of MFMA block row i.  While such a stage is resident each
-  // lane reads the 16-byte chunks holding its FN x 4 groups of 4 consecutive
-  // m (half h of each chunk) and adds gamma * X to the accumulators, so the
-  // epilogue reads no r x r input.
+  // Identity-term harvest (POLY, PQPG, PH, XUPD, XFINAL).  The term X(m, n)
+  // that the epilogue adds is symmetric, and X(n, m) is this tile's own B
+  // operand at K = m: stages hk0 .. hk0+3 hold the wave's 128 rows m, stage
+  // hk0 + s the 32 rows of MFMA block rows 2s and 2s + 1.  While such a stage
+  // is resident each lane reads, for each of its FN block columns n and both
+  // block rows, the 16-byte chunk holding its 4 consecutive m (half q4 & 1 of
+  // chunk 2 (i & 1) + (q4 >> 1)) and adds gamma * X to the accumulators, so
+  // the epilogue reads no r x r input.
   constexpr bool HARVEST =
       EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH || EPI == EPI_XUPD || EPI == EPI_XFINAL;
   float gam = 0.0f;
@@ -255,45 +263,45 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS + DPS / 2, 15));
   barrier();
 #pragma unroll
-  for (int f = 0; f < FM; ++f) fa0[f] = *(const u32x4*)(smem + offA[0][f]);
+  for (int f = 0; f < FM / 2; ++f) fa[f] = frag(smem, offA, f);
 #pragma unroll
-  for (int f = 0; f < FN; ++f) fb0[f] = *(const u32x4*)(smem + offB[0][f]);
+  for (int f = 0; f < FN; ++f) fb0[f] = frag(smem, offB, f);
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // one K step; fb holds this stage's B fragments, fbn receives the next's
+  auto step = [&](int kt, u32x4* fb, u32x4* fbn) {
     const int buf = kt & (DSTAGES - 1);
     const char* sb = smem + buf * STAGEB;
-    // first half: one row of MFMAs, then this stage's second-half fragment
-    // reads, then the remaining MFMAs (the reads land behind them)
+    // first half (block rows 0..3): one block row of MFMAs, then this
+    // stage's second-half A fragments (and harvest chunks), then the other
+    // three block rows
     if constexpr (SP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) mfma<KIND>(fa0[0], fb0[j], acc[0][j]);
+    for (int j = 0; j < FN; ++j) mfma<KIND>(fa[0], fb[j], acc[0][j]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SP) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int f = 0; f < FM; ++f) fa1[f] = *(const u32x4*)(sb + offA[1][f]);
-#pragma unroll
-    for (int f = 0; f < FN; ++f) fb1[f] = *(const u32x4*)(sb + offB[1][f]);
+    for (int f = FM / 2; f < FM; ++f) fa[f] = frag(sb, offA, f);
     const int hs = kt - hk0;
-    u32x4 hv[FN][4];  // whole 16-byte chunks; this lane's 4 values are half h
+    u32x4 hv[FN][2];  // whole 16-byte chunks; this lane's 4 values are half q4 & 1
     if (HARVEST && (unsigned)hs < 4u) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int rb = wn * WTN + j * 32 + l32;
+        const int rb = wn * WTN + j * 16 + c16;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          hv[j][g] = *(const u32x4*)(sb + OPB + rb * ROWB + ((g ^ swz4(rb)) << 4));
+        for (int ii = 0; ii < 2; ++ii)
+          hv[j][ii] = *(const u32x4*)(sb + OPB + rb * ROWB + (((2 * ii + (q4 >> 1)) ^ swz4(rb)) << 4));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SP) __builtin_amdgcn_s_setprio(1);
-    // the rest of the first half, with the second half of stage kt+3's DMAs
-    // (its buffer was released at the previous iteration's barrier): one
-    // DMA instruction after every two MFMAs
+    // the other three block rows of the first half, with the second half of
+    // stage kt+3's DMAs (its buffer was released at the previous iteration's
+    // barrier)
 #pragma unroll
-    for (int n = 0; n < (FM - 1) * FN; ++n) {
-      mfma<KIND>(fa0[1 + n / FN], fb0[n % FN], acc[1 + n / FN][n % FN]);
-      if (n % 2 == 1 && n / 2 < DPS / 2) {
-        dma(DPS / 2 + n / 2, (kt + DSTAGES - 1) & (DSTAGES - 1), kt + DSTAGES - 1);
+    for (int n = 0; n < 3 * FN; ++n) {
+      mfma<KIND>(fa[1 + n / FN], fb[n % FN], acc[1 + n / FN][n % FN]);
+      if (n % I1 == I1 - 1) {
+        dma(DPS / 2 + n / I1, (kt + DSTAGES - 1) & (DSTAGES - 1), kt + DSTAGES - 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -304,60 +312,75 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     // retire
     __builtin_amdgcn_s_waitcnt(wait_imm(2 * DPS, 0));
     if (HARVEST && (unsigned)hs < 4u) {
+      // every block row takes gamma X or 0 by a select on the wave-uniform
+      // stage index: branching to the two block rows of stage hs lets the
+      // compiler merge the four branches into one dynamically indexed add,
+      // which moves the accumulators to scratch memory
+      float gx[2][FN][4];
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 h = hv[j][ii];
+          const uint32_t w0 = (q4 & 1) ? h[2] : h[0];
+          const uint32_t w1 = (q4 & 1) ? h[3] : h[1];
+          gx[ii][j][0] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)w0);
+          gx[ii][j][1] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16));
+          gx[ii][j][2] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)w1);
+          gx[ii][j][3] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16));
+        }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if (i != hs) continue;
+        const bool on = (i >> 1) == hs;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const uint32_t w0 = h ? hv[j][g][2] : hv[j][g][0];
-            const uint32_t w1 = h ? hv[j][g][3] : hv[j][g][1];
-            const _Float16 x[4] = {__builtin_bit_cast(_Float16, (uint16_t)w0),
-                                   __builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16)),
-                                   __builtin_bit_cast(_Float16, (uint16_t)w1),
-                                   __builtin_bit_cast(_Float16, (uint16_t)(w1 >> 16))};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += gam * (float)x[e];
-          }
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += on ? gx[i & 1][j][e] : 0.0f;
       }
     }
     barrier();
     {  // next stage's first half (unused after the last step; in LDS bounds)
       const char* sn = smem + ((kt + 1) & (DSTAGES - 1)) * STAGEB;
 #pragma unroll
-      for (int f = 0; f < FM; ++f) fa0[f] = *(const u32x4*)(sn + offA[0][f]);
+      for (int f = 0; f < FM / 2; ++f) fa[f] = frag(sn, offA, f);
 #pragma unroll
-      for (int f = 0; f < FN; ++f) fb0[f] = *(const u32x4*)(sn + offB[0][f]);
+      for (int f = 0; f < FN; ++f) fbn[f] = frag(sn, offB, f);
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (SP) __builtin_amdgcn_s_setprio(1);
-    // second half, with the first half of the refill of this stage's buffer
-    // (stage kt+4): one DMA instruction after every four MFMAs
+    // second half (block rows 4..7), with the first half of the refill of
+    // this stage's buffer (stage kt+4)
 #pragma unroll
-    for (int g = 0; g < DPS; ++g) {
-      mfma<KIND>(fa1[(2 * g) / FN], fb1[(2 * g) % FN], acc[(2 * g) / FN][(2 * g) % FN]);
-      mfma<KIND>(fa1[(2 * g + 1) / FN], fb1[(2 * g + 1) % FN],
-                 acc[(2 * g + 1) / FN][(2 * g + 1) % FN]);
-      if (g % 2 == 0) dma(g / 2, buf, kt + DSTAGES);
+    for (int n = 0; n < 4 * FN; ++n) {
+      mfma<KIND>(fa[FM / 2 + n / FN], fb[n % FN], acc[FM / 2 + n / FN][n % FN]);
+      if (n % I2 == I2 - 1) dma(n / I2, buf, kt + DSTAGES);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // two K steps per trip, so that the B fragments alternate between two
+  // register sets without copies
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, fb0, fb1);
+    step(kt + 1, fb1, fb0);
   }
+  if (kt < nk) step(kt, fb0, fb1);
   if constexpr (SP) __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
   __syncthreads();
 
+  // accumulator element e of block (i, j) is tile row wm*128 + i*16 + 4*q4 + e,
+  // tile column wn*WTN + j*16 + c16
   if constexpr (EPI == EPI_FINAL || EPI == EPI_XFINAL) {
     // Final product (and the direct form's last X', whose identity term the
     // loop has harvested): the fp32 tile goes through LDS in two rounds of 128
-    // rows, its 16-byte column chunks XOR-swizzled by (row / 4) (epi_off) so
-    // that the staging writes and the row reads are conflict free.  All of a
-    // round's W rows are requested before the staging, so their latency
-    // overlaps it; each thread then updates four consecutive columns of a row
-    // (64 threads per tile row).
-    auto epi_off = [](int il, int jc) {
-      return il * DT + ((((jc >> 2) ^ ((il >> 2) & 63)) << 2) | (jc & 3));
-    };
+    // rows, its 16-column groups XOR-swizzled by bits 2-3 of the row
+    // (epi_off) so that the staging writes (16 columns of 4 rows 4 apart per
+    // instruction) and the row reads are conflict free.  All of a round's W
+    // rows are requested before the staging, so their latency overlaps it;
+    // each thread then updates four consecutive columns of a row (64 threads
+    // per tile row).
+    auto epi_off = [](int il, int jc) { return il * DT + (jc ^ (((il >> 2) & 3) << 4)); };
     const int jl = (tid & 63) * 4;
     const int gj = row0B + jl;
     constexpr int RPI = NT / 64;   // tile rows per row-pass iteration
@@ -381,11 +404,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
           for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int il = i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-              const int jc = wn * WTN + j * 32 + l32;
-              stile[epi_off(il, jc)] = acc[i][j][v];
-            }
+            for (int v = 0; v < 4; ++v)
+              stile[epi_off(i * 16 + 4 * q4 + v, wn * WTN + j * 16 + c16)] = acc[i][j][v];
       }
       __syncthreads();
 #pragma unroll
@@ -412,8 +432,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     // 16-bit output format (v = beta * acc, scaled fp16 or bf16) and stages
     // the whole tile once, column-major, in the freed operand ring: T[c] holds
     // column c of the tile as 64 chunks of 4 rows (8 bytes), chunk q stored at
-    // slot q ^ f(c) (t_off), which keeps the staging writes and both read
-    // passes below free of bank conflicts.  After one barrier:
+    // slot slot16(c, q), which keeps the staging writes and both read passes
+    // below free of bank conflicts.  After one barrier:
     //   rows:    lane L of an iteration reads the 4 x 4 block of columns
     //            4L..4L+3 x rows 4q..4q+3, transposes it in registers and
     //            writes 4 rows (each store instruction is one 512-byte row)
@@ -421,7 +441,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     // Diagonal tiles store the lower triangle directly and mirror the strictly
     // lower part; POLY on the first iteration also writes Q1 = a I + P~,
     // derived from the staged P~ (power-of-two rescale).
-    auto t_off = [](int c, int q) { return c * 512 + ((q ^ (((c >> 2) ^ ((c & 3) << 3)) & 31)) << 3); };
+    auto t_off = [](int c, int q) { return c * 512 + (slot16(c, q) << 3); };
     const bool diag = p.triangular && ti == tj;
     const float beta = rr_beta<EPI>(p, mat, prod);
     uint16_t* out1;
@@ -450,15 +470,12 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 v = make_float4(acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                                       acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *(uint2*)(smem + t_off(wn * WTN + 32 * j + l32, wm * 32 + 8 * i + 2 * g + h)) =
-              bf1 ? pack_b4(make_float4(v.x * bsc, v.y * bsc, v.z * bsc, v.w * bsc))
-                  : pack_h4(v, bsc);
-        }
+      for (int j = 0; j < FN; ++j) {
+        const f32x4 v = acc[i][j];
+        *(uint2*)(smem + t_off(wn * WTN + 16 * j + c16, wm * 32 + 4 * i + q4)) =
+            bf1 ? pack_b4(make_float4(v[0] * bsc, v[1] * bsc, v[2] * bsc, v[3] * bsc))
+                : pack_h4(make_float4(v[0], v[1], v[2], v[3]), bsc);
+      }
     __syncthreads();
     const bool qout = EPI == EPI_POLY && p.first;
     uint16_t* out2 = (uint16_t*)p.Qh_dst;
@@ -499,14 +516,14 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     }
     // mirror pass: two staged columns per iteration, half a wave each; lane
     // k of a half takes chunks 2k and 2k + 1 (tile rows 8k..8k+7), which sit
-    // in slots s and s ^ 1 (s = 2k ^ f(c)) of one aligned 16-byte pair, and
-    // stores them as eight consecutive elements of mirrored row c
+    // in slots s and s ^ 1 (s = slot16(c, 2k)) of one aligned 16-byte pair,
+    // and stores them as eight consecutive elements of mirrored row c
     constexpr int CPW = 256 / NW;  // mirrored rows per wave
 #pragma unroll 4
     for (int it = 0; it < CPW / 2; ++it) {
       const int jc = wave * CPW + 2 * it + (lane >> 5);
       const int k = lane & 31;
-      const int sl = (2 * k) ^ (((jc >> 2) ^ ((jc & 3) << 3)) & 31);
+      const int sl = slot16(jc, 2 * k);
       const uint4 w = *(const uint4*)(smem + jc * 512 + ((sl & ~1) << 3));
       const bool sw = sl & 1;
       const uint2 v0 = sw ? make_uint2(w.z, w.w) : make_uint2(w.x, w.y);  // rows 8k..8k+3
