@@ -136,6 +136,31 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
   const int nk = p.Kdim / KT;
   load_tile<ES, BT>(Ab, p.lda, row0A, 0, tid, ra);
   load_tile<ES, BT>(Bb, p.ldb, row0B, 0, tid, rb);
+
+  // Final product (and the direct form's last X') on 64-wide 16-bit tiles: the
+  // W values (and the a X term of XFINAL) that this thread updates in the
+  // epilogue's row pass, four groups of four, are requested before the K
+  // loop, so their memory latency overlaps the loop instead of following it
+  // (the small buckets that take this tile run a few K steps, and the tile's
+  // time was mostly these loads' latency).
+  constexpr bool FIN = EPI == EPI_FINAL || EPI == EPI_XFINAL;
+  constexpr bool PRE = FIN && BT == 64 && !F32PATH;
+  constexpr int FTPR = BT / 4;       // threads per tile row in the row pass
+  constexpr int FRPI = 256 / FTPR;   // tile rows per row-pass iteration
+  constexpr int FNE = PRE ? RR / FRPI : 1;
+  float4 wpre[FNE], xpre[FNE];
+  bool wok[FNE];
+  if constexpr (PRE) {
+    const MatPtrs mp = p.table[mat];
+#pragma unroll
+    for (int e = 0; e < FNE; ++e) {
+      const int gi = row0A + e * FRPI + tid / FTPR, gj = row0B + (tid % FTPR) * 4;
+      wok[e] = p.vec && gi < p.out_rows && gj + 4 <= p.out_cols;
+      wpre[e] = wok[e] ? nt_load4(mp.W + (size_t)gi * p.out_cols + gj) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (EPI == EPI_XFINAL)
+        xpre[e] = ld4h(p.Xid, (size_t)mat * p.y_stride + (size_t)gi * p.ldyn + gj);
+    }
+  }
   store_tile<BT>(smem[0][0], ra, tid);
   store_tile<BT>(smem[0][1], rb, tid);
   __syncthreads();
@@ -196,19 +221,33 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
       // (W is touched once; the fp32 tile row is read from LDS as scalars).
       // XFINAL (the direct form's last X' = a X + P~ X, X and P~ scaled
       // fp16): acc + a sP X^ is sP sX X', so O = (acc + a sP X^) / (sP sX)
-      constexpr int TPR = BT / 4;        // threads per tile row
-      constexpr int RPI = 256 / TPR;     // tile rows per iteration
+      constexpr int TPR = FTPR;          // threads per tile row
+      constexpr int RPI = FRPI;          // tile rows per iteration
       const float inv = EPI == EPI_FINAL ? p.inv_norm[mat] : 1.0f / (p.sP * p.sX);
 #pragma unroll 4
       for (int e = 0; e < RR / RPI; ++e) {
         const int il = e * RPI + tid / TPR, jl = (tid % TPR) * 4;
         const float* sr = stile + il * EPI_LD + jl;
         float4 acc4 = make_float4(sr[0], sr[1], sr[2], sr[3]);
-        if constexpr (EPI == EPI_XFINAL) {
-          const float4 x = ld4h(p.Xid, (size_t)mat * p.y_stride + (size_t)(gr0 + il) * p.ldyn + row0B + jl);
-          acc4 = f4_axpy(1.0f, acc4, p.a * p.sP, x);
+        if constexpr (PRE) {
+          // W (and X) were requested before the K loop
+          if constexpr (EPI == EPI_XFINAL) acc4 = f4_axpy(1.0f, acc4, p.a * p.sP, xpre[e]);
+          if (wok[e]) {
+            const MatPtrs mp = p.table[mat];
+            const float4 o = make_float4(acc4.x * inv, acc4.y * inv, acc4.z * inv, acc4.w * inv);
+            const size_t idx = (size_t)(gr0 + il) * p.out_cols + row0B + jl;
+            nt_store4(mp.W + idx, f4_axpy(p.decay, wpre[e], -p.step, o));
+            if (mp.O) nt_store4(mp.O + idx, o);
+          } else {
+            epilogue_final4(p, mat, gr0 + il, row0B + jl, acc4, inv);
+          }
+        } else {
+          if constexpr (EPI == EPI_XFINAL) {
+            const float4 x = ld4h(p.Xid, (size_t)mat * p.y_stride + (size_t)(gr0 + il) * p.ldyn + row0B + jl);
+            acc4 = f4_axpy(1.0f, acc4, p.a * p.sP, x);
+          }
+          epilogue_final4(p, mat, gr0 + il, row0B + jl, acc4, inv);
         }
-        epilogue_final4(p, mat, gr0 + il, row0B + jl, acc4, inv);
       }
     } else if constexpr (EPI == EPI_XUPD) {
       // X'^ = a X^ + acc / sP in the scaled fp16 units of X^ (acc = sP sX P~ X):

@@ -201,13 +201,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   // last stage (in bounds; their buffer is never read), so every K step
   // issues the same number of DMAs and the vmcnt bookkeeping is constant.
   const int nk = p.Kdim / DBK;
-  // Wave priority: raised while a wave issues an MFMA run and lowered for
-  // its fragment reads and the stage barrier, so that the SIMD's arbiter
-  // favours the wave that feeds the matrix core (measured with 32x32x16
-  // MFMAs in same-box A/B runs: PQPG and PH 1.7-1.8 % and SYRK 0.6 %
-  // faster, POLY 0.9 % slower, the final product and XUPD unchanged, so
-  // only the first three use it).
-  constexpr bool SP = EPI == EPI_SYRK || EPI == EPI_PQPG || EPI == EPI_PH;
   auto dma = [&](int q, int buf, int ks) {
     const int koff = (ks < nk ? ks : nk - 1) * ROWB;
     char* sb = smem + buf * STAGEB + (q >= DMA_PER_OP ? OPB : 0) +
@@ -274,11 +267,9 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     // first half (block rows 0..3): one block row of MFMAs, then this
     // stage's second-half A fragments (and harvest chunks), then the other
     // three block rows
-    if constexpr (SP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < FN; ++j) mfma<KIND>(fa[0], fb[j], acc[0][j]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SP) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int f = FM / 2; f < FM; ++f) fa[f] = frag(sb, offA, f);
     const int hs = kt - hk0;
@@ -293,7 +284,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SP) __builtin_amdgcn_s_setprio(1);
     // the other three block rows of the first half, with the second half of
     // stage kt+3's DMAs (its buffer was released at the previous iteration's
     // barrier)
@@ -306,7 +296,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SP) __builtin_amdgcn_s_setprio(0);
     // stage kt+1 landed for this wave (the later DMAs, 2 * DPS of them, may
     // still fly) and this wave's reads of stage kt are done; then publish /
     // retire
@@ -347,7 +336,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       for (int f = 0; f < FN; ++f) fbn[f] = frag(sn, offB, f);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SP) __builtin_amdgcn_s_setprio(1);
     // second half (block rows 4..7), with the first half of the refill of
     // this stage's buffer (stage kt+4)
 #pragma unroll
@@ -365,7 +353,6 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     step(kt + 1, fb1, fb0);
   }
   if (kt < nk) step(kt, fb0, fb1);
-  if constexpr (SP) __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_s_waitcnt(wait_imm(0, 0));
   __syncthreads();
 
