@@ -208,9 +208,13 @@ typedef struct {
   int tile;                  /* 64, 128 or 256                               */
   muon_formulation formulation; /* MUON_FORM_GRAM or MUON_FORM_DIRECT        */
   int transposed;            /* 1 iff rows > cols (X0 = U^T)                 */
-  int fused_recursion;       /* 1: the Gram form's whole r x r recursion runs
-                                as one launch, one workgroup per matrix (16-bit
-                                path, tiles below 256, r padded to <= 128)   */
+  int fused_recursion;       /* 1: the whole Newton-Schulz iteration runs as
+                                one launch, one workgroup per matrix: the Gram
+                                form's r x r recursion (16-bit path, tiles
+                                below 256, r padded to <= 128), or the direct
+                                form's products and the update (16-bit path,
+                                tiles below 256, padded squares of 128 or
+                                256, rows <= cols)                           */
   float operand_scales[5];   /* fp16 operand scales of G, P~, H, Q and the
                                 direct form's X (plan-wide; all 1 on the fp32
                                 path); see muon_plan                         */

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmuon.so")
-SOURCES = ["gemm.hip", "gemm_dma.hip", "rr_fused.hip", "elementwise.hip", "muon_api.cpp"]
+SOURCES = ["gemm.hip", "gemm_dma.hip", "rr_fused.hip", "direct_fused.hip", "elementwise.hip", "muon_api.cpp"]
 ARCH = os.environ.get("MUON_OFFLOAD_ARCH", "gfx950")
 
 

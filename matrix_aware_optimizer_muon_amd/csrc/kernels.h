@@ -91,6 +91,27 @@ struct RrFusedParams {
 };
 hipError_t launch_rr_fused(const RrFusedParams& p, int nmat, hipStream_t s);
 
+// The whole direct-form iteration and the weight update in one launch for
+// buckets of padded squares, r_pad = c_pad in {128, 256}, on the 16-bit path
+// (direct_fused.hip): X^ (fp16, scaled by sX) in both layouts from the cast
+// pass; the pair buffers alternate per iteration (the r x r intermediates
+// stay in LDS).
+struct DirectFusedParams {
+  const MatPtrs* table;    // chunk's first entry (W, O)
+  void* Xn[2];             // natural layout X^, per iteration parity
+  void* Xt[2];             // transposed layout
+  int64_t x_stride;        // elements between matrices in Xn / Xt
+  int rp;                  // r_pad = c_pad
+  int m, n;                // true sizes (m <= n)
+  float a, b, c;
+  float sX, sG, sP;
+  float syrk_scale;        // 1 / sX^2
+  int N;
+  float decay, step;
+  int vec;                 // W / O rows allow 16-byte access
+};
+hipError_t launch_direct_fused(const DirectFusedParams& p, int nmat, hipStream_t s);
+
 // Write up to kTableChunk pointer-table entries, passed by value as kernel
 // arguments, to dst[0 .. count) (the allocation-free step uploads its table
 // this way: no staging buffer and no host-memory copy).

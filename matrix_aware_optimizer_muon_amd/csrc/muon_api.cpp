@@ -148,6 +148,7 @@ struct Bucket {
   bool dma;  // 256-tile direct-to-LDS path with fp16-only r x r buffers
   bool direct;  // direct form (eq. (2) on X)
   bool fused_rr;  // Gram form with the whole r x r recursion in one launch
+  bool fused_direct;  // direct form: every iteration and the update in one launch
   int bt;
   int group = 0, xcd = 0, waves = 0;  // 256-wide kernels' hint values (0: rule)
   int first, count;  // range in plan order
@@ -663,9 +664,10 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
         if (B.direct) {
           Xn2 = take(xbytes);
           Xt2 = take(xbytes);
-          Gh = take(h16b);
-          Ph = take(h16b);
-          if (!B.dma) Gf = (float*)take(f32b);
+          // the one-launch direct form keeps its r x r matrices in LDS
+          Gh = B.fused_direct ? nullptr : take(h16b);
+          Ph = B.fused_direct ? nullptr : take(h16b);
+          if (!B.dma && !B.fused_direct) Gf = (float*)take(f32b);
         } else if (f32path) {
           Gh = Gf;
           Ph = take(f32b);
@@ -776,6 +778,36 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
           if (st != MUON_OK) return st;
           void* Xn[2] = {Xnat, Xn2};
           void* Xt[2] = {Xtr, Xt2};
+          if (B.fused_direct) {
+            DirectFusedParams dp{};
+            dp.table = d_table + ch.first;
+            dp.Xn[0] = Xn[0];
+            dp.Xn[1] = Xn[1];
+            dp.Xt[0] = Xt[0];
+            dp.Xt[1] = Xt[1];
+            dp.x_stride = x_stride;
+            dp.rp = (int)B.r_pad;
+            dp.m = (int)B.m;
+            dp.n = (int)B.n;
+            dp.a = hp.a;
+            dp.b = hp.b;
+            dp.c = hp.c;
+            dp.sX = p->scales.sX;
+            dp.sG = p->scales.sG;
+            dp.sP = p->scales.sP;
+            dp.syrk_scale = 1.0f / (p->scales.sX * p->scales.sX);
+            dp.N = N;
+            dp.decay = decay;
+            dp.step = step_c;
+            dp.vec = vec;
+            // per iteration: X^ read twice (both layouts), the a X term, X'
+            // written in both layouts (the r x r matrices stay in LDS)
+            st = timed(p, stream, MUON_K_XUPD, N * (r2 * cc + r3 + 2.0 * r2 * cc) * nm,
+                       N * 10.0 * rcf * nm,
+                       [&] { return launch_direct_fused(dp, nm, stream); });
+            if (st != MUON_OK) return st;
+            continue;
+          }
           g.xkind = 1;
           g.syrk_scale = 1.0f / (p->scales.sX * p->scales.sX);
           g.sX = p->scales.sX;
@@ -1134,6 +1166,10 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       const int64_t rr = B.r_pad * B.r_pad;
       B.dma = !f32path && B.bt == 256;
       B.fused_rr = !f32path && !B.dma && !B.direct && B.r_pad <= 128;
+      // padded squares of 128 or 256 on the small-tile 16-bit path: the
+      // direct form's 3 N products and the update in one launch
+      B.fused_direct = !f32path && !B.dma && B.direct && !B.transposed && B.r_pad == B.c_pad &&
+                       (B.r_pad == 128 || B.r_pad == 256);
       // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
       // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
       // the 256-tile path keeps only the fp16 copies
@@ -1144,7 +1180,8 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       const int64_t xb = (int64_t)align256((size_t)(B.r_pad * B.c_pad * xes));
       // direct form: X and X^T twice (double buffered) plus A and P~ in fp16
       // (and A in fp32 for the small-tile kernel's quintic epilogue)
-      B.scratch_per_mat = B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) +
+      B.scratch_per_mat = B.fused_direct ? 4 * xb
+                        : B.direct ? 4 * xb + 2 * (int64_t)align256((size_t)(rr * 2)) +
                                          (B.dma ? 0 : (int64_t)align256((size_t)(rr * 4)))
                                    : 2 * xb + rr_bytes;
       int64_t per_chunk = std::max<int64_t>(1, cap / B.scratch_per_mat);
@@ -1258,7 +1295,7 @@ muon_status muon_plan_bucket_info(muon_plan_t plan, int64_t index, muon_bucket_i
   info->tile = B.bt;
   info->formulation = B.direct ? MUON_FORM_DIRECT : MUON_FORM_GRAM;
   info->transposed = B.transposed ? 1 : 0;
-  info->fused_recursion = B.fused_rr ? 1 : 0;
+  info->fused_recursion = (B.fused_rr || B.fused_direct) ? 1 : 0;
   const NsScales& sc = plan->scales;
   const float scales[5] = {sc.sG, sc.sP, sc.sH, sc.sQ, sc.sX};
   std::memcpy(info->operand_scales, scales, sizeof scales);

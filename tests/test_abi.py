@@ -101,13 +101,29 @@ def test_fused_recursion_rule():
     # below 256 and r padded to <= 128
     b2 = {tuple(b["shape"]): b for b in L.Plan(WL.config(2).shapes).buckets()}
     assert b2[(128, 3584)]["fused"] and b2[(128, 3584)]["tile"] == 64
-    assert not b2[(256, 256)]["fused"]  # square: direct form
+    # square: the direct form, as one launch (padded squares of 128 / 256)
+    assert b2[(256, 256)]["fused"] and b2[(256, 256)]["formulation"] == "direct"
     assert not any(b["fused"] for b in L.Plan(WL.config(3).shapes).buckets())
     assert not L.Plan([(128, 3584)], ns_dtype="f32").buckets()[0]["fused"]  # fp32 path
     assert L.Plan([(3584, 64)]).buckets()[0]["fused"]  # tall: r = 64
     assert not L.Plan([(200, 900)]).buckets()[0]["fused"]  # r_pad = 256
     assert L.Plan([(64, 80)]).buckets()[0]["fused"]  # c > 1.125 r: Gram form
     assert not L.Plan([(64, 72)]).buckets()[0]["fused"]  # near-square: direct form
+
+
+def test_fused_direct_rule():
+    # the one-launch direct form: padded squares of 128 or 256 (rows <= cols)
+    # on the small-tile 16-bit path
+    def b(shapes, **kw):
+        return L.Plan(shapes, **kw).buckets()[0]
+    assert b([(256, 256)] * 64)["formulation"] == "direct" and b([(256, 256)] * 64)["fused"]
+    assert b([(120, 128)])["fused"] and b([(250, 256)])["fused"] and b([(100, 110)])["fused"]
+    assert not b([(240, 270)])["fused"]  # direct, but c_pad 320 != r_pad 256
+    assert not b([(64, 64)])["fused"]  # r_pad 64
+    assert not b([(256, 256)], ns_dtype="f32")["fused"]  # fp32 path
+    assert not b([(3584, 3584)] * 2)["fused"]  # 256-wide tiles
+    assert not b([(256, 256)], hints={(256, 256): {"tile": 256}})["fused"]
+    assert b([(256, 256)], hints={(256, 256): {"tile": 128}})["fused"]
 
 
 def _scales(n, ns_dtype="bf16", **coef):

@@ -57,6 +57,42 @@ def test_direct_tile_widths(tile, steps):
         assert rel(Wg[i], W_epi) <= 1e-5, (tile, steps, shapes[i])
 
 
+# The one-launch direct form (padded squares of 128 or 256 on small tiles):
+# both sizes, ragged extents inside the padding, N = 1, 2, 5 (the iterations
+# alternate the X buffer pair), the update epilogue and the O output.
+@pytest.mark.parametrize("steps", [1, 2, 5])
+def test_fused_direct_form(steps):
+    from matrix_aware_optimizer_muon_amd import default_hparams
+    hp = default_hparams()
+    hp.ns_steps = steps
+    shapes = [(256, 256)] * 3 + [(250, 256), (120, 128), (128, 128), (100, 110)]
+    W, M, G = seeded(shapes, 140 + steps, mscale=1e-3)
+    (Wg, Mg, Og), plan = run(shapes, W, M, G, LR, WD, "f32", "bf16", hp=hp)
+    assert all(b["formulation"] == "direct" and b["fused"] for b in plan.buckets()), plan.buckets()
+    ohp = OR.Hyper(ns_steps=steps)
+    for i, (m, n) in enumerate(shapes):
+        Wo, Mo, Oo = OR.muon_step(W[i], M[i], G[i], LR, WD, hp=ohp, form="direct")
+        e = rel(Og[i], Oo)
+        assert e <= 2e-2, (steps, shapes[i], e)
+        assert rel(Mg[i], Mo) <= 1e-6
+        W_epi = OR.apply_update(W[i], Og[i], LR, WD, OR.update_scale(m, n))
+        assert rel(Wg[i], W_epi) <= 1e-5, (steps, shapes[i])
+
+
+def test_fused_direct_is_deterministic_and_matches_the_launch_sequence():
+    # same inputs twice: bit-identical; against the same products launched
+    # one by one on 256-wide tiles (hint), close to the products' rounding
+    shapes = [(256, 256)] * 4
+    W, M, G = seeded(shapes, 151, mscale=1e-3)
+    (W1, _, O1), p1 = run(shapes, W, M, G, LR, WD)
+    (W2, _, O2), _ = run(shapes, W, M, G, LR, WD)
+    (_, _, O3), p3 = run(shapes, W, M, G, LR, WD, hints={(256, 256): {"tile": 256}})
+    assert p1.buckets()[0]["fused"] and not p3.buckets()[0]["fused"]
+    for i in range(len(shapes)):
+        assert np.array_equal(W1[i], W2[i]) and np.array_equal(O1[i], O2[i])
+        assert rel(O1[i], O3[i]) <= 5e-3, rel(O1[i], O3[i])
+
+
 def test_direct_small_tiles_match_large_tiles_closely():
     # the same iteration on the two kernels: both within the bar of the
     # oracle and close to each other (the a X term and A's b-term differ in
