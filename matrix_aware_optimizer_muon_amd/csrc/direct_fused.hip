@@ -10,7 +10,8 @@
 //
 // Arithmetic (the small-tile kernels' direct-form epilogues, gemm.hip, with
 // the same operand formats and power-of-two scales; X^ = X sX in fp16, both
-// layouts, from the cast pass), per iteration
+// layouts, cast by the workgroup itself from the prep pass's bf16 U and the
+// norm), per iteration
 //   SYRK  A^ = fp16(acc sG / sX^2)                    (A = X X^T)
 //   POLY  P~ = b A^ / sG + c acc / sG^2,  P^ = fp16(P~ sP)
 //   XUPD  X'^ = fp16(a X^ + acc / sP), both layouts
@@ -160,6 +161,34 @@ __global__ void __launch_bounds__(1024, 1) direct_fused_kernel(const DirectFused
       if (st + 2 < NST) issue(st + 2);
     }
   };
+
+  // X^ = fp16(U sX / ||U||) in place over both layouts of U (bf16 from the
+  // prep pass; the cast pass of the launch sequence, done here by the
+  // matrix's own workgroup)
+  {
+    // every load of both layouts in flight at once: U was written by the
+    // prep pass well before and comes from memory, and one chunk at a time
+    // paid that latency 2 RP^2 / 8192 times per thread
+    constexpr int CPT = RP * RP / 8 / 1024;  // 16-byte chunks per thread per layout
+    const float sc = p.inv_norm[mat] * p.sX;
+    uint32_t* bl[2] = {(uint32_t*)((uint16_t*)p.Xn[0] + xo), (uint32_t*)((uint16_t*)p.Xt[0] + xo)};
+    u32x4 v[2][CPT];
+#pragma unroll
+    for (int lay = 0; lay < 2; ++lay)
+#pragma unroll
+      for (int t = 0; t < CPT; ++t) v[lay][t] = *(const u32x4*)(bl[lay] + 4 * (tid + 1024 * t));
+#pragma unroll
+    for (int lay = 0; lay < 2; ++lay)
+#pragma unroll
+      for (int t = 0; t < CPT; ++t) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[lay][t][q] = df_h2(__uint_as_float(v[lay][t][q] << 16) * sc,
+                               __uint_as_float(v[lay][t][q] & 0xffff0000u) * sc);
+        *(u32x4*)(bl[lay] + 4 * (tid + 1024 * t)) = v[lay][t];
+      }
+    __syncthreads();
+  }
 
   // accumulator element e of block (i, j): row wr*BS + i*16 + 4*q4 + e,
   // column wc*BS + j*16 + c16

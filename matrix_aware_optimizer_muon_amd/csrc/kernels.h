@@ -93,13 +93,14 @@ hipError_t launch_rr_fused(const RrFusedParams& p, int nmat, hipStream_t s);
 
 // The whole direct-form iteration and the weight update in one launch for
 // buckets of padded squares, r_pad = c_pad in {128, 256}, on the 16-bit path
-// (direct_fused.hip): X^ (fp16, scaled by sX) in both layouts from the cast
-// pass; the pair buffers alternate per iteration (the r x r intermediates
-// stay in LDS).
+// (direct_fused.hip): U (bf16, both layouts, from the prep pass) is cast to
+// X^ (fp16, scaled by sX / ||U||) in place; the pair buffers alternate per
+// iteration (the r x r intermediates stay in LDS).
 struct DirectFusedParams {
   const MatPtrs* table;    // chunk's first entry (W, O)
-  void* Xn[2];             // natural layout X^, per iteration parity
-  void* Xt[2];             // transposed layout
+  const float* inv_norm;   // 1 / ||U|| per matrix of the chunk
+  void* Xn[2];             // natural layout, per iteration parity (Xn[0]: U
+  void* Xt[2];             // in bf16 on entry, cast in place); transposed
   int64_t x_stride;        // elements between matrices in Xn / Xt
   int rp;                  // r_pad = c_pad
   int m, n;                // true sizes (m <= n)

@@ -765,22 +765,12 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
         };
 
         if (B.direct) {
-          // X0 = U / ||U||, in place, as fp16 scaled by sX
-          XcastParams xc{};
-          xc.Xn = Xnat;
-          xc.Xt = Xtr;
-          xc.x_stride = x_stride;
-          xc.elems = B.m_pad * B.n_pad;
-          xc.inv_norm = d_inv + ch.first;
-          xc.sx = p->scales.sX;
-          st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
-                     [&] { return launch_xcast(xc, nm, stream); });
-          if (st != MUON_OK) return st;
           void* Xn[2] = {Xnat, Xn2};
           void* Xt[2] = {Xtr, Xt2};
           if (B.fused_direct) {
             DirectFusedParams dp{};
             dp.table = d_table + ch.first;
+            dp.inv_norm = d_inv + ch.first;
             dp.Xn[0] = Xn[0];
             dp.Xn[1] = Xn[1];
             dp.Xt[0] = Xt[0];
@@ -801,13 +791,24 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
             dp.step = step_c;
             dp.vec = vec;
             // per iteration: X^ read twice (both layouts), the a X term, X'
-            // written in both layouts (the r x r matrices stay in LDS)
+            // written in both layouts (the r x r matrices stay in LDS); the
+            // cast reads and writes both layouts once
             st = timed(p, stream, MUON_K_XUPD, N * (r2 * cc + r3 + 2.0 * r2 * cc) * nm,
-                       N * 10.0 * rcf * nm,
-                       [&] { return launch_direct_fused(dp, nm, stream); });
+                       (N * 10.0 + 8.0) * rcf * nm, [&] { return launch_direct_fused(dp, nm, stream); });
             if (st != MUON_OK) return st;
             continue;
           }
+          // X0 = U / ||U||, in place, as fp16 scaled by sX
+          XcastParams xc{};
+          xc.Xn = Xnat;
+          xc.Xt = Xtr;
+          xc.x_stride = x_stride;
+          xc.elems = B.m_pad * B.n_pad;
+          xc.inv_norm = d_inv + ch.first;
+          xc.sx = p->scales.sX;
+          st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
+                     [&] { return launch_xcast(xc, nm, stream); });
+          if (st != MUON_OK) return st;
           g.xkind = 1;
           g.syrk_scale = 1.0f / (p->scales.sX * p->scales.sX);
           g.sX = p->scales.sX;
