@@ -20,7 +20,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 # The kernels and the planner (which decides the launches, tiles and forms
 # whose traffic a profile records).
-KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/rr_fused.hip", "csrc/gemm_epilogue.hpp",
+KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/rr_fused.hip", "csrc/direct_fused.hip",
+                  "csrc/gemm_epilogue.hpp",
                   "csrc/elementwise.hip", "csrc/common.hpp", "csrc/kernels.h",
                   "csrc/muon_api.cpp")
 EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final", 5: "xupd", 6: "xupd"}
@@ -40,7 +41,8 @@ def kernel_class(name: str) -> str | None:
         r"gemm_kernel<(\d+), \d+, (\d+)", name)
     if m:
         return EPI_CLASS[int(m.group(2))]
-    for key, cls in (("rr_fused_kernel", "poly"), ("xcast_kernel", "xcast"), ("wupd_kernel", "wupd"),
+    for key, cls in (("rr_fused_kernel", "poly"), ("direct_fused_kernel", "xupd"),
+                     ("xcast_kernel", "xcast"), ("wupd_kernel", "wupd"),
                      ("prep_tile_kernel", "prep"), ("norm_finalize", "norm"),
                      ("rownorm_rows", "rownorm"), ("rownorm_colsum", "colsum"),
                      ("rownorm_colfinal", "colfinal"), ("rownorm_colapply", "colapply")):
