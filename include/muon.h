@@ -123,7 +123,9 @@ typedef enum { MUON_FORM_AUTO = 0, MUON_FORM_GRAM = 1, MUON_FORM_DIRECT = 2 } mu
  *                1..65536 = runs of that many (rule: 32).
  *   waves:       wave64s per workgroup of the SYRK and final-product
  *                launches: 8 (rule; two per SIMD, 128 x 64 each) or 4 (one
- *                per SIMD, 128 x 128 each).  The other products always use 8.
+ *                per SIMD, 128 x 128 each).  The other products always use
+ *                8, and so does the final product of buckets with rows <=
+ *                cols (it reads X0 across K).
  * Hints whose shape matches no planned matrix are ignored.  Two hints for
  * the same shape, or a value outside these ranges, give
  * MUON_ERR_INVALID_ARGUMENT; combinations the kernels do not provide give

@@ -4,8 +4,9 @@
 //             (Nesterov remark); partial sums of ||U||_F^2; U stored in the
 //             Newton-Schulz operand type both as is and transposed through
 //             LDS, zero padded to the GEMM tile: one copy is X0 = O(U)
-//             ("Scaling Muon for DiT" 3.1), the other X0^T.  One read of M
-//             and G, one write of M and of the two copies.
+//             ("Scaling Muon for DiT" 3.1), the other X0^T (left out when
+//             the products read X0 across K).  One read of M and G, one
+//             write of M and of the copies.
 // finalize:   deterministic (fixed order, fp64) reduction of the partial sums
 //             to 1/||U||_F per matrix (0 when the norm is 0, NaN when the sum
 //             is NaN or infinite).
@@ -154,32 +155,36 @@ __global__ void __launch_bounds__(256) prep_tile_kernel(const PrepParams p, int 
                           (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16)};
         __builtin_nontemporal_store(pk, (u32x2*)((uint16_t*)p.X + xo));
       }
-      tile[rl][c4 + 0] = u.x;
-      tile[rl][c4 + 1] = u.y;
-      tile[rl][c4 + 2] = u.z;
-      tile[rl][c4 + 3] = u.w;
+      if (p.XT) {
+        tile[rl][c4 + 0] = u.x;
+        tile[rl][c4 + 1] = u.y;
+        tile[rl][c4 + 2] = u.z;
+        tile[rl][c4 + 3] = u.w;
+      }
     }
   }
-  __syncthreads();
-  {
-    const int jl = t >> 2;        // transposed row within the tile
-    const int i0 = (t & 3) * 16;  // 16 consecutive transposed columns
-    const size_t xo = xbase + (size_t)(tj * 64 + jl) * p.m_pad + ti * 64 + i0;
-    if (XF32) {
-      float* xp = (float*)p.XT + xo;
+  if (p.XT) {  // (uniform) the transposed copy, unless the products read U across K
+    __syncthreads();
+    {
+      const int jl = t >> 2;        // transposed row within the tile
+      const int i0 = (t & 3) * 16;  // 16 consecutive transposed columns
+      const size_t xo = xbase + (size_t)(tj * 64 + jl) * p.m_pad + ti * 64 + i0;
+      if (XF32) {
+        float* xp = (float*)p.XT + xo;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        nt_store4(xp + 4 * q, make_float4(tile[i0 + 4 * q][jl], tile[i0 + 4 * q + 1][jl],
-                                          tile[i0 + 4 * q + 2][jl], tile[i0 + 4 * q + 3][jl]));
-    } else {
-      uint32_t w[8];
+        for (int q = 0; q < 4; ++q)
+          nt_store4(xp + 4 * q, make_float4(tile[i0 + 4 * q][jl], tile[i0 + 4 * q + 1][jl],
+                                            tile[i0 + 4 * q + 2][jl], tile[i0 + 4 * q + 3][jl]));
+      } else {
+        uint32_t w[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        w[q] = (uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q][jl]) |
-               ((uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q + 1][jl]) << 16);
-      u32x4* xp = (u32x4*)((uint16_t*)p.XT + xo);
-      __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, xp);
-      __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, xp + 1);
+        for (int q = 0; q < 8; ++q)
+          w[q] = (uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q][jl]) |
+                 ((uint32_t)f32_to_bf16_bits(tile[i0 + 2 * q + 1][jl]) << 16);
+        u32x4* xp = (u32x4*)((uint16_t*)p.XT + xo);
+        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, xp);
+        __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, xp + 1);
+      }
     }
   }
   const float tot = block_sum<256>(ss, red);
@@ -513,9 +518,10 @@ hipError_t launch_write_table(const TableChunk& t, MatPtrs* dst, hipStream_t s) 
 __global__ void __launch_bounds__(256) xcast_kernel(const XcastParams p) {
   const int64_t per_buf = p.elems / 8;
   const int64_t blocks_per_buf = (per_buf + 255) / 256;
+  const int nbuf = p.Xt ? 2 : 1;
   const int64_t b = blockIdx.x;
-  const int mat = (int)(b / (2 * blocks_per_buf));
-  const int64_t rem = b - (int64_t)mat * 2 * blocks_per_buf;
+  const int mat = (int)(b / (nbuf * blocks_per_buf));
+  const int64_t rem = b - (int64_t)mat * nbuf * blocks_per_buf;
   const int which = rem >= blocks_per_buf ? 1 : 0;
   const int64_t chunk = (rem - which * blocks_per_buf) * 256 + threadIdx.x;
   if (chunk >= per_buf) return;
@@ -533,7 +539,7 @@ __global__ void __launch_bounds__(256) xcast_kernel(const XcastParams p) {
 
 hipError_t launch_xcast(const XcastParams& p, int nmat, hipStream_t s) {
   if (p.elems % 8) return hipErrorInvalidValue;
-  const uint64_t blocks = (uint64_t)nmat * 2 * (uint64_t)((p.elems / 8 + 255) / 256);
+  const uint64_t blocks = (uint64_t)nmat * (p.Xt ? 2 : 1) * (uint64_t)((p.elems / 8 + 255) / 256);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   hipLaunchKernelGGL(xcast_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, p);

@@ -65,6 +65,25 @@ __device__ __forceinline__ int slot16(int c, int q) {
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// K-major operand stages (32 rows of k, 512 bytes = the tile's 256 columns
+// each): 16-byte chunk c of row k is stored at chunk c ^ swzk(k), an even
+// XOR (aligned chunk pairs stay pairs) from row bits 0, 1 and 3.  A
+// transposing read instruction reads 16 rows (bits 0-1 and 3-4 vary) of 32
+// bytes each: eight distinct pair positions, so two rows per bank group.
+__device__ __forceinline__ int swzk(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
+
+// gfx950 transposing LDS read of 16-bit elements: in each group of 16 lanes,
+// lane 4e + i/4 of the group supplies the 64-bit row whose element i % 4
+// lane i receives as its element e.  With lane i addressing row i / 4 and
+// columns 4 (i % 4) .. +3 of a 4 x 16 block, lane i receives column i of
+// the block's 4 rows: four consecutive k of one n, half a 16x16x32 MFMA
+// operand fragment.
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+__device__ __forceinline__ uint2 tr_read(const char* p) {
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)p));
+}
+
 template <int KIND>
 __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x4& c) {
   if constexpr (KIND == 0) {
@@ -143,7 +162,10 @@ __device__ __forceinline__ uint2 q_from_p(uint2 pv, float inv_sp, const GemmPara
 
 // NW = 4: waves in 2 x 2, each 128 x 128 (8 x 8 MFMA blocks, one wave per SIMD)
 // NW = 8: waves in 2 x 4, each 128 x 64 (8 x 4 MFMA blocks, two waves per SIMD)
-template <int KIND, int EPI, int NW>
+// BKN: the B operand is stored K-major (rows of k, ld ldb, the tile's n
+// contiguous: X itself instead of a transposed copy); its stages hold 32
+// rows of 512 bytes and its fragments come from transposing reads.
+template <int KIND, int EPI, int NW, bool BKN = false>
 __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p) {
   constexpr int NT = 64 * NW;                    // threads
   constexpr int WGN = NW / 2;                    // waves along N
@@ -194,7 +216,14 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     const int row = (wave * DMA_PER_OP + i) * 16 + (lane >> 2);
     const int ch = (lane & 3) ^ swz4(row);
     srcA[i] = Ab + ((size_t)(row0A + row) * p.lda + ch * 8) * 2;
-    srcB[i] = Bb + ((size_t)(row0B + row) * p.ldb + ch * 8) * 2;
+    if constexpr (BKN) {
+      // two 512-byte rows of k per instruction; lane L -> row L >> 5,
+      // physical chunk L & 31, which holds logical chunk (L & 31) ^ swzk
+      const int krow = (wave * DMA_PER_OP + i) * 2 + (lane >> 5);
+      srcB[i] = Bb + ((size_t)krow * p.ldb + row0B + (((lane & 31) ^ swzk(krow)) << 3)) * 2;
+    } else {
+      srcB[i] = Bb + ((size_t)(row0B + row) * p.ldb + ch * 8) * 2;
+    }
   }
   // One 1-KB DMA instruction (q = 0..DPS-1: A blocks, then B blocks) of
   // stage ks into ring buffer `buf`.  Stages past the last one re-read the
@@ -202,10 +231,11 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   // issues the same number of DMAs and the vmcnt bookkeeping is constant.
   const int nk = p.Kdim / DBK;
   auto dma = [&](int q, int buf, int ks) {
-    const int koff = (ks < nk ? ks : nk - 1) * ROWB;
+    const int kc = ks < nk ? ks : nk - 1;
     char* sb = smem + buf * STAGEB + (q >= DMA_PER_OP ? OPB : 0) +
                (wave * DMA_PER_OP + (q % DMA_PER_OP)) * 1024;
-    const char* src = (q < DMA_PER_OP ? srcA[q] : srcB[q - DMA_PER_OP]) + koff;
+    const char* src = q < DMA_PER_OP ? srcA[q] + kc * ROWB
+                                     : srcB[q - DMA_PER_OP] + (BKN ? (size_t)kc * DBK * p.ldb * 2 : (size_t)kc * ROWB);
     __builtin_amdgcn_global_load_lds((gbl_ptr_t*)src, (lds_ptr_t*)sb, 16, 0, 0);
   };
 
@@ -216,6 +246,23 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   const int offA = ra0 * ROWB + ((q4 ^ swz4(ra0)) << 4);
   const int offB = OPB + rb0 * ROWB + ((q4 ^ swz4(rb0)) << 4);
   auto frag = [&](const char* sb, int off, int f) { return *(const u32x4*)(sb + off + f * 16 * ROWB); };
+  // K-major B: block f's fragment is two transposing reads (k 8 q4 .. +3 and
+  // +4 .. +7); lane (q4, c16) addresses row 8 q4 + c16 / 4 (+ 4) and
+  // columns wn WTN + 16 f + 4 (c16 % 4) .. +3.  swzk is the same for both
+  // rows (bit 2 does not enter it)
+  const int kb0 = 8 * q4 + (c16 >> 2);
+  const int offBK = OPB + kb0 * 512 + ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8;
+  const int swB = swzk(kb0) << 4;
+  auto fragB = [&](const char* sb, int f) -> u32x4 {
+    if constexpr (BKN) {
+      const int co = (((wn * WTN) >> 3) + 2 * f) << 4;
+      const char* a = sb + offBK + (co ^ swB);
+      const uint2 lo = tr_read(a), hi = tr_read(a + 4 * 512);
+      return u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      return frag(sb, offB, f);
+    }
+  };
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -258,7 +305,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
   for (int f = 0; f < FM / 2; ++f) fa[f] = frag(smem, offA, f);
 #pragma unroll
-  for (int f = 0; f < FN; ++f) fb0[f] = frag(smem, offB, f);
+  for (int f = 0; f < FN; ++f) fb0[f] = fragB(smem, f);
 
   // one K step; fb holds this stage's B fragments, fbn receives the next's
   auto step = [&](int kt, u32x4* fb, u32x4* fbn) {
@@ -279,8 +326,19 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
       for (int j = 0; j < FN; ++j) {
         const int rb = wn * WTN + j * 16 + c16;
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-          hv[j][ii] = *(const u32x4*)(sb + OPB + rb * ROWB + (((2 * ii + (q4 >> 1)) ^ swz4(rb)) << 4));
+        for (int ii = 0; ii < 2; ++ii) {
+          if constexpr (BKN) {
+            // rows 16 ii + 4 q4 + c16 / 4 of the stage: lane c16 receives
+            // X(m .. m + 3, n) for its own 4 rows m and column n (half 0)
+            const int kr = 16 * ii + 4 * q4 + (c16 >> 2);
+            const int co = (((wn * WTN) >> 3) + 2 * j) << 4;
+            const uint2 t = tr_read(sb + OPB + kr * 512 + ((c16 & 3) >> 1) * 16 + (c16 & 1) * 8 +
+                                    (co ^ (swzk(kr) << 4)));
+            hv[j][ii] = u32x4{t.x, t.y, 0u, 0u};
+          } else {
+            hv[j][ii] = *(const u32x4*)(sb + OPB + rb * ROWB + (((2 * ii + (q4 >> 1)) ^ swz4(rb)) << 4));
+          }
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -311,8 +369,8 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const u32x4 h = hv[j][ii];
-          const uint32_t w0 = (q4 & 1) ? h[2] : h[0];
-          const uint32_t w1 = (q4 & 1) ? h[3] : h[1];
+          const uint32_t w0 = (!BKN && (q4 & 1)) ? h[2] : h[0];
+          const uint32_t w1 = (!BKN && (q4 & 1)) ? h[3] : h[1];
           gx[ii][j][0] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)w0);
           gx[ii][j][1] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16));
           gx[ii][j][2] = gam * (float)__builtin_bit_cast(_Float16, (uint16_t)w1);
@@ -333,7 +391,7 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
 #pragma unroll
       for (int f = 0; f < FM / 2; ++f) fa[f] = frag(sn, offA, f);
 #pragma unroll
-      for (int f = 0; f < FN; ++f) fbn[f] = frag(sn, offB, f);
+      for (int f = 0; f < FN; ++f) fbn[f] = fragB(sn, f);
     }
     __builtin_amdgcn_sched_barrier(0);
     // second half (block rows 4..7), with the first half of the refill of
@@ -505,9 +563,10 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
     // k of a half takes chunks 2k and 2k + 1 (tile rows 8k..8k+7), which sit
     // in slots s and s ^ 1 (s = slot16(c, 2k)) of one aligned 16-byte pair,
     // and stores them as eight consecutive elements of mirrored row c
+    // (X' kept in one layout: no transposed block)
     constexpr int CPW = 256 / NW;  // mirrored rows per wave
 #pragma unroll 4
-    for (int it = 0; it < CPW / 2; ++it) {
+    for (int it = 0; it < ((EPI != EPI_XUPD || p.Yt) ? CPW / 2 : 0); ++it) {
       const int jc = wave * CPW + 2 * it + (lane >> 5);
       const int k = lane & 31;
       const int sl = slot16(jc, 2 * k);
@@ -525,13 +584,13 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   }
 }
 
-template <int KIND, int EPI, int NW>
+template <int KIND, int EPI, int NW, bool BKN = false>
 static hipError_t launch_dma_one(const GemmParams& p, int nmat, hipStream_t s) {
   const uint64_t blocks = (uint64_t)nmat * p.tiles_per_prod * p.products;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
   if (p.Kdim % DBK != 0 || p.Mdim % DT != 0 || p.Ndim % DT != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_dma_kernel<KIND, EPI, NW>), dim3((uint32_t)blocks), dim3(64 * NW), 0, s,
+  hipLaunchKernelGGL((gemm_dma_kernel<KIND, EPI, NW, BKN>), dim3((uint32_t)blocks), dim3(64 * NW), 0, s,
                      p);
   return hipGetLastError();
 }
@@ -543,6 +602,14 @@ hipError_t launch_gemm_dma(const GemmParams& p, int epi, int nmat, hipStream_t s
   const bool w4 = p.waves == 4;
   if (p.waves != 0 && p.waves != 4 && p.waves != 8) return hipErrorInvalidValue;
   if (w4 && epi != EPI_SYRK && epi != EPI_FINAL) return hipErrorInvalidValue;
+  if (p.b_kn) {  // K-major B operand: the final product and the direct form's X'
+    switch (epi) {
+      case EPI_XUPD: return launch_dma_one<1, EPI_XUPD, 8, true>(p, nmat, s);
+      case EPI_XFINAL: return launch_dma_one<1, EPI_XFINAL, 8, true>(p, nmat, s);
+      case EPI_FINAL: return launch_dma_one<0, EPI_FINAL, 8, true>(p, nmat, s);  // (8 waves)
+    }
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case EPI_SYRK:
       if (p.xkind) return w4 ? launch_dma_one<1, EPI_SYRK, 4>(p, nmat, s) : launch_dma_one<1, EPI_SYRK, 8>(p, nmat, s);

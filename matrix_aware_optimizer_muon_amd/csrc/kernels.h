@@ -40,6 +40,9 @@ struct GemmParams {
                            // (0: 8 for full grids, 4 for triangular ones)
   int waves;               // 256-wide kernels: 8, or 4 (SYRK and the final product)
   int prod_base;           // epilogue product index of the first product
+  int b_kn;                // 256-wide kernels: B stored K-major (rows of k, ld ldb,
+                           // the tile's n contiguous); final product and
+                           // EPI_XUPD / EPI_XFINAL only
   // r x r recursion buffers (fp32 master copies and MFMA operand copies)
   float* Gf;
   float* Qf_src;
@@ -67,7 +70,8 @@ struct GemmParams {
   float syrk_scale;        // SYRK result scale; 0: 1/||U||^2
   float sX;                // fp16 scale of X
   void* Yn;                // EPI_XUPD: X' natural layout (r_pad x c_pad, ld ldyn)
-  void* Yt;                // EPI_XUPD: X' transposed (c_pad x r_pad, ld ldyt)
+  void* Yt;                // EPI_XUPD: X' transposed (c_pad x r_pad, ld ldyt); null on
+                           // the 256-wide kernels: X' in the natural layout only
   int ldyn, ldyt;
   int64_t y_stride;        // elements between matrices (both)
   const void* Xid;         // small-tile EPI_XUPD / EPI_XFINAL: X in the layout
@@ -131,7 +135,7 @@ struct PrepParams {
   float mu;
   int nesterov;
   void* X;                 // U, natural layout m_pad x n_pad (matrix 0 of the chunk)
-  void* XT;                // U^T, n_pad x m_pad
+  void* XT;                // U^T, n_pad x m_pad (null: not written)
   int64_t x_stride;        // elements between matrices (both copies)
   float* partials;         // [nmat][blocks_per_mat]
   int blocks_per_mat;
@@ -160,7 +164,7 @@ struct RowNormParams {
 // chunk (natural m_pad x n_pad and transposed n_pad x m_pad, bf16 on entry).
 struct XcastParams {
   void* Xn;                // natural layout, matrix 0 of the chunk
-  void* Xt;                // transposed layout
+  void* Xt;                // transposed layout (null: one layout)
   int64_t x_stride;        // elements between matrices (both buffers)
   int64_t elems;           // m_pad * n_pad (a multiple of 8)
   const float* inv_norm;   // [nmat]

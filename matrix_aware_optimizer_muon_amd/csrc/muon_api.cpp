@@ -149,6 +149,10 @@ struct Bucket {
   bool direct;  // direct form (eq. (2) on X)
   bool fused_rr;  // Gram form with the whole r x r recursion in one launch
   bool fused_direct;  // direct form: every iteration and the update in one launch
+  bool one_layout;    // 256-wide tiles, rows <= cols: U / X kept in the natural
+                      // layout only; the products that read it across K (the
+                      // final product, the direct form's X') take it K-major
+                      // through transposing LDS reads instead of a copy
   int bt;
   int group = 0, xcd = 0, waves = 0;  // 256-wide kernels' hint values (0: rule)
   int first, count;  // range in plan order
@@ -719,13 +723,13 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
         pp.mu = hp.momentum;
         pp.nesterov = hp.nesterov;
         pp.X = Xnat;
-        pp.XT = Xtr;
+        pp.XT = B.one_layout ? nullptr : Xtr;
         pp.x_stride = x_stride;
         pp.partials = d_part;
         pp.blocks_per_mat = B.prep_blocks;
         pp.inv_norm = d_inv + ch.first;
         const double elems = (double)B.m * B.n * nm;
-        st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + 2 * xes), [&] {
+        st = timed(p, stream, MUON_K_PREP, 0.0, elems * (4 + (gbf16 ? 2 : 4) + 4 + (B.one_layout ? 1 : 2) * xes), [&] {
           return launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream);
         });
         if (st != MUON_OK) return st;
@@ -801,12 +805,12 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
           // X0 = U / ||U||, in place, as fp16 scaled by sX
           XcastParams xc{};
           xc.Xn = Xnat;
-          xc.Xt = Xtr;
+          xc.Xt = B.one_layout ? nullptr : Xtr;
           xc.x_stride = x_stride;
           xc.elems = B.m_pad * B.n_pad;
           xc.inv_norm = d_inv + ch.first;
           xc.sx = p->scales.sX;
-          st = timed(p, stream, MUON_K_XCAST, 0.0, 8.0 * (double)xc.elems * nm,
+          st = timed(p, stream, MUON_K_XCAST, 0.0, (B.one_layout ? 4.0 : 8.0) * (double)xc.elems * nm,
                      [&] { return launch_xcast(xc, nm, stream); });
           if (st != MUON_OK) return st;
           g.xkind = 1;
@@ -840,9 +844,10 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
             xg.A = Ph;
             xg.a_stride = h_stride;
             xg.lda = (int)B.r_pad;
-            xg.B = xg.B2 = XTk;
+            xg.B = xg.B2 = B.one_layout ? Xk : XTk;  // K-major: X itself
             xg.b_stride = xg.b2_stride = x_stride;
-            xg.ldb = (int)B.r_pad;
+            xg.ldb = B.one_layout ? (int)B.c_pad : (int)B.r_pad;
+            xg.b_kn = B.one_layout ? 1 : 0;
             xg.Mdim = (int)B.r_pad;
             xg.Ndim = (int)B.c_pad;
             xg.Kdim = (int)B.r_pad;
@@ -852,7 +857,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
             xg.tiles_per_prod = tm * tn;
             xg.products = 1;
             xg.Yn = B.transposed ? Xt[nx] : Xn[nx];
-            xg.Yt = B.transposed ? Xn[nx] : Xt[nx];
+            xg.Yt = B.one_layout ? nullptr : (B.transposed ? Xn[nx] : Xt[nx]);
             xg.ldyn = (int)B.c_pad;
             xg.ldyt = (int)B.r_pad;
             xg.y_stride = x_stride;
@@ -871,7 +876,7 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
               if (st != MUON_OK) return st;
               break;
             }
-            st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + 6.0 * rcf) * nm,
+            st = timed(p, stream, MUON_K_XUPD, 2.0 * r2 * cc * nm, (2.0 * r2 + (B.one_layout ? 4.0 : 6.0) * rcf) * nm,
                        [&] { return gemm(xg, EPI_XUPD); });
             if (st != MUON_OK) return st;
           }
@@ -986,9 +991,10 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr
           fg.A = Qfinal;
           fg.a_stride = h_stride;
           fg.lda = (int)B.r_pad;
-          fg.B = fg.B2 = XT;
+          fg.B = fg.B2 = B.one_layout ? X : XT;  // K-major: X0 itself
           fg.b_stride = fg.b2_stride = x_stride;
-          fg.ldb = (int)B.r_pad;
+          fg.ldb = B.one_layout ? (int)B.c_pad : (int)B.r_pad;
+          fg.b_kn = B.one_layout ? 1 : 0;
           fg.Mdim = (int)B.r_pad;
           fg.Ndim = (int)B.c_pad;
         } else {  // O^T (c x r) = X0^T (c x r) * Q
@@ -1171,6 +1177,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       // direct form's 3 N products and the update in one launch
       B.fused_direct = !f32path && !B.dma && B.direct && !B.transposed && B.r_pad == B.c_pad &&
                        (B.r_pad == 128 || B.r_pad == 256);
+      B.one_layout = B.dma && !B.transposed;
       // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
       // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
       // the 256-tile path keeps only the fp16 copies
