@@ -20,7 +20,8 @@
 // fp32 accumulate) or 32x32x2 fp32 MFMAs.  Operand tiles (both K-contiguous)
 // are staged global -> registers -> LDS with an XOR swizzle on 16-byte chunks
 // (bank conflict free for both the MFMA fragment reads and the LDS writes),
-// double buffered with one barrier per K step.  Workgroup ids are remapped so
+// double buffered in LDS with one barrier per K step, and up to 4 K steps
+// in flight in registers.  Workgroup ids are remapped so
 // that consecutive tiles share an XCD's L2.  This kernel serves the fp32 path
 // and tiles below 256; 256-tile 16-bit products use gemm_dma.hip.
 #include "common.hpp"
@@ -122,8 +123,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
   const char* Bb = pi ? (const char*)p.B2 + (size_t)mat * p.b2_stride * ES
                         : (const char*)p.B + (size_t)mat * p.b_stride * ES;
 
-  u32x4 ra[LOADS];
-  u32x4 rb[LOADS];
+  // K steps in flight: a ring of D register stages ahead of the LDS double
+  // buffer (long-K products on few tiles, e.g. a 128 x 3584 SYRK: 336
+  // workgroups over 56 K steps, otherwise pay one memory latency per step)
+  constexpr int D = BT == 64 ? 4 : (BT == 128 ? 2 : 1);
+  u32x4 ra[D][LOADS];
+  u32x4 rb[D][LOADS];
 
   f32x16 acc[F][F];
 #pragma unroll
@@ -134,8 +139,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int nk = p.Kdim / KT;
-  load_tile<ES, BT>(Ab, p.lda, row0A, 0, tid, ra);
-  load_tile<ES, BT>(Bb, p.ldb, row0B, 0, tid, rb);
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < nk) {
+      load_tile<ES, BT>(Ab, p.lda, row0A, u * KT, tid, ra[u]);
+      load_tile<ES, BT>(Bb, p.ldb, row0B, u * KT, tid, rb[u]);
+    }
 
   // Final product (and the direct form's last X') on 64-wide 16-bit tiles: the
   // W values (and the a X term of XFINAL) that this thread updates in the
@@ -161,40 +170,48 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
         xpre[e] = ld4h(p.Xid, (size_t)mat * p.y_stride + (size_t)gi * p.ldyn + gj);
     }
   }
-  store_tile<BT>(smem[0][0], ra, tid);
-  store_tile<BT>(smem[0][1], rb, tid);
+  store_tile<BT>(smem[0][0], ra[0], tid);
+  store_tile<BT>(smem[0][1], rb[0], tid);
   __syncthreads();
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_tile<ES, BT>(Ab, p.lda, row0A, (kt + 1) * KT, tid, ra);
-      load_tile<ES, BT>(Bb, p.ldb, row0B, (kt + 1) * KT, tid, rb);
-    }
-    const u32x4* sA = smem[cur][0];
-    const u32x4* sB = smem[cur][1];
+  // ring slot u holds K step k0 + u; unrolled by D so that every step's
+  // register slot is static
+#pragma unroll 1
+  for (int k0 = 0; k0 < nk; k0 += D) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = 2 * s + h;
-      u32x4 af[F], bfr[F];
+    for (int u = 0; u < D; ++u) {
+      const int kt = k0 + u;
+      if (kt < nk) {
+        // step kt is in LDS: its slot takes step kt + D
+        if (kt + D < nk) {
+          load_tile<ES, BT>(Ab, p.lda, row0A, (kt + D) * KT, tid, ra[u]);
+          load_tile<ES, BT>(Bb, p.ldb, row0B, (kt + D) * KT, tid, rb[u]);
+        }
+        const u32x4* sA = smem[kt & 1][0];
+        const u32x4* sB = smem[kt & 1][1];
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const int ra_ = wm * WT + f * 32 + l32;
-        af[f] = sA[ra_ * 8 + (ch ^ swz(ra_))];
-        const int rb_ = wn * WT + f * 32 + l32;
-        bfr[f] = sB[rb_ * 8 + (ch ^ swz(rb_))];
+        for (int s = 0; s < 4; ++s) {
+          const int ch = 2 * s + h;
+          u32x4 af[F], bfr[F];
+#pragma unroll
+          for (int f = 0; f < F; ++f) {
+            const int ra_ = wm * WT + f * 32 + l32;
+            af[f] = sA[ra_ * 8 + (ch ^ swz(ra_))];
+            const int rb_ = wn * WT + f * 32 + l32;
+            bfr[f] = sB[rb_ * 8 + (ch ^ swz(rb_))];
+          }
+#pragma unroll
+          for (int i = 0; i < F; ++i)
+#pragma unroll
+            for (int j = 0; j < F; ++j) mfma16B<KIND>(af[i], bfr[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) {
+          store_tile<BT>(smem[(kt + 1) & 1][0], ra[(u + 1) % D], tid);
+          store_tile<BT>(smem[(kt + 1) & 1][1], rb[(u + 1) % D], tid);
+        }
+        __syncthreads();
       }
-#pragma unroll
-      for (int i = 0; i < F; ++i)
-#pragma unroll
-        for (int j = 0; j < F; ++j) mfma16B<KIND>(af[i], bfr[j], acc[i][j]);
     }
-    if (more) {
-      store_tile<BT>(smem[cur ^ 1][0], ra, tid);
-      store_tile<BT>(smem[cur ^ 1][1], rb, tid);
-    }
-    __syncthreads();
   }
 
   // Epilogue: stage RR rows of the fp32 tile through LDS per round, then let
