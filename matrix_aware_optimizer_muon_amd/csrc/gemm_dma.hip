@@ -3,7 +3,9 @@
 // products of the Newton-Schulz step: SYRK, the r x r recursion and the final
 // product of the Gram form, and the direct form's X' = a X + P~ X (XUPD).
 //
-// Both operands are K-contiguous (the prep kernel writes X0 and X0^T).
+// Both operands are K-contiguous (the prep kernel writes X0 and X0^T), or,
+// for the final product and X' of buckets kept in one layout, B is X0 (X)
+// itself, K-major, read through gfx950's transposing LDS loads (BKN).
 // 8 wave64 (two per SIMD) in 2 x 4, each owning 128 x 64 = 8 x 4 blocks of
 // 16x16x32 MFMAs (128 fp32 accumulators), so one wave's barrier, DMA-issue
 // and LDS waits overlap the other's MFMAs (a 4-wave 128 x 128 variant serves
@@ -279,7 +281,9 @@ __global__ void __launch_bounds__(64 * NW, 1) gemm_dma_kernel(const GemmParams p
   // is resident each lane reads, for each of its FN block columns n and both
   // block rows, the 16-byte chunk holding its 4 consecutive m (half q4 & 1 of
   // chunk 2 (i & 1) + (q4 >> 1)) and adds gamma * X to the accumulators, so
-  // the epilogue reads no r x r input.
+  // the epilogue reads no r x r input.  With a K-major B (X' only) the stage
+  // rows are the m themselves, and one transposing read per block returns
+  // exactly the lane's 4 values.
   constexpr bool HARVEST =
       EPI == EPI_POLY || EPI == EPI_PQPG || EPI == EPI_PH || EPI == EPI_XUPD || EPI == EPI_XFINAL;
   float gam = 0.0f;
