@@ -181,6 +181,34 @@ def test_rownorm_bf16_grad_and_no_nesterov():
         assert rel(Rg[i], Ro) <= 1e-6 and rel(Wg[i], Wo) <= 1e-6
 
 
+@pytest.mark.parametrize("shapes,grad", [
+    ([(20000, 1000)], "f32"),        # tall, many row blocks, aligned rows
+    ([(20003, 1001)], "f32"),        # ragged rows and columns, unaligned rows
+    ([(20000, 1000)], "bf16"),       # bf16 gradients
+    ([(4096, 1024)] * 6, "f32"),     # several matrices in one bucket
+])
+def test_rownorm_column_strips_and_groups(shapes, grad):
+    """m > n at sizes where the column passes span many workgroups along both
+    axes ("Scaling Muon for Diffusion Transformers", 3.1: R_eps over the
+    oriented rows, i.e. U's columns): every column must match the oracle,
+    including an eps column and a zero column placed mid-matrix."""
+    W, M, G = seeded(shapes, 31 + len(shapes), mscale=1e-3)
+    for i in range(len(shapes)):
+        M[i][:, 511] = 0.0; G[i][:, 511] = 0.0
+        M[i][:, 512] = 0.0; G[i][:, 512] *= 1e-8
+    if grad == "bf16":  # the oracle sees the gradients the device holds
+        G = [WL.bf16_round(g) for g in G]
+    (Wg, Mg, Rg), _ = run(shapes, W, M, G, LR, WD, grad_dtype=grad, rownorm=True)
+    for i in range(len(shapes)):
+        Wo, Mo, Ro = OR.rownorm_step(W[i], M[i], G[i], LR, WD)
+        assert rel(Rg[i], Ro) <= 1e-6, (shapes[i], i)
+        assert rel(Mg[i], Mo) <= 1e-6, (shapes[i], i)
+        assert rel(Wg[i], Wo) <= 1e-6, (shapes[i], i)
+        # the boundary columns: zero stays zero, the eps column is U / eps
+        assert np.all(Rg[i][:, 511] == 0.0)
+        assert np.allclose(Rg[i][:, 512], Ro[:, 512], rtol=1e-5, atol=0)
+
+
 def test_checkpoint_resume_bitwise():
     import torch
     from matrix_aware_optimizer_muon_amd.optim import MuonMI355X
