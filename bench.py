@@ -200,30 +200,43 @@ def run_workload(k: int, steps: int, warmup: int, form: str = "auto", hints=None
         plan.step_ptrs(Wp, Mp, Gp, w.lr, w.wd, ws.data_ptr(), ws.numel(), sp)
         return "refresh"
 
-    def timed_pass(n):
+    def timed_pass(n, per_step):
+        # per_step: an event pair around every step (each record is a marker
+        # packet on the stream, a few us of idle per step); else one pair
+        # around the whole pass
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
+               for _ in range(n if per_step else 1)]
         kinds = []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        if not per_step:
+            evs[0][0].record(stream)
         for t in range(n):
-            evs[t][0].record(stream)
+            if per_step:
+                evs[t][0].record(stream)
             kinds.append(one_step(t))
-            evs[t][1].record(stream)
+            if per_step:
+                evs[t][1].record(stream)
+        if not per_step:
+            evs[0][1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return wall, [a.elapsed_time(b) for a, b in evs], kinds
 
     for t in range(warmup):
         one_step(t)
-    # timed region: launch profiler off
-    wall, step_ms, kinds = timed_pass(steps)
+    # timed region: launch profiler off; per-step events only where the
+    # refresh and RowNorm steps are reported apart
+    wall, step_ms, kinds = timed_pass(steps, per_step=bool(K))
+    if not K:
+        # spread of single steps, from a separate pass with per-step events
+        _, step_ms, _ = timed_pass(steps, per_step=True)
     ktimes = {}
     prof_wall = None
     if profile:
         # second pass, same steps, per-launch HIP events on the library's stream
         plan.set_profiling(True)
-        prof_wall, _, _ = timed_pass(steps)
+        prof_wall, _, _ = timed_pass(steps, per_step=False)
         ktimes = plan.kernel_times()
         plan.set_profiling(False)
 

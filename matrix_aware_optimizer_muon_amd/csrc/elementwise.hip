@@ -501,14 +501,17 @@ hipError_t launch_rownorm(const RowNormParams& p, int grad_bf16, int nmat, int v
 
 // ---------------------------------------------------------------------------
 // Pointer-table upload from kernel arguments (one thread per entry).
-__global__ void __launch_bounds__(64) write_table_kernel(const TableChunk t, MatPtrs* dst) {
+constexpr int kTableThreads = (kTableChunk + 63) / 64 * 64;
+static_assert(sizeof(TableChunk) + sizeof(MatPtrs*) <= 4096, "kernel argument block over 4 KB");
+
+__global__ void __launch_bounds__(kTableThreads) write_table_kernel(const TableChunk t, MatPtrs* dst) {
   const int i = threadIdx.x;
   if (i < t.count) dst[i] = t.e[i];
 }
 
 hipError_t launch_write_table(const TableChunk& t, MatPtrs* dst, hipStream_t s) {
   if (t.count < 1 || t.count > kTableChunk) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(write_table_kernel, dim3(1), dim3(64), 0, s, t, dst);
+  hipLaunchKernelGGL(write_table_kernel, dim3(1), dim3(kTableThreads), 0, s, t, dst);
   return hipGetLastError();
 }
 

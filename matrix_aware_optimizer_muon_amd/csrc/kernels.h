@@ -118,9 +118,9 @@ struct DirectFusedParams {
 hipError_t launch_direct_fused(const DirectFusedParams& p, int nmat, hipStream_t s);
 
 // Write up to kTableChunk pointer-table entries, passed by value as kernel
-// arguments, to dst[0 .. count) (the allocation-free step uploads its table
-// this way: no staging buffer and no host-memory copy).
-constexpr int kTableChunk = 32;
+// arguments, to dst[0 .. count) (no staging buffer and no host-memory copy;
+// 120 entries keep the argument block under 4 KB).
+constexpr int kTableChunk = 120;
 struct TableChunk {
   MatPtrs e[kTableChunk];
   int count;

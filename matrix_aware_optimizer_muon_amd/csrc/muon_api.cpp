@@ -301,8 +301,6 @@ muon_status ensure_ring(muon_plan_s* p) {
   return MUON_OK;
 }
 
-// Upload the per-matrix pointer table into the workspace (one H->D copy per
-// call, from a pinned slot that is reused only after its previous copy ran).
 // Write the pointer table from kernel arguments (kTableChunk entries per
 // launch) at dst: no staging buffer, and the stream stays on its compute
 // queue (a host-to-device copy between kernels costs a copy-engine hand-off
@@ -317,9 +315,11 @@ muon_status write_table(const muon_plan_s* p, MatPtrs* dst, hipStream_t stream) 
   return MUON_OK;
 }
 
-// Small tables (up to kKernelTable entries) go through write_table; larger
-// ones through one copy from a pinned ring slot.
-constexpr int64_t kKernelTable = 4 * kTableChunk;
+// Upload the per-matrix pointer table into the workspace.  Tables of up to
+// kKernelTable entries (8 launches) go through write_table; larger ones
+// through one host-to-device copy from a pinned ring slot that is reused only
+// after its previous copy ran.
+constexpr int64_t kKernelTable = 8 * kTableChunk;
 
 muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
   if (p->nmat <= kKernelTable) return write_table(p, (MatPtrs*)((char*)ws + p->lay.off_table), stream);
