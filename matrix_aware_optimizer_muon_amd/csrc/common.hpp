@@ -119,6 +119,18 @@ __host__ __device__ __forceinline__ void tri_tile_grouped(int t, int T, int SH, 
 
 // Streaming (non-temporal) 16-byte global access for data touched once per
 // step (M, G, W, the X0 copies): keeps it from displacing reusable lines.
+// gfx950 transposing LDS read of 16-bit elements (ds_read_b64_tr_b16): in
+// each group of 16 lanes, lane 4e + i/4 of the group supplies the 64-bit row
+// whose element i % 4 lane i receives as its element e.  With lane i
+// addressing row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16 block of a
+// row-major (k, n) tile, lane i receives column i of the block's 4 rows:
+// four consecutive k of one n.  p must point into LDS.
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
+__device__ __forceinline__ uint2 tr_read(const char* p) {
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)p));
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 nt_load4(const float* p) {
   const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);

@@ -21,7 +21,11 @@
 // are staged global -> registers -> LDS with an XOR swizzle on 16-byte chunks
 // (bank conflict free for both the MFMA fragment reads and the LDS writes),
 // double buffered in LDS with one barrier per K step, and up to 4 K steps
-// in flight in registers.  Workgroup ids are remapped so
+// in flight in registers.  The final product can instead take X0 itself as
+// its B operand, K-major (rows of k, n contiguous; BKN): the tile is staged
+// as it lies, 64-byte segments of a row XOR-swizzled by the row's low bits,
+// and each 32x32x16 B fragment (eight consecutive k of one n) is two
+// transposing LDS reads, so that no transposed copy of X0 is needed.  Workgroup ids are remapped so
 // that consecutive tiles share an XCD's L2.  This kernel serves the fp32 path
 // and tiles below 256; 256-tile 16-bit products use gemm_dma.hip.
 #include "common.hpp"
@@ -76,8 +80,72 @@ __device__ __forceinline__ void store_tile(u32x4* s, const u32x4* r, int tid) {
   }
 }
 
-template <int KIND, int BT, int EPI, bool F32PATH>
-__global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
+// K-major operand tile (KT = 64 rows of k, BT elements of n each, 16-bit):
+// the 64-byte segments of row k are permuted by segk(k), so that the four
+// consecutive rows one transposing read touches (same columns) fall in four
+// different 64-byte bank groups.
+template <int BT>
+__device__ __forceinline__ int segk(int k) {
+  static_assert(BT == 64 || BT == 128, "K-major tiles are 64 or 128 wide");
+  return BT == 64 ? ((k >> 1) & 1) : (k & 3);
+}
+
+template <int BT>
+__device__ __forceinline__ void load_tile_kn(const char* __restrict__ base, int ld, int col0, int k0,
+                                             int tid, u32x4* r) {
+  constexpr int LOADS = BT * 8 / 256;
+  constexpr int CPR = BT / 8;  // 16-byte chunks per row of k
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int q = tid + 256 * i;
+    const int row = q / CPR, ch = q % CPR;
+    r[i] = *(const u32x4*)(base + ((size_t)(k0 + row) * ld + col0) * 2 + ch * 16);
+  }
+}
+
+template <int BT>
+__device__ __forceinline__ void store_tile_kn(u32x4* s, const u32x4* r, int tid) {
+  constexpr int LOADS = BT * 8 / 256;
+  constexpr int CPR = BT / 8;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int q = tid + 256 * i;
+    const int row = q / CPR, ch = q % CPR;
+    s[row * CPR + (ch ^ (segk<BT>(row) << 2))] = r[i];
+  }
+}
+
+// B fragments of 32x32x16 MFMAs (lane: n = l32, k = 16 s + 8 h .. +7) from a
+// K-major tile: lane i of each 16-lane group addresses row k + i / 4 and
+// columns 4 (i % 4) .. +3 of its 16-column half; two reads give k .. k+3 and
+// k+4 .. k+7.  The rows a lane reads differ by multiples of 4 (and 8 h), which
+// leave segk unchanged, so each lane's byte offset for the block of columns
+// n0 is fixed (kn_lane_offset) and the step s and the half are immediates.
+template <int BT>
+__device__ __forceinline__ int kn_lane_offset(int n0, int lane) {
+  const int h = lane >> 5, g = (lane >> 4) & 1, i = lane & 15;
+  const int kl = 8 * h + (i >> 2);
+  const int ch = (((n0 >> 3) ^ (segk<BT>(kl) << 2)) + 2 * g + ((i & 3) >> 1));
+  return kl * 2 * BT + ch * 16 + 8 * (i & 1);
+}
+
+template <int BT>
+__device__ __forceinline__ u32x4 frag_kn(const char* lp, int s) {
+  const uint2 lo = tr_read(lp + s * 32 * BT);
+  const uint2 hi = tr_read(lp + s * 32 * BT + 8 * BT);
+  u32x4 f;
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+  return f;
+}
+
+// (the K-major 128-wide final product is held to two waves per SIMD, which
+// the other 128-wide 16-bit variants reach by themselves)
+template <int KIND, int BT, int EPI, bool F32PATH, bool BKN = false>
+__global__ void __launch_bounds__(256, (BKN && BT == 128) ? 2 : 1) gemm_kernel(const GemmParams p) {
+  static_assert(!BKN || (EPI == EPI_FINAL && KIND == K_BF16), "K-major B: bf16 final product only");
   constexpr int ES = (KIND == K_F32) ? 4 : 2;
   constexpr int E = 16 / ES;           // elements per 16-byte chunk
   constexpr int KT = 128 / ES;         // K elements per step (8 chunks per row)
@@ -143,7 +211,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
   for (int u = 0; u < D; ++u)
     if (u < nk) {
       load_tile<ES, BT>(Ab, p.lda, row0A, u * KT, tid, ra[u]);
-      load_tile<ES, BT>(Bb, p.ldb, row0B, u * KT, tid, rb[u]);
+      if constexpr (BKN) load_tile_kn<BT>(Bb, p.ldb, row0B, u * KT, tid, rb[u]);
+      else load_tile<ES, BT>(Bb, p.ldb, row0B, u * KT, tid, rb[u]);
     }
 
   // Final product (and the direct form's last X') on 64-wide 16-bit tiles: the
@@ -170,8 +239,15 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
         xpre[e] = ld4h(p.Xid, (size_t)mat * p.y_stride + (size_t)gi * p.ldyn + gj);
     }
   }
+  int kn_off[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    if constexpr (BKN) kn_off[f] = kn_lane_offset<BT>(wn * WT + f * 32, lane);
+    else kn_off[f] = 0;
+  }
   store_tile<BT>(smem[0][0], ra[0], tid);
-  store_tile<BT>(smem[0][1], rb[0], tid);
+  if constexpr (BKN) store_tile_kn<BT>(smem[0][1], rb[0], tid);
+  else store_tile<BT>(smem[0][1], rb[0], tid);
   __syncthreads();
 
   // ring slot u holds K step k0 + u; unrolled by D so that every step's
@@ -185,7 +261,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
         // step kt is in LDS: its slot takes step kt + D
         if (kt + D < nk) {
           load_tile<ES, BT>(Ab, p.lda, row0A, (kt + D) * KT, tid, ra[u]);
-          load_tile<ES, BT>(Bb, p.ldb, row0B, (kt + D) * KT, tid, rb[u]);
+          if constexpr (BKN) load_tile_kn<BT>(Bb, p.ldb, row0B, (kt + D) * KT, tid, rb[u]);
+          else load_tile<ES, BT>(Bb, p.ldb, row0B, (kt + D) * KT, tid, rb[u]);
         }
         const u32x4* sA = smem[kt & 1][0];
         const u32x4* sB = smem[kt & 1][1];
@@ -197,8 +274,12 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
           for (int f = 0; f < F; ++f) {
             const int ra_ = wm * WT + f * 32 + l32;
             af[f] = sA[ra_ * 8 + (ch ^ swz(ra_))];
-            const int rb_ = wn * WT + f * 32 + l32;
-            bfr[f] = sB[rb_ * 8 + (ch ^ swz(rb_))];
+            if constexpr (BKN) {
+              bfr[f] = frag_kn<BT>((const char*)sB + kn_off[f], s);
+            } else {
+              const int rb_ = wn * WT + f * 32 + l32;
+              bfr[f] = sB[rb_ * 8 + (ch ^ swz(rb_))];
+            }
           }
 #pragma unroll
           for (int i = 0; i < F; ++i)
@@ -207,7 +288,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
         }
         if (kt + 1 < nk) {
           store_tile<BT>(smem[(kt + 1) & 1][0], ra[(u + 1) % D], tid);
-          store_tile<BT>(smem[(kt + 1) & 1][1], rb[(u + 1) % D], tid);
+          if constexpr (BKN) store_tile_kn<BT>(smem[(kt + 1) & 1][1], rb[(u + 1) % D], tid);
+          else store_tile<BT>(smem[(kt + 1) & 1][1], rb[(u + 1) % D], tid);
         }
         __syncthreads();
       }
@@ -332,13 +414,13 @@ __global__ void __launch_bounds__(256) gemm_kernel(const GemmParams p) {
   }
 }
 
-template <int KIND, int BT, int EPI, bool F32PATH>
+template <int KIND, int BT, int EPI, bool F32PATH, bool BKN = false>
 static hipError_t launch_one(const GemmParams& p, int nmat, hipStream_t s) {
   const uint64_t blocks = (uint64_t)nmat * p.tiles_per_prod * p.products;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_kernel<KIND, BT, EPI, F32PATH>), dim3((uint32_t)blocks), dim3(256), 0, s,
-                     p);
+  hipLaunchKernelGGL((gemm_kernel<KIND, BT, EPI, F32PATH, BKN>), dim3((uint32_t)blocks), dim3(256), 0,
+                     s, p);
   return hipGetLastError();
 }
 
@@ -356,6 +438,12 @@ static hipError_t launch_bt(const GemmParams& p, int epi, int nmat, hipStream_t 
       case EPI_XFINAL: return launch_one<K_F16, BT, EPI_XFINAL, false>(p, nmat, s);
       default: break;
     }
+  }
+  if (p.b_kn) {
+    // K-major B: the 16-bit final product on 64- and 128-wide tiles only
+    if constexpr (!F32PATH && BT <= 128)
+      if (epi == EPI_FINAL) return launch_one<K_BF16, BT, EPI_FINAL, false, true>(p, nmat, s);
+    return hipErrorInvalidValue;
   }
   switch (epi) {
     case EPI_SYRK: return launch_one<KX, BT, EPI_SYRK, F32PATH>(p, nmat, s);

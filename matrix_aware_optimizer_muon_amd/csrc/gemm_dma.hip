@@ -74,17 +74,10 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // bytes each: eight distinct pair positions, so two rows per bank group.
 __device__ __forceinline__ int swzk(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
 
-// gfx950 transposing LDS read of 16-bit elements: in each group of 16 lanes,
-// lane 4e + i/4 of the group supplies the 64-bit row whose element i % 4
-// lane i receives as its element e.  With lane i addressing row i / 4 and
-// columns 4 (i % 4) .. +3 of a 4 x 16 block, lane i receives column i of
-// the block's 4 rows: four consecutive k of one n, half a 16x16x32 MFMA
-// operand fragment.
-typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
-__device__ __forceinline__ uint2 tr_read(const char* p) {
-  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)p));
-}
+// (tr_read, the transposing LDS read, is in common.hpp: with lane i of a
+// 16-lane group addressing row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16
+// block, lane i receives four consecutive k of one n, half a 16x16x32 MFMA
+// operand fragment.)
 
 template <int KIND>
 __device__ __forceinline__ void mfma(const u32x4& a, const u32x4& b, f32x4& c) {

@@ -40,9 +40,10 @@ struct GemmParams {
                            // (0: 8 for full grids, 4 for triangular ones)
   int waves;               // 256-wide kernels: 8, or 4 (SYRK and the final product)
   int prod_base;           // epilogue product index of the first product
-  int b_kn;                // 256-wide kernels: B stored K-major (rows of k, ld ldb,
-                           // the tile's n contiguous); final product and
-                           // EPI_XUPD / EPI_XFINAL only
+  int b_kn;                // B stored K-major (rows of k, ld ldb, the tile's n
+                           // contiguous): 256-wide kernels' final product and
+                           // EPI_XUPD / EPI_XFINAL; the 64- and 128-wide 16-bit
+                           // final product
   // r x r recursion buffers (fp32 master copies and MFMA operand copies)
   float* Gf;
   float* Qf_src;

@@ -149,9 +149,10 @@ struct Bucket {
   bool direct;  // direct form (eq. (2) on X)
   bool fused_rr;  // Gram form with the whole r x r recursion in one launch
   bool fused_direct;  // direct form: every iteration and the update in one launch
-  bool one_layout;    // 256-wide tiles, rows <= cols: U / X kept in the natural
-                      // layout only; the products that read it across K (the
-                      // final product, the direct form's X') take it K-major
+  bool one_layout;    // rows <= cols on the 16-bit path (256-wide tiles, or the
+                      // small-tile Gram form): U / X kept in the natural layout
+                      // only; the products that read it across K (the final
+                      // product, the 256-wide direct form's X') take it K-major
                       // through transposing LDS reads instead of a copy
   int bt;
   int group = 0, xcd = 0, waves = 0;  // 256-wide kernels' hint values (0: rule)
@@ -1177,7 +1178,10 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
       // direct form's 3 N products and the update in one launch
       B.fused_direct = !f32path && !B.dma && B.direct && !B.transposed && B.r_pad == B.c_pad &&
                        (B.r_pad == 128 || B.r_pad == 256);
-      B.one_layout = B.dma && !B.transposed;
+      // rows <= cols on the 16-bit path: the products that would read X0^T
+      // (the final product, the 256-wide direct form's X') read X0 across K
+      // instead; the small-tile direct form keeps both layouts
+      B.one_layout = !f32path && !B.transposed && (B.dma || !B.direct);
       // r x r buffers: fp32 path: G, Q x2, H, P~ in fp32; bf16 path: fp32
       // master copies G, Q x2, H plus fp16 operand copies G, P~, Q x2, H;
       // the 256-tile path keeps only the fp16 copies
