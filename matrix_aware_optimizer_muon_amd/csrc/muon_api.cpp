@@ -229,6 +229,15 @@ struct muon_plan_s {
   int next_slot = 0;
   bool ring_ready = false;
   std::vector<MatPtrs> host_table;
+  // device copy of the first step call's pointer table (a training loop
+  // passes the same parameters every step): later calls whose pointers all
+  // match it read it instead of a table written into their workspace
+  MatPtrs* d_cache = nullptr;
+  std::vector<MatPtrs> cached;
+  int cache_dev = -1;
+  hipStream_t cache_stream = nullptr;
+  hipEvent_t cache_ev = nullptr;  // after the copy was written
+  bool cache_tried = false;
   // launch profiler (prof_active: profiling and the running call records)
   bool profiling = false;
   bool prof_active = false;
@@ -270,6 +279,13 @@ int choose_tile(int64_t r, int64_t count, bool f32path) {
     return count * (t * (t + 1) / 2) < 512 ? 64 : 128;
   }
   return 256;
+}
+
+void release_cache(muon_plan_s* p) {
+  if (p->d_cache) (void)hipFree(p->d_cache);
+  if (p->cache_ev) (void)hipEventDestroy(p->cache_ev);
+  p->d_cache = nullptr;
+  p->cache_ev = nullptr;
 }
 
 void release_ring(muon_plan_s* p) {
@@ -336,6 +352,46 @@ muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
     return MUON_ERR_HIP;
   if (hipEventRecord(s.ev, stream) != hipSuccess) return MUON_ERR_HIP;
   s.used = true;
+  return MUON_OK;
+}
+
+// The device pointer table for this call (host_table filled): the plan's
+// cached copy when every pointer matches it, else the table written into the
+// workspace.  The first call makes the copy (a 32-byte-per-matrix hipMalloc
+// kept until the plan is destroyed; if it fails, every call uses its
+// workspace).  A call on another stream than the one that wrote the copy
+// waits for that write.
+muon_status table_for_call(muon_plan_s* p, void* ws, hipStream_t stream, const MatPtrs** d_table) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MUON_ERR_HIP;
+  const size_t bytes = sizeof(MatPtrs) * (size_t)p->nmat;
+  if (!p->cache_tried) {
+    p->cache_tried = true;
+    if (hipMalloc((void**)&p->d_cache, bytes) != hipSuccess) {
+      p->d_cache = nullptr;
+      (void)hipGetLastError();
+    } else if (hipEventCreateWithFlags(&p->cache_ev, hipEventDisableTiming) != hipSuccess) {
+      release_cache(p);
+      (void)hipGetLastError();
+    } else {
+      if (write_table(p, p->d_cache, stream) != MUON_OK || hipEventRecord(p->cache_ev, stream) != hipSuccess)
+        return MUON_ERR_HIP;
+      p->cached = p->host_table;
+      p->cache_dev = dev;
+      p->cache_stream = stream;
+      *d_table = p->d_cache;
+      return MUON_OK;
+    }
+  } else if (p->d_cache && dev == p->cache_dev &&
+             std::memcmp(p->cached.data(), p->host_table.data(), bytes) == 0) {
+    if (stream != p->cache_stream && hipStreamWaitEvent(stream, p->cache_ev, 0) != hipSuccess)
+      return MUON_ERR_HIP;
+    *d_table = p->d_cache;
+    return MUON_OK;
+  }
+  muon_status st = upload_table(p, ws, stream);
+  if (st != MUON_OK) return st;
+  *d_table = (const MatPtrs*)((char*)ws + p->lay.off_table);
   return MUON_OK;
 }
 
@@ -596,11 +652,11 @@ const muon_bucket_hint* find_hint(const muon_plan_desc* desc, int64_t m, int64_t
 }
 
 // Enqueue the refresh step of every bucket with workspace layout L at wsb
-// (the pointer table already at L.off_table), ordered after `caller`'s
-// earlier work; `caller` waits for all of it.
-muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, float lr, float wd,
-                            hipStream_t caller) {
-  const MatPtrs* d_table = (const MatPtrs*)(wsb + L.off_table);
+// and the pointer table d_table (on the device, ordered before `caller`'s
+// next work), ordered after `caller`'s earlier work; `caller` waits for all
+// of it.
+muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, const MatPtrs* d_table,
+                            float lr, float wd, hipStream_t caller) {
   float* d_inv = (float*)(wsb + L.off_inv);
   const bool f32path = p->ns_dtype == MUON_F32;
   const int op = f32path ? OP_F32 : OP_BF16;
@@ -1277,6 +1333,7 @@ muon_status muon_plan_destroy(muon_plan_t plan) {
   release_ring(plan);
   release_profile(plan);
   release_slots(plan);
+  release_cache(plan);
   delete plan;
   return MUON_OK;
 }
@@ -1327,10 +1384,11 @@ muon_status muon_step_batched(muon_plan_t p, float* const* W, float* const* M, c
   } catch (const std::bad_alloc&) {
     return MUON_ERR_INVALID_ARGUMENT;
   }
-  st = upload_table(p, ws, stream);
+  const MatPtrs* d_table = nullptr;
+  st = table_for_call(p, ws, stream, &d_table);
   if (st != MUON_OK) return st;
   p->prof_active = p->profiling;
-  return enqueue_refresh(p, p->lay, (char*)ws, lr, wd, stream);
+  return enqueue_refresh(p, p->lay, (char*)ws, d_table, lr, wd, stream);
 }
 
 muon_status muon_step_batched_noalloc(muon_plan_t p, float* const* W, float* const* M,
@@ -1348,7 +1406,7 @@ muon_status muon_step_batched_noalloc(muon_plan_t p, float* const* W, float* con
   st = write_table(p, (MatPtrs*)(ws + p->serial.off_table), stream);
   if (st != MUON_OK) return st;
   p->prof_active = false;
-  return enqueue_refresh(p, p->serial, ws, lr, wd, stream);
+  return enqueue_refresh(p, p->serial, ws, (const MatPtrs*)(ws + p->serial.off_table), lr, wd, stream);
 }
 
 muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const void* const* G,
@@ -1361,11 +1419,11 @@ muon_status rownorm_step(muon_plan_t p, float* const* W, float* const* M, const 
   } catch (const std::bad_alloc&) {
     return MUON_ERR_INVALID_ARGUMENT;
   }
-  st = upload_table(p, ws, stream);
+  const MatPtrs* d_table = nullptr;
+  st = table_for_call(p, ws, stream, &d_table);
   if (st != MUON_OK) return st;
   p->prof_active = p->profiling;
   char* wsb = (char*)ws;
-  const MatPtrs* d_table = (const MatPtrs*)(wsb + p->lay.off_table);
   const int gbf16 = p->grad_dtype == MUON_BF16 ? 1 : 0;
   for (const Bucket& B : p->buckets) {
     RowNormParams rp{};

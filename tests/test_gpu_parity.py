@@ -209,6 +209,44 @@ def test_rownorm_column_strips_and_groups(shapes, grad):
         assert np.allclose(Rg[i][:, 512], Ro[:, 512], rtol=1e-5, atol=0)
 
 
+def test_pointer_table_copy_across_calls():
+    """The plan keeps a device copy of its first call's pointer table: a call
+    with other pointers must use its own table, and a later call with the
+    first pointers on another stream must see the copy written.  Every call
+    is checked bitwise against a fresh plan on the same inputs."""
+    import torch
+    from matrix_aware_optimizer_muon_amd import Plan
+    from tests.gpu_common import to_dev
+    shapes = [(256, 1024), (1024, 256), (130, 70)] * 50  # 150 matrices: two table launches
+    sets = [seeded(shapes, 41 + k, mscale=1e-3) for k in range(2)]
+
+    def fresh(W, M, G):
+        (Wg, Mg, Og), _ = run(shapes, W, M, G, LR, WD)
+        return Wg, Mg, Og
+
+    plan = Plan(shapes, "f32", "bf16")
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    ptr = lambda L: [x.data_ptr() for x in L]
+    dev = [([to_dev(x) for x in W], [to_dev(x) for x in M], [to_dev(x) for x in G]) for W, M, G in sets]
+    outs = [[torch.empty_like(x) for x in d[0]] for d in dev]
+    side = torch.cuda.Stream()
+    for k, stream in ((0, torch.cuda.current_stream()), (1, torch.cuda.current_stream()), (0, side)):
+        Wd, Md, Gd = dev[k]
+        W0 = [x.cpu().numpy() for x in Wd]
+        M0 = [x.cpu().numpy() for x in Md]
+        G0 = [x.cpu().numpy() for x in Gd]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            plan.step_ptrs(ptr(Wd), ptr(Md), ptr(Gd), LR, WD, ws.data_ptr(), ws.numel(),
+                           stream.cuda_stream, ptr(outs[k]))
+        torch.cuda.synchronize()
+        Wr, Mr, Or = fresh(W0, M0, G0)
+        for i in range(len(shapes)):
+            assert np.array_equal(outs[k][i].cpu().numpy(), Or[i]), (k, i)
+            assert np.array_equal(Wd[i].cpu().numpy(), Wr[i]), (k, i)
+            assert np.array_equal(Md[i].cpu().numpy(), Mr[i]), (k, i)
+
+
 def test_checkpoint_resume_bitwise():
     import torch
     from matrix_aware_optimizer_muon_amd.optim import MuonMI355X
