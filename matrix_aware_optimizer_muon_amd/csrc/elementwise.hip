@@ -211,7 +211,65 @@ __global__ void __launch_bounds__(256) norm_finalize_kernel(const PrepParams p) 
   }
 }
 
-int prep_blocks_per_mat(int m_pad, int n_pad) { return (m_pad / 64) * (n_pad / 64); }
+// prep with one layout (the products read X0 across K, no transposed copy):
+// 8 rows x 512 columns of U per workgroup, each half of the workgroup one row
+// segment (2 KB of M, 1 KB of X, 1 or 2 KB of G, all contiguous), the
+// workgroups walking along the rows; the four rows of a thread are loaded
+// before any is stored.
+template <bool GBF16>
+__global__ void __launch_bounds__(256) prep_rows_kernel(const PrepParams p, int vec) {
+  __shared__ float red[4];
+  const int cb = (p.n_pad + 511) / 512;
+  const int per_mat = (p.m_pad / 8) * cb;
+  const int mat = blockIdx.x / per_mat;
+  const int bl = blockIdx.x - mat * per_mat;
+  const int rb = bl / cb, c = bl - rb * cb;
+  const MatPtrs mp = p.table[mat];
+  const int t = threadIdx.x;
+  const int j = c * 512 + (t & 127) * 4;
+  const size_t xbase = (size_t)mat * p.x_stride;
+  const int valid = p.n - j;
+  const bool v4 = vec && valid >= 4;
+  float ss = 0.f;
+  if (j < p.n_pad) {
+    float4 m[4], g[4];
+    bool in[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = rb * 8 + 2 * q + (t >> 7);
+      in[q] = i < p.m && valid > 0;
+      const size_t idx = (size_t)i * p.n + j;
+      m[q] = in[q] ? load_f4(mp.M + idx, v4, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+      g[q] = in[q] ? load_g4<GBF16>(mp.G, idx, v4, valid) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = rb * 8 + 2 * q + (t >> 7);
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (in[q]) {
+        float4 mn;
+        u = momentum4(m[q], g[q], p.mu, p.nesterov, &mn);
+        store_f4(mp.M + (size_t)i * p.n + j, mn, v4, valid);
+        if (valid < 4) {  // keep the padding exactly zero
+          if (valid < 2) u.y = 0.f;
+          if (valid < 3) u.z = 0.f;
+          u.w = 0.f;
+        }
+        ss += u.x * u.x + u.y * u.y + u.z * u.z + u.w * u.w;
+      }
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 pk = {(uint32_t)f32_to_bf16_bits(u.x) | ((uint32_t)f32_to_bf16_bits(u.y) << 16),
+                        (uint32_t)f32_to_bf16_bits(u.z) | ((uint32_t)f32_to_bf16_bits(u.w) << 16)};
+      __builtin_nontemporal_store(pk, (u32x2*)((uint16_t*)p.X + xbase + (size_t)i * p.n_pad + j));
+    }
+  }
+  const float tot = block_sum<256>(ss, red);
+  if (t == 0) p.partials[(size_t)mat * p.blocks_per_mat + bl] = tot;
+}
+
+int prep_blocks_per_mat(int m_pad, int n_pad, bool rows) {
+  return rows ? (m_pad / 8) * ((n_pad + 511) / 512) : (m_pad / 64) * (n_pad / 64);
+}
 
 hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, int vec,
                        hipStream_t s) {
@@ -219,6 +277,13 @@ hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, 
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffull || p.m_pad % 64 || p.n_pad % 64) return hipErrorInvalidValue;
   const dim3 g((uint32_t)blocks), b(256);
+  if (!p.XT && !x_f32) {
+    if (p.blocks_per_mat != prep_blocks_per_mat(p.m_pad, p.n_pad, true)) return hipErrorInvalidValue;
+    if (grad_bf16) hipLaunchKernelGGL((prep_rows_kernel<true>), g, b, 0, s, p, vec);
+    else hipLaunchKernelGGL((prep_rows_kernel<false>), g, b, 0, s, p, vec);
+    return hipGetLastError();
+  }
+  if (p.blocks_per_mat != prep_blocks_per_mat(p.m_pad, p.n_pad, false)) return hipErrorInvalidValue;
   if (grad_bf16) {
     if (x_f32) hipLaunchKernelGGL((prep_tile_kernel<true, true>), g, b, 0, s, p, vec);
     else hipLaunchKernelGGL((prep_tile_kernel<true, false>), g, b, 0, s, p, vec);

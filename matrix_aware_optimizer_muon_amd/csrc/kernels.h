@@ -146,7 +146,9 @@ struct PrepParams {
 hipError_t launch_prep(const PrepParams& p, int grad_bf16, int x_f32, int nmat, int vec,
                        hipStream_t s);
 hipError_t launch_norm_finalize(const PrepParams& p, int nmat, hipStream_t s);
-int prep_blocks_per_mat(int m_pad, int n_pad);
+// partial sums per matrix: 64 x 64 tiles, or 8 x 512 row tiles when rows
+// (one layout: XT null on the 16-bit path)
+int prep_blocks_per_mat(int m_pad, int n_pad, bool rows);
 
 struct RowNormParams {
   const MatPtrs* table;

@@ -1260,7 +1260,7 @@ muon_status muon_plan(const muon_plan_desc* desc, muon_plan_t* plan, size_t* wor
         B.chunks.push_back(Chunk{B.first + (int)f, (int)std::min<int64_t>(even, B.count - f)});
       B.m_pad = B.transposed ? B.c_pad : B.r_pad;
       B.n_pad = B.transposed ? B.r_pad : B.c_pad;
-      B.prep_blocks = prep_blocks_per_mat((int)B.m_pad, (int)B.n_pad);
+      B.prep_blocks = prep_blocks_per_mat((int)B.m_pad, (int)B.n_pad, B.one_layout);
       B.rn_row_blocks = rownorm_row_blocks((int)B.m, (int)B.n);
       B.chunk_scratch = (size_t)(even * B.scratch_per_mat);
       max_scratch = std::max(max_scratch, B.chunk_scratch);

@@ -43,7 +43,8 @@ def kernel_class(name: str) -> str | None:
         return EPI_CLASS[int(m.group(2))]
     for key, cls in (("rr_fused_kernel", "poly"), ("direct_fused_kernel", "xupd"),
                      ("xcast_kernel", "xcast"), ("wupd_kernel", "wupd"),
-                     ("prep_tile_kernel", "prep"), ("norm_finalize", "norm"),
+                     ("prep_tile_kernel", "prep"), ("prep_rows_kernel", "prep"),
+                     ("norm_finalize", "norm"),
                      ("rownorm_rows", "rownorm"), ("rownorm_colsum", "colsum"),
                      ("rownorm_colfinal", "colfinal"), ("rownorm_colapply", "colapply")):
         if key in name:
