@@ -4,9 +4,10 @@
 //             (Nesterov remark); partial sums of ||U||_F^2; U stored in the
 //             Newton-Schulz operand type both as is and transposed through
 //             LDS, zero padded to the GEMM tile: one copy is X0 = O(U)
-//             ("Scaling Muon for DiT" 3.1), the other X0^T (left out when
-//             the products read X0 across K).  One read of M and G, one
-//             write of M and of the copies.
+//             ("Scaling Muon for DiT" 3.1), the other X0^T.  When the
+//             products read X0 across K the transposed copy is left out and
+//             a row-tiled variant streams U in the natural layout only.  One
+//             read of M and G, one write of M and of the copies.
 // finalize:   deterministic (fixed order, fp64) reduction of the partial sums
 //             to 1/||U||_F per matrix (0 when the norm is 0, NaN when the sum
 //             is NaN or infinite).

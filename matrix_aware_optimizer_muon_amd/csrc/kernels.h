@@ -136,7 +136,8 @@ struct PrepParams {
   float mu;
   int nesterov;
   void* X;                 // U, natural layout m_pad x n_pad (matrix 0 of the chunk)
-  void* XT;                // U^T, n_pad x m_pad (null: not written)
+  void* XT;                // U^T, n_pad x m_pad (null: not written; the 16-bit path
+                           // then runs the row-tiled kernel)
   int64_t x_stride;        // elements between matrices (both copies)
   float* partials;         // [nmat][blocks_per_mat]
   int blocks_per_mat;

@@ -27,11 +27,25 @@ KERNEL_SOURCES = ("csrc/gemm.hip", "csrc/gemm_dma.hip", "csrc/rr_fused.hip", "cs
 EPI_CLASS = {0: "syrk", 1: "poly", 2: "pqpg", 3: "ph", 4: "final", 5: "xupd", 6: "xupd"}
 
 
-def source_hash() -> str:
+def code_only(text: str) -> str:
+    """The source without comments and with whitespace runs collapsed, so
+    that editing a comment does not mark a profile as taken on other code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_hash(read=None) -> str:
+    """Fingerprint of the kernel and planner code (comments excluded).
+    read(rel) -> text overrides reading the package's files."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(PKG, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_only(text).encode())
     return h.hexdigest()[:16]
 
 
