@@ -235,8 +235,6 @@ struct muon_plan_s {
   MatPtrs* d_cache = nullptr;
   std::vector<MatPtrs> cached;
   int cache_dev = -1;
-  hipStream_t cache_stream = nullptr;
-  hipEvent_t cache_ev = nullptr;  // after the copy was written
   bool cache_tried = false;
   // launch profiler (prof_active: profiling and the running call records)
   bool profiling = false;
@@ -283,9 +281,7 @@ int choose_tile(int64_t r, int64_t count, bool f32path) {
 
 void release_cache(muon_plan_s* p) {
   if (p->d_cache) (void)hipFree(p->d_cache);
-  if (p->cache_ev) (void)hipEventDestroy(p->cache_ev);
   p->d_cache = nullptr;
-  p->cache_ev = nullptr;
 }
 
 void release_ring(muon_plan_s* p) {
@@ -356,36 +352,34 @@ muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
 }
 
 // The device pointer table for this call (host_table filled): the plan's
-// cached copy when every pointer matches it, else the table written into the
+// copy when every pointer matches it, else the table written into the
 // workspace.  The first call makes the copy (a 32-byte-per-matrix hipMalloc
-// kept until the plan is destroyed; if it fails, every call uses its
-// workspace).  A call on another stream than the one that wrote the copy
-// waits for that write.
+// kept until the plan is destroyed), written on a private non-blocking stream
+// that the host waits for, so that any stream may read it afterwards without
+// an event; if any of this fails, every call uses its workspace.
 muon_status table_for_call(muon_plan_s* p, void* ws, hipStream_t stream, const MatPtrs** d_table) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return MUON_ERR_HIP;
   const size_t bytes = sizeof(MatPtrs) * (size_t)p->nmat;
   if (!p->cache_tried) {
     p->cache_tried = true;
-    if (hipMalloc((void**)&p->d_cache, bytes) != hipSuccess) {
-      p->d_cache = nullptr;
-      (void)hipGetLastError();
-    } else if (hipEventCreateWithFlags(&p->cache_ev, hipEventDisableTiming) != hipSuccess) {
-      release_cache(p);
-      (void)hipGetLastError();
-    } else {
-      if (write_table(p, p->d_cache, stream) != MUON_OK || hipEventRecord(p->cache_ev, stream) != hipSuccess)
-        return MUON_ERR_HIP;
+    hipStream_t cs = nullptr;
+    bool ok = hipMalloc((void**)&p->d_cache, bytes) == hipSuccess;
+    ok = ok && hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipMemcpyAsync(p->d_cache, p->host_table.data(), bytes, hipMemcpyHostToDevice, cs) ==
+                   hipSuccess;
+    ok = ok && hipStreamSynchronize(cs) == hipSuccess;
+    if (cs) (void)hipStreamDestroy(cs);
+    if (ok) {
       p->cached = p->host_table;
       p->cache_dev = dev;
-      p->cache_stream = stream;
-      *d_table = p->d_cache;
-      return MUON_OK;
+    } else {
+      release_cache(p);
+      (void)hipGetLastError();  // the failed call's error; the workspace path serves
     }
-  } else if (p->d_cache && dev == p->cache_dev &&
-             std::memcmp(p->cached.data(), p->host_table.data(), bytes) == 0) {
-    if (stream != p->cache_stream && hipStreamWaitEvent(stream, p->cache_ev, 0) != hipSuccess)
-      return MUON_ERR_HIP;
+  }
+  if (p->d_cache && dev == p->cache_dev &&
+      std::memcmp(p->cached.data(), p->host_table.data(), bytes) == 0) {
     *d_table = p->d_cache;
     return MUON_OK;
   }
