@@ -26,16 +26,10 @@
  *     arrays of length num_matrices, in the order given to muon_plan.
  *   - The workspace is a caller-owned device buffer of at least the size
  *     muon_plan reported, 256-byte aligned.  Its contents between calls are
- *     irrelevant (every call rewrites what it reads).
- *   - The first muon_step_batched / rownorm_step call of a plan allocates a
- *     device copy of its pointer table (32 bytes per matrix, on the current
- *     device, freed by muon_plan_destroy) and writes it on a private stream,
- *     waiting on the host for that copy only (no other device work).  A
- *     later call whose W, M, G and output pointers all equal that first
- *     call's reads the copy instead of writing the table into its workspace
- *     (a training loop passes the same parameters every step).  Other calls
- *     write their table into their workspace; so do all calls if the copy
- *     could not be made.
+ *     irrelevant (every call rewrites what it reads).  Step calls allocate
+ *     no device memory: the workspace is their only scratch (the plan's
+ *     internal streams and events, and a pinned host ring for pointer
+ *     tables of more than 960 matrices, are created on first use).
  *   - Calls enqueue work on `stream` and return without synchronising.
  *     Results are valid once the stream has reached that point.  When every
  *     bucket of a plan is too small to fill the GPU on its own and their

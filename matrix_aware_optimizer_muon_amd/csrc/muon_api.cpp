@@ -229,13 +229,6 @@ struct muon_plan_s {
   int next_slot = 0;
   bool ring_ready = false;
   std::vector<MatPtrs> host_table;
-  // device copy of the first step call's pointer table (a training loop
-  // passes the same parameters every step): later calls whose pointers all
-  // match it read it instead of a table written into their workspace
-  MatPtrs* d_cache = nullptr;
-  std::vector<MatPtrs> cached;
-  int cache_dev = -1;
-  bool cache_tried = false;
   // launch profiler (prof_active: profiling and the running call records)
   bool profiling = false;
   bool prof_active = false;
@@ -277,11 +270,6 @@ int choose_tile(int64_t r, int64_t count, bool f32path) {
     return count * (t * (t + 1) / 2) < 512 ? 64 : 128;
   }
   return 256;
-}
-
-void release_cache(muon_plan_s* p) {
-  if (p->d_cache) (void)hipFree(p->d_cache);
-  p->d_cache = nullptr;
 }
 
 void release_ring(muon_plan_s* p) {
@@ -351,38 +339,9 @@ muon_status upload_table(muon_plan_s* p, void* ws, hipStream_t stream) {
   return MUON_OK;
 }
 
-// The device pointer table for this call (host_table filled): the plan's
-// copy when every pointer matches it, else the table written into the
-// workspace.  The first call makes the copy (a 32-byte-per-matrix hipMalloc
-// kept until the plan is destroyed), written on a private non-blocking stream
-// that the host waits for, so that any stream may read it afterwards without
-// an event; if any of this fails, every call uses its workspace.
+// The device pointer table for this call (host_table filled), written into
+// the workspace on `stream`.
 muon_status table_for_call(muon_plan_s* p, void* ws, hipStream_t stream, const MatPtrs** d_table) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return MUON_ERR_HIP;
-  const size_t bytes = sizeof(MatPtrs) * (size_t)p->nmat;
-  if (!p->cache_tried) {
-    p->cache_tried = true;
-    hipStream_t cs = nullptr;
-    bool ok = hipMalloc((void**)&p->d_cache, bytes) == hipSuccess;
-    ok = ok && hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipMemcpyAsync(p->d_cache, p->host_table.data(), bytes, hipMemcpyHostToDevice, cs) ==
-                   hipSuccess;
-    ok = ok && hipStreamSynchronize(cs) == hipSuccess;
-    if (cs) (void)hipStreamDestroy(cs);
-    if (ok) {
-      p->cached = p->host_table;
-      p->cache_dev = dev;
-    } else {
-      release_cache(p);
-      (void)hipGetLastError();  // the failed call's error; the workspace path serves
-    }
-  }
-  if (p->d_cache && dev == p->cache_dev &&
-      std::memcmp(p->cached.data(), p->host_table.data(), bytes) == 0) {
-    *d_table = p->d_cache;
-    return MUON_OK;
-  }
   muon_status st = upload_table(p, ws, stream);
   if (st != MUON_OK) return st;
   *d_table = (const MatPtrs*)((char*)ws + p->lay.off_table);
@@ -1327,7 +1286,6 @@ muon_status muon_plan_destroy(muon_plan_t plan) {
   release_ring(plan);
   release_profile(plan);
   release_slots(plan);
-  release_cache(plan);
   delete plan;
   return MUON_OK;
 }

@@ -209,11 +209,11 @@ def test_rownorm_column_strips_and_groups(shapes, grad):
         assert np.allclose(Rg[i][:, 512], Ro[:, 512], rtol=1e-5, atol=0)
 
 
-def test_pointer_table_copy_across_calls():
-    """The plan keeps a device copy of its first call's pointer table: a call
-    with other pointers must use its own table, and a later call with the
-    first pointers on another stream must see the copy written.  Every call
-    is checked bitwise against a fresh plan on the same inputs."""
+def test_pointer_tables_across_calls():
+    """One plan called with one set of matrices, then another, then the first
+    again on another stream (150 matrices: a pointer table of two launches
+    per call): every call must use its own table.  Each is checked bitwise
+    against a fresh plan on the same inputs."""
     import torch
     from matrix_aware_optimizer_muon_amd import Plan
     from tests.gpu_common import to_dev
