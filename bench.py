@@ -118,6 +118,37 @@ def cpu_baseline(w, flops_per_shape: dict, sample_shapes_max: int = 3):
     }
 
 
+def cpu_baseline_whole(w, flops_per_shape: dict):
+    """Time the float64 oracle on every matrix of a small workload (one step
+    from zero momentum), for the workloads small enough to time whole."""
+    import numpy as np
+    from matrix_aware_optimizer_muon_amd import workloads as WL
+    from oracle import muon_oracle as OR
+    vendor, threads = blas_info()
+    cores = len(os.sched_getaffinity(0))
+    total_s = 0.0
+    for i in range(len(w.shapes)):
+        Wh = WL.host_weight(w, i)
+        Gh = WL.host_grad(w, i, 0)
+        Mh = np.zeros_like(Wh)
+        t0 = time.perf_counter()
+        OR.muon_step(Wh, Mh, Gh, w.lr, w.wd)
+        total_s += time.perf_counter() - t0
+    F = sum(flops_per_shape[tuple(s)] for s in w.shapes)
+    return {
+        "value": F / total_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads if threads else cores,
+        "kind": "oracle",
+        "sample": (f"float64 direct-form oracle on all {len(w.shapes)} matrices, one step "
+                   f"(whole workload); value = the GPU path's algorithmic flops / oracle seconds"),
+        "blas": vendor,
+        "blas_threads": threads,
+        "ms_per_step": total_s * 1e3,
+        "host_cores_visible": cores,
+    }
+
+
 def roofline_of(ktimes: dict, ns_dtype: str, traffic: dict, classes=None):
     """Roofline entry of the class with the largest total time (among
     `classes` if given)."""
@@ -378,10 +409,13 @@ def main():
             out[key] = head[key]
     if not args.no_extras and not args.tuned and form == "auto" and not max_ws:
         extra = {}
+        whole = {}  # small workloads whose oracle is timed whole: (w, flops per shape)
         for k in (1, 2, 3, 4, 5):
             if k == args.config:
                 continue
-            r, _, _ = run_workload(k, EXTRA_STEPS[k], 3, profile=not args.no_profile)
+            r, flops_k, w_k = run_workload(k, EXTRA_STEPS[k], 3, profile=not args.no_profile)
+            if k <= 3:
+                whole[k] = (w_k, flops_k)
             r.pop("plan", None)
             r.pop("kernels", None)
             extra[f"config{k}"] = r
@@ -404,6 +438,11 @@ def main():
                 extra["config4_tuned"] = r
                 print(f"extra config 4 tuned: {r['ms_per_step']} ms/step", file=sys.stderr, flush=True)
         out["extra"] = extra
+        if not args.no_cpu_baseline:
+            for k, (w_k, fk) in whole.items():
+                extra[f"config{k}"]["cpu_baseline"] = cpu_baseline_whole(w_k, fk)
+                print(f"extra config {k}: oracle {extra[f'config{k}']['cpu_baseline']['ms_per_step']:.0f} ms "
+                      f"whole", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, per_shape)
     print(json.dumps(out), flush=True)
