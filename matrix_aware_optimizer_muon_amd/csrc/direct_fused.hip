@@ -162,6 +162,27 @@ __global__ void __launch_bounds__(1024, 1) direct_fused_kernel(const DirectFused
     }
   };
 
+  // 1 / ||U|| from the prep pass's partial sums, reduced exactly as the
+  // finalize kernel does (threads 0..255 in fp64, a wave-level butterfly,
+  // then the four wave sums in order), so that the value agrees bit for bit
+  // and the launch sequence needs no finalize launch for these buckets;
+  // the LDS it uses is not touched again before the cast's closing barrier
+  float inv_norm;
+  {
+    double* red = reinterpret_cast<double*>(smem);
+    if (tid < 256) {  // waves 0..3, whole
+      const float* part = p.partials + (size_t)mat * p.blocks_per_mat;
+      double s = 0.0;
+      for (int i = tid; i < p.blocks_per_mat; i += 256) s += (double)part[i];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == 0) red[wave] = s;
+    }
+    __syncthreads();
+    const double tot = red[0] + red[1] + red[2] + red[3];
+    inv_norm = tot == 0.0 ? 0.0f : (tot < INFINITY ? (float)(1.0 / sqrt(tot)) : NAN);
+  }
+
   // X^ = fp16(U sX / ||U||) in place over both layouts of U (bf16 from the
   // prep pass; the cast pass of the launch sequence, done here by the
   // matrix's own workgroup)
@@ -170,7 +191,7 @@ __global__ void __launch_bounds__(1024, 1) direct_fused_kernel(const DirectFused
     // prep pass well before and comes from memory, and one chunk at a time
     // paid that latency 2 RP^2 / 8192 times per thread
     constexpr int CPT = RP * RP / 8 / 1024;  // 16-byte chunks per thread per layout
-    const float sc = p.inv_norm[mat] * p.sX;
+    const float sc = inv_norm * p.sX;
     uint32_t* bl[2] = {(uint32_t*)((uint16_t*)p.Xn[0] + xo), (uint32_t*)((uint16_t*)p.Xt[0] + xo)};
     u32x4 v[2][CPT];
 #pragma unroll

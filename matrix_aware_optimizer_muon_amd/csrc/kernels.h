@@ -103,7 +103,8 @@ hipError_t launch_rr_fused(const RrFusedParams& p, int nmat, hipStream_t s);
 // iteration (the r x r intermediates stay in LDS).
 struct DirectFusedParams {
   const MatPtrs* table;    // chunk's first entry (W, O)
-  const float* inv_norm;   // 1 / ||U|| per matrix of the chunk
+  const float* partials;   // the prep pass's ||U||^2 partial sums, [nmat][blocks_per_mat]
+  int blocks_per_mat;      // (each workgroup forms its matrix's 1 / ||U|| from them)
   void* Xn[2];             // natural layout, per iteration parity (Xn[0]: U
   void* Xt[2];             // in bf16 on entry, cast in place); transposed
   int64_t x_stride;        // elements between matrices in Xn / Xt

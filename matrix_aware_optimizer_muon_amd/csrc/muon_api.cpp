@@ -743,9 +743,11 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, const Ma
           return launch_prep(pp, gbf16, f32path ? 1 : 0, nm, vec, stream);
         });
         if (st != MUON_OK) return st;
-        st = timed(p, stream, MUON_K_NORM, 0.0, 4.0 * B.prep_blocks * nm,
-                   [&] { return launch_norm_finalize(pp, nm, stream); });
-        if (st != MUON_OK) return st;
+        if (!B.fused_direct) {  // the one-launch direct form reduces its own partials
+          st = timed(p, stream, MUON_K_NORM, 0.0, 4.0 * B.prep_blocks * nm,
+                     [&] { return launch_norm_finalize(pp, nm, stream); });
+          if (st != MUON_OK) return st;
+        }
 
         GemmParams g{};
         g.rr_stride = rr_stride;
@@ -784,7 +786,8 @@ muon_status enqueue_refresh(muon_plan_s* p, const Layout& L, char* wsb, const Ma
           if (B.fused_direct) {
             DirectFusedParams dp{};
             dp.table = d_table + ch.first;
-            dp.inv_norm = d_inv + ch.first;
+            dp.partials = d_part;
+            dp.blocks_per_mat = B.prep_blocks;
             dp.Xn[0] = Xn[0];
             dp.Xn[1] = Xn[1];
             dp.Xt[0] = Xt[0];
