@@ -338,7 +338,7 @@ def main():
                     help="only run a plain device copy of this many MiB (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

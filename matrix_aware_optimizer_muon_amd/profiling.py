@@ -141,7 +141,7 @@ def mfma_table(path, workload, command, xcds):
         a[3] += (d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)) * 512
         a[4] += d.get("GRBM_GUI_ACTIVE", 0.0)
     print(f"# MFMA utilisation per launch class: {workload}\n")
-    print("Counter run (GPU box, repo root), one refresh step:\n")
+    print("Counter run (MI355X, repository root), one refresh step:\n")
     print(f"```\n{command}\n```\n")
     print(f"kernel source hash: `{source_hash()}`\n")
     print("MfmaUtil is relative to the running clock; the clock column is only "
@@ -180,7 +180,7 @@ def lds_table(path, workload, command):
         a[4] += d.get("SQ_INSTS_LDS_LOAD_BANDWIDTH", 0.0) * 64
         a[5] += d.get("SQ_INSTS_LDS_STORE_BANDWIDTH", 0.0) * 64
     print(f"# LDS use per launch class: {workload}\n")
-    print("Counter run (GPU box, repo root), one refresh step:\n")
+    print("Counter run (MI355X, repository root), one refresh step:\n")
     print(f"```\n{command}\n```\n")
     print(f"kernel source hash: `{source_hash()}`\n")
     print("LdsUtil and LDSBankConflict are percentages of GPU-busy cycles x compute units; "
@@ -227,7 +227,7 @@ def main(argv=None):
     if a.cmd == "trace":
         rows = list(csv.DictReader(open(a.stats)))
         print(f"# Kernel trace: {a.title}\n")
-        print("Command (GPU box, repo root):\n")
+        print("Command (MI355X, repository root):\n")
         print(f"```\n{a.command}\n```\n")
         print(f"kernel source hash: `{source_hash()}`\n")
         print("| kernel | class | calls | total ms | avg ms | % |")
@@ -256,7 +256,7 @@ def main(argv=None):
         return
     table, sf, sw = traffic_table(a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_bytes)
     print(f"# HBM traffic per launch: {a.workload}\n")
-    print("Counter runs (GPU box, repo root), one refresh step each:\n")
+    print("Counter runs (MI355X, repository root), one refresh step each:\n")
     print(f"```\n{a.command}\n```\n")
     print(f"Scale factors from a plain device copy of {a.copy_bytes} bytes: "
           f"FETCH_SIZE x {sf:.3f}, WRITE_SIZE x {sw:.3f}.\n")
