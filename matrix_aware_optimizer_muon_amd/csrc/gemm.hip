@@ -118,9 +118,12 @@ __device__ __forceinline__ void store_tile_kn(u32x4* s, const u32x4* r, int tid)
 // B fragments of 32x32x16 MFMAs (lane: n = l32, k = 16 s + 8 h .. +7) from a
 // K-major tile: lane i of each 16-lane group addresses row k + i / 4 and
 // columns 4 (i % 4) .. +3 of its 16-column half; two reads give k .. k+3 and
-// k+4 .. k+7.  The rows a lane reads differ by multiples of 4 (and 8 h), which
-// leave segk unchanged, so each lane's byte offset for the block of columns
-// n0 is fixed (kn_lane_offset) and the step s and the half are immediates.
+// k+4 .. k+7.  A lane reads rows kl + 16 s + 4 e (kl = 8 h + i / 4, e = 0, 1):
+// adding multiples of 4 leaves segk unchanged, so each lane's byte offset
+// for the block of columns n0 is fixed (kn_lane_offset) and the step s and
+// the half e are immediates.  n0 is a multiple of 32 (its chunk index a
+// multiple of 4), so the segment permutation and the lane's chunk within the
+// segment (0..3) combine by addition.
 template <int BT>
 __device__ __forceinline__ int kn_lane_offset(int n0, int lane) {
   const int h = lane >> 5, g = (lane >> 4) & 1, i = lane & 15;
