@@ -64,3 +64,25 @@ def test_more_than_one_gpu_is_refused():
     assert p.returncode == 2
     assert "one GPU" in p.stderr
     assert p.stdout == ""
+
+
+def test_roofline_entry_arithmetic():
+    # four launches of the final product: 1e14 flops in 100 ms -> 1000
+    # TFLOP/s, 0.4 of the 2.5 PFLOP/s 16-bit peak; prep is the HBM class
+    kt = {"final": {"ms": 100.0, "launches": 4, "flops": 1e14, "bytes": 8e10},
+          "prep": {"ms": 20.0, "launches": 4, "flops": 0.0, "bytes": 1.2e11},
+          "syrk": {"ms": 30.0, "launches": 2, "flops": 2e13, "bytes": 1e9}}
+    r = bench.roofline_of(kt, "bf16", {"final": (3e10, 1e10)})
+    assert (r["bound"], r["kernel"], r["unit"], r["peak"]) == ("mfma", "final", "TFLOP/s", 2500.0)
+    assert r["achieved"] == 1000.0 and r["frac"] == 0.4
+    assert r["ms_per_launch"] == 25.0 and r["share_of_step"] == round(100 / 150, 3)
+    assert r["algorithmic_flops_per_launch"] == 2.5e13 and r["algorithmic_bytes_per_launch"] == 2e10
+    assert r["traffic"] == 4e10
+    # the fp32 path prices against the fp32 matrix peak
+    r32 = bench.roofline_of(kt, "f32", {})
+    assert r32["peak"] == 157.3 and r32["frac"] == round(1000.0 / 157.3, 4) and r32["traffic"] is None
+    # restricted to the memory-bound classes: 1.2e11 B in 20 ms = 6000 GB/s
+    h = bench.roofline_of(kt, "bf16", {}, classes=bench.HBM_CLASSES)
+    assert (h["bound"], h["kernel"], h["unit"], h["peak"]) == ("hbm", "prep", "GB/s", 8000.0)
+    assert h["achieved"] == 6000.0 and h["frac"] == 0.75
+    assert bench.roofline_of(kt, "bf16", {}, classes=("rownorm",)) is None
